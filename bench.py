@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-quantized integer GEMM/GEMV hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only-headline]
+
+One step = the decode hot path on the decode workload (M=1, K=4096, N=12288):
+quantize the fp32 activation row to Q8_0, then the thin-M Q8_0 GEMV against
+Q8_0 weights.  The weights are rotated over 8 resident copies (428 MB, more
+than the 256 MB Infinity Cache) so every step streams its weights from HBM.
+`value` is algorithmic bytes per step / time per step (GB/s); inputs are
+resident in HBM before timing starts.
+
+Also reported (key "also"): the prefill GEMM (M=2048, K=5120, N=17408), the
+long-prefill GEMM (M=18432, K=5120, N=5120, Student-t activations with outlier
+channels), the grouped W4A8 MoE GEMM (947 tokens, top-8 of 128 experts,
+K=2048, N=768) and the activation quantizer, each with its own roofline.
+
+"roofline" describes the dominant kernel of the step (the GEMV): achieved =
+algorithmic bytes per launch / mean launch duration, measured with HIP events
+recorded on the launch stream around each launch.
+
+"cpu_baseline" times the CPU oracle (plain C, all host cores) on the same step
+for ~10 s; it is a reported baseline, not a target.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "int8-equiv TOPS (% MFMA peak) prefill GEMM; GB/s (% HBM peak) M=1 GEMV"
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0      # dense int8 MFMA, MI355X
+# fp32 VALU without packed-fp32 instructions: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
+VALU_LANE_OPS_PEAK = 256 * 4 * 16 * 2.4e9
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--only-headline", action="store_true", help="skip the secondary workloads")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def log(msg):
+    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.flush()
+
+
+class Timer:
+    """Mean duration of one callable per launch, from HIP events recorded on
+    the current (launch) stream around every launch."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def per_launch(self, fn, iters):
+        torch = self.torch
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        torch.cuda.synchronize()
+        for i in range(iters):
+            ev[i][0].record()
+            fn(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in ev])
+        return float(ms.mean()), float(np.median(ms)), ms
+
+    def loop(self, fn, iters):
+        torch = self.torch
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(iters):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+
+def device_q8(bqi, torch, rows, k, std, gen, t_dist=False, outlier_cols=None):
+    """Synthetic fp32 matrix on the device (seeded torch generator), quantized
+    with the library's own quantize_q8_0."""
+    if t_dist:
+        # Student-t(3) = N / sqrt(chi2_3 / 3)
+        z = torch.randn((rows, k), generator=gen, device="cuda", dtype=torch.float32)
+        c = torch.randn((rows, k, 3), generator=gen, device="cuda", dtype=torch.float32)
+        x = z / torch.sqrt((c * c).sum(-1) / 3.0)
+        del c
+        if outlier_cols is not None:
+            x[:, torch.as_tensor(outlier_cols, device="cuda")] *= 20.0
+    else:
+        x = torch.randn((rows, k), generator=gen, device="cuda", dtype=torch.float32) * std
+    q, d = bqi.quantize_q8_0(x)
+    return x, q, d
+
+
+def bench_headline(bqi, torch, W, args):
+    s = W.DECODE[0]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1)
+    copies = 8
+    log("decode workload M=%d K=%d N=%d, %d weight copies" % (s.m, s.k, s.n, copies))
+    wq, wd = [], []
+    for c in range(copies):
+        _, q, d = device_q8(bqi, torch, s.n, s.k, 0.02, gen)
+        wq.append(q)
+        wd.append(d)
+    x = torch.randn((s.m, s.k), generator=gen, device="cuda", dtype=torch.float32)
+    aq = torch.empty((s.m, s.k), dtype=torch.int8, device="cuda")
+    ad = torch.empty((s.m, s.k // 32), dtype=torch.int16, device="cuda")
+    y = torch.empty((s.m, s.n), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(i):
+        bqi.quantize_q8_0(x, aq, ad)
+        bqi.qgemm_q8_0(aq, ad, wq[i % copies], wd[i % copies], y)
+
+    def gemv(i):
+        bqi.qgemm_q8_0(aq, ad, wq[i % copies], wd[i % copies], y)
+
+    for i in range(args.warmup):
+        step(i)
+    T = Timer(torch)
+    ms_step = T.loop(step, args.steps)
+    gemv_mean, gemv_med, _ = T.per_launch(gemv, args.steps)
+    gemv_loop = T.loop(gemv, args.steps)
+
+    w_bytes = s.n * s.k + s.n * (s.k // 32) * 2
+    a_bytes = s.m * s.k + s.m * (s.k // 32) * 2
+    y_bytes = s.m * s.n * 4
+    gemv_bytes = w_bytes + a_bytes + y_bytes
+    quant_bytes = s.m * s.k * 4 + a_bytes
+    step_bytes = gemv_bytes + quant_bytes
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = gemv_bytes / (gemv_mean * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "decode GEMV M=1 K=4096 N=12288 (quantize + qgemm_q8_0)",
+                   "m": s.m, "k": s.k, "n": s.n, "weights": "Q8_0 of N(0,0.02)",
+                   "activations": "N(0,1) fp32 quantized to Q8_0 in the step",
+                   "weight_copies_rotated": copies, "bytes_per_step": step_bytes},
+        "roofline": {"bound": "hbm", "kernel": "k_gemv_thin<1>",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": gemv_bytes,
+                     "mean_launch_us": round(gemv_mean * 1e3, 3),
+                     "median_launch_us": round(gemv_med * 1e3, 3),
+                     "back_to_back_us": round(gemv_loop * 1e3, 3)},
+    }
+    ctx = dict(s=s, wq=wq, wd=wd, x=x, step_bytes=step_bytes)
+    return res, ctx
+
+
+def bench_gemm(bqi, torch, W, name, iters):
+    s = W.PREFILL if name == "prefill" else W.LONG
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2 if name == "prefill" else 3)
+    log("%s GEMM M=%d K=%d N=%d" % (name, s.m, s.k, s.n))
+    if name == "long":
+        xa, aq, ad = device_q8(bqi, torch, s.m, s.k, 1.0, gen, t_dist=True,
+                               outlier_cols=W.outlier_columns(s.k))
+    else:
+        xa, aq, ad = device_q8(bqi, torch, s.m, s.k, 1.0, gen)
+    _, wq, wd = device_q8(bqi, torch, s.n, s.k, 0.02, gen)
+    y = torch.empty((s.m, s.n), dtype=torch.float32, device="cuda")
+    T = Timer(torch)
+    for _ in range(3):
+        bqi.qgemm_q8_0(aq, ad, wq, wd, y)
+    mean, med, _ = T.per_launch(lambda i: bqi.qgemm_q8_0(aq, ad, wq, wd, y), iters)
+    qmean, _, _ = T.per_launch(lambda i: bqi.quantize_q8_0(xa, aq, ad), max(3, iters // 2))
+    ops = 2.0 * s.m * s.n * s.k
+    tops = ops / (mean * 1e-3) / 1e12
+    out_blocks = s.m * s.n * (s.k // 32)
+    valu_ops = 2.0 * out_blocks  # the scale epilogue's two fp32 ops per output-block
+    byt = (s.m + s.n) * (s.k + s.k // 32 * 2) + s.m * s.n * 4
+    qbytes = s.m * s.k * 4 + s.m * (s.k + s.k // 32 * 2)
+    del xa
+    return {
+        "workload": "%s GEMM M=%d K=%d N=%d" % (name, s.m, s.k, s.n),
+        "kernel": "k_gemm_mfma", "value": round(tops, 2), "unit": "int8-equiv TOPS",
+        "mean_launch_us": round(mean * 1e3, 2), "median_launch_us": round(med * 1e3, 2),
+        "frac_int8_mfma_peak": round(tops / INT8_PEAK_TOPS, 4),
+        "epilogue_valu_frac": round(valu_ops / (mean * 1e-3) / VALU_LANE_OPS_PEAK, 4),
+        "hbm_bytes_algorithmic": byt,
+        "quantize": {"kernel": "k_quantize_q8_0", "mean_launch_us": round(qmean * 1e3, 2),
+                     "GB/s": round(qbytes / (qmean * 1e-3) / 1e9, 1),
+                     "frac_hbm_peak": round(qbytes / (qmean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+
+
+def bench_moe(bqi, torch, W, iters):
+    m = W.MOE
+    log("moe grouped W4A8: %d tokens top-%d of %d experts K=%d N=%d"
+        % (m.tokens, m.top_k, m.experts, m.k, m.n))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    _, aq, ad = device_q8(bqi, torch, m.tokens, m.k, 1.0, gen)
+    ids = torch.from_numpy(W.topk_ids(m.tokens, m.top_k, m.experts)).cuda()
+    copies = 5
+    wq, wd = [], []
+    for _ in range(copies):
+        wq.append(torch.randint(0, 256, (m.experts, m.n, m.k // 2), generator=gen,
+                                device="cuda", dtype=torch.uint8))
+        e = torch.randint(-12, -5, (m.experts, m.n, m.k // 32), generator=gen, device="cuda")
+        mant = torch.rand((m.experts, m.n, m.k // 32), generator=gen, device="cuda") + 1.0
+        wd.append(torch.ldexp(mant, e.float()).half().view(torch.int16))
+    y = torch.empty((m.tokens, m.top_k, m.n), dtype=torch.float32, device="cuda")
+    ws = torch.empty(bqi.workspace_size(m.tokens, m.top_k, m.experts), dtype=torch.uint8,
+                     device="cuda")
+    fn = lambda i: bqi.qgemm_w4a8_grouped(aq, ad, ids, wq[i % copies], wd[i % copies], y, ws)
+    for i in range(3):
+        fn(i)
+    T = Timer(torch)
+    mean, med, _ = T.per_launch(fn, iters)
+    R = m.tokens * m.top_k
+    byt = (m.experts * m.n * (m.k // 2 + m.k // 32 * 2) + m.tokens * (m.k + m.k // 32 * 2)
+           + R * 4 + R * m.n * 4)
+    ops = 2.0 * R * m.n * m.k
+    gbs = byt / (mean * 1e-3) / 1e9
+    return {"workload": "grouped W4A8 T=%d top-%d E=%d K=%d N=%d" % (m.tokens, m.top_k, m.experts,
+                                                                    m.k, m.n),
+            "kernel": "k_route + k_grouped_w4a8", "value": round(gbs, 1), "unit": "GB/s",
+            "mean_call_us": round(mean * 1e3, 2), "median_call_us": round(med * 1e3, 2),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "int8_equiv_TOPS": round(ops / (mean * 1e-3) / 1e12, 2),
+            "weight_copies_rotated": copies, "hbm_bytes_algorithmic": byt}
+
+
+def cpu_baseline(W, step_bytes, seconds):
+    """The CPU oracle (test infrastructure, plain C, all host cores) on the
+    same decode step: quantize the activation row, then the full GEMV."""
+    import oracle
+    s = W.DECODE[0]
+    threads = oracle.default_threads()
+    w = W.weights("decode", s.n, s.k)
+    qw, dw = oracle.quantize_q8_0(w)
+    x = W.activations("decode", s.m, s.k)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        qa, da = oracle.quantize_q8_0(x)
+        oracle.qgemm_q8_0(qa, da, qw, dw, nthreads=threads)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per = el / n
+    return {"value": round(step_bytes / per / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "sample": "%d full decode steps (quantize 1x4096 + GEMV "
+            "12288x4096), %.3f s each" % (n, per)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_quantized_integer_amd as bqi
+    import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    bqi.lib()
+    res, ctx = bench_headline(bqi, torch, W, args)
+    log("headline: %.1f GB/s per step, GEMV %.2f us (%.1f%% of HBM peak)" % (
+        res["value"], res["roofline"]["mean_launch_us"], 100 * res["roofline"]["frac"]))
+    del ctx["wq"], ctx["wd"]
+    torch.cuda.empty_cache()
+    if not args.only_headline:
+        also = []
+        for name in ("prefill", "long"):
+            also.append(bench_gemm(bqi, torch, W, name, 20))
+            log(json.dumps(also[-1]))
+            torch.cuda.empty_cache()
+        also.append(bench_moe(bqi, torch, W, 50))
+        log(json.dumps(also[-1]))
+        res["also"] = also
+    if not args.no_cpu:
+        log("cpu baseline (~%.0f s)" % args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(W, ctx["step_bytes"], args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

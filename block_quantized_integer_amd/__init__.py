@@ -1,0 +1,200 @@
+"""block_quantized_integer_amd -- block-quantized integer GEMM/GEMV on MI355X.
+
+Thin Python binding over the C ABI of ``libbqi.so`` (``include/bqi.h``).  The
+functions here only check tensor dtypes/shapes/devices and pass raw pointers
+and the current HIP stream; every step of the computation runs in the
+library's gfx950 kernels.  There is no CPU fallback: if ``libbqi.so`` is
+missing, importing the library functions raises.
+
+Entry points (same names as the C ABI):
+  quantize_q8_0(x)                       -> (q int8 [R][K], d uint16-as-int16 fp16 bits [R][K/32])
+  qgemm_q8_0(aq, ad, wq, wd)             -> y fp32 [M][N] = A W^T
+  route_topk(topk_ids, n_experts)        -> (counts, offsets, rows)
+  qgemm_w4a8_grouped(aq, ad, topk_ids, wq4, wd) -> y fp32 [T][top_k][N]
+
+fp16 scale bit patterns travel as torch.int16 tensors (torch has no uint16
+arithmetic on GPU); only their bits matter.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libbqi.so")
+
+BQI_OK, BQI_EINVAL, BQI_ESHAPE, BQI_EALIGN, BQI_EHIP = 0, -1, -2, -3, -4
+BQI_F32, BQI_F16 = 0, 1
+
+SYMBOLS = ("bqi_status_string", "bqi_abi_version", "quantize_q8_0", "qgemm_q8_0",
+           "route_topk", "qgemm_w4a8_grouped_workspace_size", "qgemm_w4a8_grouped")
+
+_lib = None
+
+
+class BqiError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s" % (where, lib().bqi_status_string(status).decode()))
+
+
+def lib() -> C.CDLL:
+    """Load libbqi.so (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libbqi.so not found at %s; build it with "
+                          "`python -m block_quantized_integer_amd.build`" % LIB_PATH)
+    L = C.CDLL(LIB_PATH)
+    P, I64, I32 = C.c_void_p, C.c_int64, C.c_int
+    L.bqi_status_string.restype = C.c_char_p
+    L.bqi_status_string.argtypes = [I32]
+    L.bqi_abi_version.restype = I32
+    L.bqi_abi_version.argtypes = []
+    L.quantize_q8_0.restype = I32
+    L.quantize_q8_0.argtypes = [P, I32, I64, I64, I64, P, P, P]
+    L.qgemm_q8_0.restype = I32
+    L.qgemm_q8_0.argtypes = [P, P, I64, P, P, I64, I64, P, P]
+    L.route_topk.restype = I32
+    L.route_topk.argtypes = [P, I64, I64, I64, P, P, P, P]
+    L.qgemm_w4a8_grouped_workspace_size.restype = C.c_size_t
+    L.qgemm_w4a8_grouped_workspace_size.argtypes = [I64, I64, I64]
+    L.qgemm_w4a8_grouped.restype = I32
+    L.qgemm_w4a8_grouped.argtypes = [P, P, I64, P, I64, P, P, I64, I64, I64, P, P,
+                                     C.c_size_t, P]
+    _lib = L
+    return L
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if hasattr(stream, "cuda_stream"):
+        return C.c_void_p(stream.cuda_stream)
+    return C.c_void_p(int(stream))
+
+
+def _check(t, dtype, ndim, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got %d" % (name, ndim, t.dim()))
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else C.c_void_p(0)
+
+
+def _raise(st, where):
+    if st != BQI_OK:
+        raise BqiError(st, where)
+
+
+def quantize_q8_0(x, q=None, d=None, stream=None):
+    """Q8_0-quantize the rows of x (fp32 or fp16, [R][ldx] with row stride
+    ldx >= K; pass a column slice x[:, :K] of a contiguous tensor to quantize
+    only the first K columns).  Returns (q int8 [R][K], d int16 [R][K/32])."""
+    torch = _torch()
+    if x.dtype not in (torch.float32, torch.float16):
+        raise TypeError("x must be float32 or float16")
+    if x.dim() != 2 or x.stride(1) != 1 or not x.is_cuda:
+        raise ValueError("x must be a 2-D GPU tensor with unit column stride")
+    R, K = x.shape
+    ldx = x.stride(0) if R > 1 else K
+    if q is None:
+        q = torch.empty((R, K), dtype=torch.int8, device=x.device)
+    if d is None:
+        d = torch.empty((R, K // 32), dtype=torch.int16, device=x.device)
+    _check(q, torch.int8, 2, "q")
+    _check(d, torch.int16, 2, "d")
+    dt = BQI_F32 if x.dtype == torch.float32 else BQI_F16
+    st = lib().quantize_q8_0(_ptr(x), dt, R, K, ldx, _ptr(q), _ptr(d), _stream(stream))
+    _raise(st, "quantize_q8_0")
+    return q, d
+
+
+def qgemm_q8_0(aq, ad, wq, wd, y=None, stream=None):
+    """y[M][N] = A W^T for Q8_0 activations (aq, ad) and Q8_0 weights (wq, wd)."""
+    torch = _torch()
+    _check(aq, torch.int8, 2, "aq")
+    _check(ad, torch.int16, 2, "ad")
+    _check(wq, torch.int8, 2, "wq")
+    _check(wd, torch.int16, 2, "wd")
+    M, K = aq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or tuple(ad.shape) != (M, K // 32) or tuple(wd.shape) != (N, K // 32):
+        raise ValueError("shape mismatch: aq %s ad %s wq %s wd %s" % (
+            tuple(aq.shape), tuple(ad.shape), tuple(wq.shape), tuple(wd.shape)))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=aq.device)
+    _check(y, torch.float32, 2, "y")
+    st = lib().qgemm_q8_0(_ptr(aq), _ptr(ad), M, _ptr(wq), _ptr(wd), N, K, _ptr(y),
+                          _stream(stream))
+    _raise(st, "qgemm_q8_0")
+    return y
+
+
+def route_topk(topk_ids, n_experts, counts=None, offsets=None, rows=None, stream=None):
+    """Group routed rows by expert.  Returns (counts [E], offsets [E+1], rows [T*top_k])."""
+    torch = _torch()
+    _check(topk_ids, torch.int32, 2, "topk_ids")
+    T, top_k = topk_ids.shape
+    dev = topk_ids.device
+    if counts is None:
+        counts = torch.empty(n_experts, dtype=torch.int32, device=dev)
+    if offsets is None:
+        offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
+    if rows is None:
+        rows = torch.empty(max(1, T * top_k), dtype=torch.int32, device=dev)
+    st = lib().route_topk(_ptr(topk_ids), T, top_k, n_experts, _ptr(counts), _ptr(offsets),
+                          _ptr(rows), _stream(stream))
+    _raise(st, "route_topk")
+    return counts, offsets, rows
+
+
+def workspace_size(n_tokens, top_k, n_experts) -> int:
+    return int(lib().qgemm_w4a8_grouped_workspace_size(n_tokens, top_k, n_experts))
+
+
+def qgemm_w4a8_grouped(aq, ad, topk_ids, wq4, wd, y=None, workspace=None, stream=None):
+    """Grouped W4A8: y[T][top_k][N] for 4-bit expert weights wq4 [E][N][K/2]
+    (uint8), wd [E][N][K/32] (int16 fp16 bits) and Q8_0 activations."""
+    torch = _torch()
+    _check(aq, torch.int8, 2, "aq")
+    _check(ad, torch.int16, 2, "ad")
+    _check(topk_ids, torch.int32, 2, "topk_ids")
+    _check(wq4, torch.uint8, 3, "wq4")
+    _check(wd, torch.int16, 3, "wd")
+    T, K = aq.shape
+    top_k = topk_ids.shape[1]
+    E, N, KH = wq4.shape
+    if KH * 2 != K or tuple(ad.shape) != (T, K // 32) or topk_ids.shape[0] != T \
+            or tuple(wd.shape) != (E, N, K // 32):
+        raise ValueError("shape mismatch")
+    if y is None:
+        y = torch.empty((T, top_k, N), dtype=torch.float32, device=aq.device)
+    _check(y, torch.float32, 3, "y")
+    need = workspace_size(T, top_k, E)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=aq.device)
+    if workspace.numel() < need:
+        raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel(), need))
+    st = lib().qgemm_w4a8_grouped(_ptr(aq), _ptr(ad), T, _ptr(topk_ids), top_k, _ptr(wq4),
+                                  _ptr(wd), E, N, K, _ptr(y), _ptr(workspace),
+                                  workspace.numel(), _stream(stream))
+    _raise(st, "qgemm_w4a8_grouped")
+    return y

@@ -1,0 +1,158 @@
+// api.hip -- the C ABI of libbqi (declared in include/bqi.h): host-side
+// argument validation, then dispatch to the gfx950 kernels.  Validation runs
+// before any HIP call, so a rejected call touches neither the device nor the
+// stream and can be exercised on a machine without a GPU.
+#include "../../include/bqi.h"
+#include "bqi_launch.h"
+
+namespace {
+
+constexpr int64_t kQK = 32;
+constexpr int64_t kI32Max = 0x7fffffffLL;
+
+bool aligned(const void *p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? BQI_OK : BQI_EHIP; }
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Workspace layout of qgemm_w4a8_grouped: counts[E], offsets[E+1],
+// rows[T*top_k] (int32), each section starting on a 256-byte boundary.
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t counts, offsets, rows, total;
+};
+
+WsLayout ws_layout(int64_t rows_total, int64_t n_experts) {
+  WsLayout L;
+  L.counts = 0;
+  L.offsets = round256((size_t)n_experts * 4);
+  L.rows = L.offsets + round256((size_t)(n_experts + 1) * 4);
+  L.total = L.rows + round256((size_t)rows_total * 4);
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *bqi_status_string(int status) {
+  switch (status) {
+    case BQI_OK: return "BQI_OK";
+    case BQI_EINVAL: return "BQI_EINVAL: null pointer, bad dtype or workspace too small";
+    case BQI_ESHAPE: return "BQI_ESHAPE: bad size (negative, k not a multiple of 32, ldx < k, too large)";
+    case BQI_EALIGN: return "BQI_EALIGN: pointer or leading dimension misaligned";
+    case BQI_EHIP: return "BQI_EHIP: HIP runtime error at launch";
+    default: return "unknown bqi status";
+  }
+}
+
+int bqi_abi_version(void) { return 100; }
+
+int quantize_q8_0(const void *x, int x_dtype, int64_t rows, int64_t k,
+                  int64_t ldx, int8_t *q, uint16_t *d, void *stream) {
+  if (x_dtype != BQI_F32 && x_dtype != BQI_F16) return BQI_EINVAL;
+  if (rows < 0 || k < 0 || k % kQK != 0 || ldx < k) return BQI_ESHAPE;
+  if (rows == 0 || k == 0) return BQI_OK;
+  if (rows > kI32Max || k > kI32Max) return BQI_ESHAPE;
+  if (!x || !q || !d) return BQI_EINVAL;
+  const int64_t esize = x_dtype == BQI_F32 ? 4 : 2;
+  const int64_t vec = x_dtype == BQI_F32 ? 16 : 8;  // bytes per lane load
+  if (!aligned(x, 16) || (ldx * esize) % vec != 0 || !aligned(q, 16) ||
+      !aligned(d, 2))
+    return BQI_EALIGN;
+  return hip_status(bqi::launch_quantize_q8_0(x, x_dtype == BQI_F16, rows, k,
+                                              ldx, q, d, as_stream(stream)));
+}
+
+int qgemm_q8_0(const int8_t *aq, const uint16_t *ad, int64_t m,
+               const int8_t *wq, const uint16_t *wd, int64_t n, int64_t k,
+               float *y, void *stream) {
+  if (m < 0 || n < 0 || k < 0 || k % kQK != 0) return BQI_ESHAPE;
+  if (m == 0 || n == 0) return BQI_OK;
+  if (!y) return BQI_EINVAL;
+  if (m > kI32Max || n > kI32Max || k > kI32Max) return BQI_ESHAPE;
+  if (k == 0) {
+    // empty sum: y = 0
+    if (!aligned(y, 4)) return BQI_EALIGN;
+    return hip_status(bqi::launch_zero_f32(y, m * n, as_stream(stream)));
+  }
+  if (!aq || !ad || !wq || !wd) return BQI_EINVAL;
+  if (!aligned(aq, 16) || !aligned(wq, 16) || !aligned(ad, 2) ||
+      !aligned(wd, 2) || !aligned(y, 4))
+    return BQI_EALIGN;
+  if (m <= 16)
+    return hip_status(
+        bqi::launch_gemv_thin(aq, ad, m, wq, wd, n, k, y, as_stream(stream)));
+  // the MFMA kernel indexes tiles and rows in 32-bit
+  if ((m + 127) / 128 * ((n + 127) / 128) > kI32Max) return BQI_ESHAPE;
+  return hip_status(
+      bqi::launch_gemm_mfma(aq, ad, m, wq, wd, n, k, y, as_stream(stream)));
+}
+
+int route_topk(const int32_t *topk_ids, int64_t n_tokens, int64_t top_k,
+               int64_t n_experts, int32_t *counts, int32_t *offsets,
+               int32_t *rows, void *stream) {
+  if (n_tokens < 0 || top_k < 0 || n_experts < 0) return BQI_ESHAPE;
+  if (n_experts > 65536 || n_tokens * top_k > kI32Max - 1) return BQI_ESHAPE;
+  if (n_experts == 0) return BQI_OK;
+  if (!counts || !offsets) return BQI_EINVAL;
+  if (n_tokens * top_k > 0 && (!topk_ids || !rows)) return BQI_EINVAL;
+  if (!aligned(topk_ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) ||
+      !aligned(rows, 4))
+    return BQI_EALIGN;
+  return hip_status(bqi::launch_route_topk(topk_ids, n_tokens * top_k,
+                                           n_experts, counts, offsets, rows,
+                                           nullptr, 0, as_stream(stream)));
+}
+
+size_t qgemm_w4a8_grouped_workspace_size(int64_t n_tokens, int64_t top_k,
+                                         int64_t n_experts) {
+  if (n_tokens < 0 || top_k < 0 || n_experts < 0) return 0;
+  return ws_layout(n_tokens * top_k, n_experts).total;
+}
+
+int qgemm_w4a8_grouped(const int8_t *aq, const uint16_t *ad, int64_t n_tokens,
+                       const int32_t *topk_ids, int64_t top_k,
+                       const uint8_t *wq4, const uint16_t *wd,
+                       int64_t n_experts, int64_t n, int64_t k, float *y,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+  if (n_tokens < 0 || top_k < 0 || n_experts < 0 || n < 0 || k < 0 ||
+      k % kQK != 0)
+    return BQI_ESHAPE;
+  if (n_experts > 65536 || n_tokens * top_k > kI32Max - 1 || n > kI32Max ||
+      k > kI32Max)
+    return BQI_ESHAPE;
+  const int64_t rows_total = n_tokens * top_k;
+  if (rows_total == 0 || n == 0) return BQI_OK;
+  if (!y || !topk_ids) return BQI_EINVAL;
+  if (n_experts > 0 && n_experts * ((n + 127) / 128) > kI32Max) return BQI_ESHAPE;
+  if (k > 0 && (!aq || !ad)) return BQI_EINVAL;
+  if (k > 0 && n_experts > 0 && (!wq4 || !wd)) return BQI_EINVAL;
+  if (!aligned(y, 4) || !aligned(topk_ids, 4)) return BQI_EALIGN;
+  if (k > 0 && (!aligned(aq, 16) || !aligned(ad, 2))) return BQI_EALIGN;
+  if (k > 0 && n_experts > 0 && (!aligned(wq4, 16) || !aligned(wd, 2)))
+    return BQI_EALIGN;
+  hipStream_t s = as_stream(stream);
+  if (k == 0 || n_experts == 0) {
+    // every valid row is an empty sum, or every row is invalid: y = 0
+    return hip_status(bqi::launch_zero_f32(y, rows_total * n, s));
+  }
+  const WsLayout L = ws_layout(rows_total, n_experts);
+  if (!workspace || workspace_bytes < L.total) return BQI_EINVAL;
+  if (!aligned(workspace, 256)) return BQI_EALIGN;
+  char *ws = static_cast<char *>(workspace);
+  int32_t *counts = reinterpret_cast<int32_t *>(ws + L.counts);
+  int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
+  int32_t *rows = reinterpret_cast<int32_t *>(ws + L.rows);
+  hipError_t e = bqi::launch_route_topk(topk_ids, rows_total, n_experts, counts,
+                                        offsets, rows, y, n, s);
+  if (e != hipSuccess) return BQI_EHIP;
+  return hip_status(bqi::launch_grouped_w4a8(aq, ad, top_k, wq4, wd, n_experts,
+                                             n, k, counts, offsets, rows, y, s));
+}
+
+}  // extern "C"

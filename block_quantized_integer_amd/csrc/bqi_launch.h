@@ -1,0 +1,44 @@
+// bqi_launch.h -- host-side launchers of the gfx950 kernels (internal to
+// libbqi; the public C ABI is include/bqi.h).  Each launcher assumes its
+// arguments were already validated by the ABI layer and returns the HIP
+// error state after enqueueing its kernels on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bqi {
+
+hipError_t launch_quantize_q8_0(const void *x, bool f16, int64_t rows,
+                                int64_t k, int64_t ldx, int8_t *q, uint16_t *d,
+                                hipStream_t stream);
+
+hipError_t launch_zero_f32(float *y, int64_t count, hipStream_t stream);
+
+// thin-M (m <= 16) Q8_0 GEMM/GEMV
+hipError_t launch_gemv_thin(const int8_t *aq, const uint16_t *ad, int64_t m,
+                            const int8_t *wq, const uint16_t *wd, int64_t n,
+                            int64_t k, float *y, hipStream_t stream);
+
+// large-M Q8_0 GEMM on int8 MFMA
+hipError_t launch_gemm_mfma(const int8_t *aq, const uint16_t *ad, int64_t m,
+                            const int8_t *wq, const uint16_t *wd, int64_t n,
+                            int64_t k, float *y, hipStream_t stream);
+
+// routing (counting sort by expert); y != nullptr also zeroes the output
+// rows of invalid ids ([rows_total][n] floats)
+hipError_t launch_route_topk(const int32_t *ids, int64_t rows_total,
+                             int64_t n_experts, int32_t *counts,
+                             int32_t *offsets, int32_t *rows, float *y,
+                             int64_t n, hipStream_t stream);
+
+// grouped W4A8 GEMM reading a routing produced by launch_route_topk
+hipError_t launch_grouped_w4a8(const int8_t *aq, const uint16_t *ad,
+                               int64_t top_k, const uint8_t *wq4,
+                               const uint16_t *wd, int64_t n_experts,
+                               int64_t n, int64_t k, const int32_t *counts,
+                               const int32_t *offsets, const int32_t *rows,
+                               float *y, hipStream_t stream);
+
+}  // namespace bqi

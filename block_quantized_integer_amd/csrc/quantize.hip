@@ -1,0 +1,124 @@
+// quantize.hip -- fp32/fp16 activations -> Q8_0 (32-element blocks, fp16
+// scale), the activation quantizer of the Q8_0 prefill path ("I wrote a custom
+// CUDA inference engine to run Qwen3.5-27B on a $130 mining card", section
+// Features) and the 8-bit activations of W4A8 ("A 35B Hybrid-Attention
+// Mixture-of-Experts Model on a 6GB 2011 GPU", Method 2).
+//
+// HBM-bound streaming kernel: 8 lanes own one 32-element block (each lane a
+// 16-byte fp32 / 8-byte fp16 vector), the block's absmax is reduced across
+// the 8 lanes, and each lane stores its 4 codes as one 32-bit word, so a wave
+// reads 1 KB (fp32) and writes 256 B of codes, all coalesced.
+//
+// Exactness: d = fp16_rne(amax / 127) uses HIP's correctly rounded fp32
+// division followed by the RNE conversion (equal to rounding the exact
+// quotient, because a correctly rounded fp32 quotient can never land on an
+// fp16 rounding midpoint it did not start on).  Codes use the correctly
+// rounded fp32 quotient x / d and round-half-away-from-zero; for |x| <= 2^24
+// ulps of d this decides the same integer as the exact rational quotient,
+// because a non-tie quotient is at least one fp32 half-ulp away from every
+// k + 1/2.  This file must not be compiled with fast-math.
+#include "bqi_device.h"
+#include "bqi_launch.h"
+
+namespace bqi {
+
+template <bool F16, typename Idx>
+__global__ __launch_bounds__(256) void k_quantize_q8_0(
+    const void *__restrict__ x, Idx ldx, Idx blocks_per_row, Idx total_blocks,
+    int8_t *__restrict__ q, uint16_t *__restrict__ d) {
+  const int sub = threadIdx.x & 7;  // this lane's 4-element slice of the block
+  const Idx stride = (Idx)((gridDim.x * (uint32_t)blockDim.x) >> 3);
+  for (Idx blk = (Idx)((blockIdx.x * (uint32_t)blockDim.x + threadIdx.x) >> 3);
+       blk < total_blocks; blk += stride) {
+    const Idx row = blk / blocks_per_row;
+    const Idx b = blk - row * blocks_per_row;
+    const Idx off = row * ldx + b * QK + sub * 4;
+    float v[4];
+    if constexpr (F16) {
+      const uint2 raw = *reinterpret_cast<const uint2 *>(
+          reinterpret_cast<const uint16_t *>(x) + off);
+      v[0] = half_bits_to_float((uint16_t)(raw.x & 0xffffu));
+      v[1] = half_bits_to_float((uint16_t)(raw.x >> 16));
+      v[2] = half_bits_to_float((uint16_t)(raw.y & 0xffffu));
+      v[3] = half_bits_to_float((uint16_t)(raw.y >> 16));
+    } else {
+      const f32x4 raw =
+          __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(
+              reinterpret_cast<const float *>(x) + off));
+      v[0] = raw.x;
+      v[1] = raw.y;
+      v[2] = raw.z;
+      v[3] = raw.w;
+    }
+    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])),
+                       fmaxf(fabsf(v[2]), fabsf(v[3])));
+    // reduce over the 8 lanes of this block (lanes differ in bits 0..2)
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));
+
+    const _Float16 dh = (_Float16)(amax / 127.0f);  // IEEE div, then RNE
+    const float dd = (float)dh;
+    uint32_t packed = 0;
+    if (dd != 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float t = roundf(v[i] / dd);  // half away from zero
+        t = fminf(fmaxf(t, -127.0f), 127.0f);
+        packed |= ((uint32_t)(int32_t)t & 0xffu) << (8 * i);
+      }
+    }
+    *reinterpret_cast<uint32_t *>(q + (size_t)blk * QK + sub * 4) = packed;
+    if (sub == 0)
+      d[blk] = dd != 0.0f ? __builtin_bit_cast(uint16_t, dh) : (uint16_t)0;
+  }
+}
+
+hipError_t launch_quantize_q8_0(const void *x, bool f16, int64_t rows,
+                                int64_t k, int64_t ldx, int8_t *q, uint16_t *d,
+                                hipStream_t stream) {
+  const int64_t bpr = k / QK;
+  const int64_t total = rows * bpr;
+  // 8 lanes per block; enough workgroups to cover the chip several times
+  // over, then grid-stride.
+  int64_t wgs = (total * 8 + 255) / 256;
+  const int64_t cap = 256 * 16;
+  if (wgs > cap) wgs = cap;
+  const dim3 grid((unsigned)wgs), block(256);
+  const bool small = rows * ldx < ((int64_t)1 << 31) && total < ((int64_t)1 << 28);
+  if (f16) {
+    if (small)
+      hipLaunchKernelGGL((k_quantize_q8_0<true, uint32_t>), grid, block, 0,
+                         stream, x, (uint32_t)ldx, (uint32_t)bpr,
+                         (uint32_t)total, q, d);
+    else
+      hipLaunchKernelGGL((k_quantize_q8_0<true, int64_t>), grid, block, 0,
+                         stream, x, ldx, bpr, total, q, d);
+  } else {
+    if (small)
+      hipLaunchKernelGGL((k_quantize_q8_0<false, uint32_t>), grid, block, 0,
+                         stream, x, (uint32_t)ldx, (uint32_t)bpr,
+                         (uint32_t)total, q, d);
+    else
+      hipLaunchKernelGGL((k_quantize_q8_0<false, int64_t>), grid, block, 0,
+                         stream, x, ldx, bpr, total, q, d);
+  }
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_zero_f32(float *__restrict__ y, int64_t count) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
+    y[i] = 0.0f;
+}
+
+// Zero-fill by a kernel rather than hipMemsetAsync, so that a caller may
+// capture the call in a HIP graph.
+hipError_t launch_zero_f32(float *y, int64_t count, hipStream_t stream) {
+  int64_t wgs = (count + 255) / 256;
+  if (wgs > 4096) wgs = 4096;
+  hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)wgs), dim3(256), 0, stream, y, count);
+  return hipGetLastError();
+}
+
+}  // namespace bqi

@@ -1,0 +1,174 @@
+/*
+ * bqi.h -- block-quantized integer GEMM/GEMV for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libbqi.so.  Every entry point takes plain pointers and sizes, is
+ * enqueued asynchronously on the caller's HIP stream, never allocates, frees
+ * or synchronizes, and returns a status code.  All argument checks happen on
+ * the host before any HIP call, so a rejected call launches nothing.
+ *
+ * Formats (the pages name them; the definitions below are this library's):
+ *
+ *  Q8_0  -- named as the format of the hand-written prefill GEMM in "I wrote a
+ *    custom CUDA inference engine to run Qwen3.5-27B on a $130 mining card"
+ *    (euno.news), section "Features", and of the benchmarked GGUF models in
+ *    section "Honest benchmark"; the axbrief.com article on the same engine,
+ *    section "DP4A kernels and 3-bit KV cache", describes the int8 DP4A GEMM.
+ *    A Q8_0 matrix with R rows and K columns (K a multiple of 32) is stored
+ *    planar: codes int8 [R][K] row-major, and scales as fp16 bit patterns
+ *    uint16 [R][K/32] row-major; element (r, c) represents
+ *    code[r][c] * scale[r][c/32].
+ *
+ *  W4 groups -- "group-wise symmetric 4-bit (Q4_0 family)" weights used with
+ *    8-bit activations, "A 35B Hybrid-Attention Mixture-of-Experts Model on a
+ *    6GB 2011 GPU: Hand-Written 4-bit CUDA Inference for Fermi" (gist.science
+ *    summary), Method 2; the grouped 4-bit GEMM for MoE routing is in its
+ *    Method 1.  A 4-bit matrix [R][K] is stored as packed codes uint8
+ *    [R][K/2] and fp16 scales uint16 [R][K/32].  Within each 32-element
+ *    group (16 bytes), byte j holds element j in its low nibble and element
+ *    j+16 in its high nibble.  Element value = (code - 8) * scale.
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers, allocated and owned by the caller.
+ *  - `stream` is a hipStream_t (NULL = the default stream).
+ *  - Zero-sized problems return BQI_OK without launching anything.
+ *  - Code arrays (int8 codes, packed nibbles) must be 16-byte aligned; scale
+ *    arrays 2-byte aligned; fp32 outputs 4-byte aligned.
+ *  - Results are deterministic: the same inputs give bit-identical outputs
+ *    (no atomics in any floating-point reduction).
+ *  - The library keeps no state between calls; calls are thread-safe.
+ */
+#ifndef BQI_H
+#define BQI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Symbols of this header are the only ones libbqi.so exports. */
+#if defined(__GNUC__) || defined(__clang__)
+#define BQI_API __attribute__((visibility("default")))
+#else
+#define BQI_API
+#endif
+
+/* status codes */
+#define BQI_OK 0
+#define BQI_EINVAL (-1) /* null pointer with nonzero size, bad dtype, workspace too small */
+#define BQI_ESHAPE (-2) /* negative size, K not a multiple of 32, ldx < k, size too large */
+#define BQI_EALIGN (-3) /* a pointer or leading dimension violates the alignment rules */
+#define BQI_EHIP (-4)   /* the HIP runtime reported an error at launch */
+
+/* activation dtypes for quantize_q8_0 */
+#define BQI_F32 0
+#define BQI_F16 1
+
+/* Human-readable name of a status code (static string, never NULL). */
+BQI_API const char *bqi_status_string(int status);
+
+/* ABI version of this header (major * 100 + minor). */
+BQI_API int bqi_abi_version(void);
+
+/*
+ * quantize_q8_0 -- activations to Q8_0 (the quantizer of the pages' Q8_0
+ * prefill path; page 1 "Features", page 3 Method 2 for the 8-bit activations
+ * of W4A8).
+ *
+ *   x      [rows][ldx] fp32 (x_dtype = BQI_F32) or fp16 (BQI_F16), row-major;
+ *          only the first k columns of each row are read.
+ *   q      [rows][k] int8 codes (output).
+ *   d      [rows][k/32] fp16 scale bits (output).
+ *
+ * Per row and 32-element block:  amax = max|x| (fp16 input widened exactly),
+ * d = fp16 round-to-nearest-even of (amax / 127) computed as an IEEE fp32
+ * division, q = clamp(round-half-away-from-zero(x / d), -127, 127) with x / d
+ * the exact quotient by the stored fp16 d; d == 0 gives q = 0 and scale bits
+ * 0x0000.  Subnormal scales are kept.  NaN/Inf inputs are outside the contract.
+ *
+ * Requirements: k % 32 == 0, ldx >= k; x 16-byte aligned and
+ * ldx * sizeof(element) a multiple of 16 (fp32) or 8 (fp16); q 16-byte aligned.
+ */
+BQI_API int quantize_q8_0(const void *x, int x_dtype, int64_t rows, int64_t k,
+                  int64_t ldx, int8_t *q, uint16_t *d, void *stream);
+
+/*
+ * qgemm_q8_0 -- y = A * W^T with both operands Q8_0 (the prefill GEMM of
+ * page 1 "Features" and the thin-M decode GEMM that page 3 "Results" names
+ * as the structural decode bottleneck).
+ *
+ *   aq [m][k] int8, ad [m][k/32] fp16 bits   -- activations A
+ *   wq [n][k] int8, wd [n][k/32] fp16 bits   -- weights W (PyTorch Linear
+ *                                               orientation: K contiguous)
+ *   y  [m][n] fp32 row-major (output)
+ *
+ * y[i][j] = sum_b wd[j][b] * ad[i][b] * P[i][j][b], where
+ * P[i][j][b] = sum_{t<32} aq[i][32b+t] * wq[j][32b+t] is the exact int32
+ * block dot product (any int8 code, -128 included, is accepted).  Each term
+ * is formed with at most one rounding and accumulated in fp32, each term
+ * passing through at most nb = k/32 additions, so
+ * |y - exact| <= (nb + 1) * 2^-24 * sum_b |term_b|  (below 1e-5 * sum|terms|
+ * for k <= 5312).
+ * m <= 16 runs the thin-M (decode) kernel, larger m the MFMA (prefill) kernel.
+ *
+ * Requirements: k % 32 == 0; aq, wq 16-byte aligned; y 4-byte aligned.
+ */
+BQI_API int qgemm_q8_0(const int8_t *aq, const uint16_t *ad, int64_t m,
+               const int8_t *wq, const uint16_t *wd, int64_t n, int64_t k,
+               float *y, void *stream);
+
+/*
+ * route_topk -- group routed rows by expert (the routing step of the grouped
+ * 4-bit GEMM for MoE routing, page 3 Method 1).
+ *
+ *   topk_ids [n_tokens][top_k] int32 expert ids; routed row r = t*top_k + j.
+ *   counts   [n_experts] int32 (output): rows routed to each expert.
+ *   offsets  [n_experts + 1] int32 (output): exclusive prefix sum of counts.
+ *   rows     [n_tokens*top_k] int32 (output): rows[offsets[e] .. offsets[e+1])
+ *            are the r with topk_ids[r] == e, in increasing r.  Entries past
+ *            offsets[n_experts] are left unwritten.
+ *
+ * Ids outside [0, n_experts) are skipped.  Deterministic (no atomics).
+ * Requirements: n_tokens * top_k < 2^31, n_experts <= 65536.
+ */
+BQI_API int route_topk(const int32_t *topk_ids, int64_t n_tokens, int64_t top_k,
+               int64_t n_experts, int32_t *counts, int32_t *offsets,
+               int32_t *rows, void *stream);
+
+/* Bytes of device workspace qgemm_w4a8_grouped needs for these sizes. */
+BQI_API size_t qgemm_w4a8_grouped_workspace_size(int64_t n_tokens, int64_t top_k,
+                                         int64_t n_experts);
+
+/*
+ * qgemm_w4a8_grouped -- expert-routed 4-bit-weight x Q8_0-activation GEMM
+ * (the grouped 4-bit GEMM for MoE routing of page 3 Method 1, with the
+ * W4A8 format of its Method 2).
+ *
+ *   aq [n_tokens][k] int8, ad [n_tokens][k/32] fp16 bits  -- Q8_0 activations
+ *   topk_ids [n_tokens][top_k] int32                       -- expert per slot
+ *   wq4 [n_experts][n][k/2] packed 4-bit codes, wd [n_experts][n][k/32] fp16
+ *   y  [n_tokens][top_k][n] fp32 (output), token-major in slot order
+ *   workspace: device memory of at least
+ *              qgemm_w4a8_grouped_workspace_size(...) bytes, 256-byte aligned;
+ *              its contents on entry do not matter and are overwritten.
+ *
+ * For routed row r = t*top_k + j with e = topk_ids[t][j]:
+ *   y[t][j][c] = sum_b wd[e][c][b] * ad[t][b] * sum_{u<32} (code[e][c][32b+u] - 8) * aq[t][32b+u]
+ * with the same per-term rounding and accumulation bound as qgemm_q8_0.
+ * Rows whose id is outside [0, n_experts) are written as 0.0f; duplicate ids
+ * within a token are legal and computed independently.
+ *
+ * Requirements: k % 32 == 0; aq and wq4 16-byte aligned; workspace 256-byte
+ * aligned; n_tokens * top_k < 2^31; n_experts <= 65536.
+ */
+BQI_API int qgemm_w4a8_grouped(const int8_t *aq, const uint16_t *ad, int64_t n_tokens,
+                       const int32_t *topk_ids, int64_t top_k,
+                       const uint8_t *wq4, const uint16_t *wd,
+                       int64_t n_experts, int64_t n, int64_t k, float *y,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BQI_H */

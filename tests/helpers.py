@@ -1,0 +1,55 @@
+"""Shared helpers for the GPU parity tests (no method arithmetic here)."""
+import os
+import sys
+
+import numpy as np
+
+QK = 32
+U = 2.0 ** -24
+
+
+def dev_tensor(a: np.ndarray, device="cuda:0"):
+    import torch
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def host(t) -> np.ndarray:
+    import torch
+    a = t.detach().cpu().numpy()
+    if t.dtype == torch.int16:
+        a = a.view(np.uint16)
+    return a
+
+
+def assert_within_bound(y_gpu, y_ref, asum, nb, what=""):
+    """|y_gpu - y_ref| <= (nb + 1) * 2^-24 * sum|terms| elementwise: the
+    library's stated worst case (each term rounded once, and each term passes
+    through at most nb accumulation roundings).  For nb <= 166 blocks
+    (K <= 5312) this is also below 1e-5 * sum|terms|."""
+    y_gpu = np.asarray(y_gpu, np.float64)
+    bound = (nb + 1) * U * (1.0 + 1e-3) * asum
+    err = np.abs(y_gpu - y_ref)
+    bad = err > bound
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError("%s: %d of %d outputs outside bound; first at %s: gpu %r ref %r "
+                             "asum %r err %r bound %r" % (what, int(bad.sum()), bad.size, tuple(i),
+                                                          y_gpu[tuple(i)], y_ref[tuple(i)],
+                                                          asum[tuple(i)], err[tuple(i)],
+                                                          bound[tuple(i)]))
+    return float((err / np.where(asum > 0, asum, 1)).max()) if err.size else 0.0
+
+
+def log(msg):
+    sys.stdout.write(msg + "\n")
+    sys.stdout.flush()
+
+
+def oracle_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))

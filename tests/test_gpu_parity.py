@@ -1,0 +1,369 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bar: bit-exact for quantized codes, scales, routing tables and per-block int32
+dot products; fp32 GEMM outputs within (nb + 1) * 2^-24 * sum|terms| of the
+oracle's exact fp64 value (below 1e-5 * sum|terms| for K <= 5312, which covers
+every workload; the K = 8192 test shape is held to the same (nb + 1) bound).
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from helpers import assert_within_bound, dev_tensor, host, log, oracle_threads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import block_quantized_integer_amd as bqi  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bqi.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def gpu_quantize(x_np):
+    q, d = bqi.quantize_q8_0(dev_tensor(x_np))
+    return q, d
+
+
+def check_quantize(x_np, what):
+    qg, dg = gpu_quantize(x_np)
+    qr, dr = oracle.quantize_q8_0(x_np)
+    qh, dh = host(qg), host(dg)
+    if not np.array_equal(dh, dr):
+        i = np.argwhere(dh != dr)[0]
+        raise AssertionError("%s: scale mismatch at %s gpu %#x oracle %#x" % (
+            what, tuple(i), dh[tuple(i)], dr[tuple(i)]))
+    if not np.array_equal(qh, qr):
+        i = np.argwhere(qh != qr)[0]
+        raise AssertionError("%s: code mismatch at %s gpu %d oracle %d" % (
+            what, tuple(i), qh[tuple(i)], qr[tuple(i)]))
+    return qg, dg, qr, dr
+
+
+# ---------------------------------------------------------------------------
+# quantize_q8_0
+# ---------------------------------------------------------------------------
+
+def test_quantize_golden_closed_forms():
+    from test_oracle import parse_golden
+    cases = parse_golden()
+    x = np.zeros((len(cases), 32), np.float32)
+    for i, c in enumerate(cases):
+        x[i, : len(c["x"])] = np.array(c["x"], np.float32)
+    qg, dg = gpu_quantize(x)
+    qh, dh = host(qg), host(dg)
+    for i, c in enumerate(cases):
+        assert int(dh[i, 0]) == c["d"], (c["name"], hex(int(dh[i, 0])))
+        want = np.zeros(32, np.int64)
+        want[: len(c["q"])] = c["q"]
+        assert np.array_equal(qh[i].astype(np.int64), want), c["name"]
+
+
+@pytest.mark.parametrize("shape", [(1, 32), (7, 96), (16, 256), (16, 4096), (33, 5120)])
+def test_quantize_bitexact_shapes(shape):
+    log("quantize %s" % (shape,))
+    check_quantize(W.normal("small", 20, shape, 1.0, seed=shape[0]), "normal%s" % (shape,))
+    check_quantize(W.activations("long", *shape, seed=shape[1]), "student-t%s" % (shape,))
+
+
+def test_quantize_scale_sweep():
+    """Blocks whose amax sweeps every fp32 exponent (subnormal fp16 scales,
+    underflow to 0, values near the fp16 overflow edge) with a stratified
+    set of mantissas, plus the low bits that decide fp16 rounding."""
+    hi = np.arange(0, 1 << 23, 1 << 15, dtype=np.uint32)
+    lo = np.arange(0, 64, dtype=np.uint32)
+    man = (hi[:, None] | lo[None, :]).ravel()
+    ex = np.arange(1, 149, dtype=np.uint32)  # amax < 2^22: amax/127 stays finite in fp16
+    bits = (ex[:, None] << 23 | man[None, :]).ravel()
+    amax = bits.view(np.float32)
+    x = np.zeros((amax.size, 32), np.float32)
+    x[:, 0] = amax
+    x[:, 1] = -amax * np.float32(0.5)
+    x[:, 2] = amax * np.float32(0.25)
+    log("quantize scale sweep: %d blocks" % amax.size)
+    check_quantize(x, "scale sweep")
+
+
+def test_quantize_near_ties():
+    """Values on and one ulp around every k + 1/2 for a spread of scales."""
+    g = np.random.default_rng(21)
+    blocks = []
+    for dbits in list(range(0x0001, 0x7bff, 97)):
+        dv = np.float32(np.array(dbits, np.uint16).view(np.float16))
+        if not np.isfinite(dv) or dv == 0 or dv * 127 > 3e38:
+            continue
+        ks = g.integers(0, 127, size=31)
+        t = ((ks + 0.5) * dv).astype(np.float32)
+        direction = g.choice([-1.0, 0.0, 1.0], size=31).astype(np.float32)
+        with np.errstate(invalid="ignore"):
+            t = np.where(direction == 0, t, np.nextafter(t, direction * np.float32(np.inf)))
+        t = t * g.choice([-1, 1], size=31).astype(np.float32)
+        blocks.append(np.concatenate([[np.float32(127) * dv], t]).astype(np.float32))
+    check_quantize(np.stack(blocks), "near ties")
+
+
+def test_quantize_fp16_input_and_ldx():
+    g = np.random.default_rng(22)
+    xh = (g.standard_normal((37, 136)) * 3).astype(np.float16)
+    xt = dev_tensor(xh.view(np.uint16)).view(torch.float16)
+    qg, dg = bqi.quantize_q8_0(xt[:, :128])  # ldx = 136 > k = 128
+    qr, dr = oracle.quantize_q8_0(xh, k=128)
+    assert np.array_equal(host(qg), qr) and np.array_equal(host(dg), dr)
+    xf = g.standard_normal((9, 200)).astype(np.float32)
+    qg, dg = bqi.quantize_q8_0(dev_tensor(xf)[:, :160])  # ldx = 200
+    qr, dr = oracle.quantize_q8_0(xf, k=160)
+    assert np.array_equal(host(qg), qr) and np.array_equal(host(dg), dr)
+
+
+def test_quantize_special_blocks():
+    x = np.zeros((5, 64), np.float32)
+    x[1] = -0.0
+    x[2] = 1e-10
+    x[3, :32] = np.float32(2.0 ** -20) * np.arange(32, dtype=np.float32)
+    x[4, 5] = 3.0
+    check_quantize(x, "special")
+
+
+# ---------------------------------------------------------------------------
+# qgemm_q8_0: both kernels, ragged shapes, full int8 range
+# ---------------------------------------------------------------------------
+
+def run_gemm(aq, ad, wq, wd):
+    y = bqi.qgemm_q8_0(dev_tensor(aq), dev_tensor(ad), dev_tensor(wq), dev_tensor(wd))
+    return host(y)
+
+
+SHAPES = [(1, 32, 1), (1, 96, 33), (2, 64, 100), (3, 160, 77), (4, 256, 512), (5, 4096, 40),
+          (8, 480, 129), (13, 8192, 17), (16, 256, 512), (17, 64, 31), (32, 32, 64),
+          (33, 96, 130), (100, 320, 257), (129, 160, 128), (256, 1024, 384), (300, 4160, 200)]
+
+
+@pytest.mark.parametrize("m,k,n", SHAPES)
+def test_qgemm_random_codes_full_range(m, k, n):
+    """Uniform int8 codes over -128..127 (the quantizer never emits -128, the
+    GEMM must still take it) with random normal-range scales."""
+    log("qgemm random codes m=%d k=%d n=%d" % (m, k, n))
+    aq = W.random_int8(0, 100 + m, (m, k), seed=k)
+    wq = W.random_int8(0, 200 + n, (n, k), seed=k)
+    ad = W.random_scales(0, 300 + m, (m, k // 32), seed=k)
+    wd = W.random_scales(0, 400 + n, (n, k // 32), seed=k)
+    y = run_gemm(aq, ad, wq, wd)
+    yr, asum = oracle.qgemm_q8_0(aq, ad, wq, wd, nthreads=oracle_threads())
+    assert_within_bound(y, yr, asum, k // 32, "m=%d k=%d n=%d" % (m, k, n))
+
+
+@pytest.mark.parametrize("m", [1, 5, 16, 40, 128])
+def test_block_dots_bitexact_probe(m):
+    """One-hot-block probe: each activation row has codes only in block
+    b = row % nb and all scales are powers of two, so y = 2^(ea+ew) * P_b is
+    exact in fp32 and P_b can be read back and compared bit-exactly with the
+    oracle's int32 block dot products."""
+    k, n = 256, 96
+    nb = k // 32
+    aq = W.random_int8(0, 500 + m, (m, k), seed=1)
+    mask = np.zeros((m, k), bool)
+    for i in range(m):
+        b = i % nb
+        mask[i, 32 * b: 32 * b + 32] = True
+    aq = np.where(mask, aq, 0).astype(np.int8)
+    wq = W.random_int8(0, 501, (n, k), seed=1)
+    ad = np.full((m, nb), 0x3400, np.uint16)    # 2^-2
+    wd = np.full((n, nb), 0x2C00, np.uint16)    # 2^-4
+    y = run_gemm(aq, ad, wq, wd)
+    P = oracle.block_dots(aq, wq)
+    want = np.stack([P[i, :, i % nb] for i in range(m)]).astype(np.int64)
+    got = y.astype(np.float64) * 64.0
+    assert np.array_equal(got, want.astype(np.float64))
+
+
+def test_qgemm_extreme_codes():
+    k = 5120
+    for code in (127, -128):
+        aq = np.full((20, k), code, np.int8)
+        wq = np.full((9, k), code, np.int8)
+        d1 = np.full((20, k // 32), 0x3C00, np.uint16)
+        d2 = np.full((9, k // 32), 0x3C00, np.uint16)
+        for m in (1, 20):
+            y = run_gemm(aq[:m], d1[:m], wq, d2)
+            assert (y == np.float32(code * code * k)).all()
+
+
+def test_qgemm_small_workload():
+    s = W.SMALL
+    _, _, qa, da = check_quantize(W.activations("small", s.m, s.k), "small A")
+    _, _, qw, dw = check_quantize(W.weights("small", s.n, s.k), "small W")
+    y = run_gemm(qa, da, qw, dw)
+    yr, asum = oracle.qgemm_q8_0(qa, da, qw, dw)
+    assert_within_bound(y, yr, asum, s.k // 32, "small")
+
+
+def test_qgemm_zero_k_and_empty():
+    y = torch.full((3, 5), 7.0, device="cuda:0")
+    e8 = torch.empty((3, 0), dtype=torch.int8, device="cuda:0")
+    e16 = torch.empty((3, 0), dtype=torch.int16, device="cuda:0")
+    w8 = torch.empty((5, 0), dtype=torch.int8, device="cuda:0")
+    w16 = torch.empty((5, 0), dtype=torch.int16, device="cuda:0")
+    bqi.qgemm_q8_0(e8, e16, w8, w16, y=y)
+    assert (host(y) == 0).all()
+
+
+def test_qgemm_deterministic():
+    aq = W.random_int8(0, 600, (700, 2048))
+    wq = W.random_int8(0, 601, (384, 2048))
+    ad = W.random_scales(0, 602, (700, 64))
+    wd = W.random_scales(0, 603, (384, 64))
+    a = [dev_tensor(v) for v in (aq, ad, wq, wd)]
+    y1 = host(bqi.qgemm_q8_0(*a))
+    y2 = host(bqi.qgemm_q8_0(*a))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    y3 = host(bqi.qgemm_q8_0(a[0][:7].contiguous(), a[1][:7].contiguous(), a[2], a[3]))
+    y4 = host(bqi.qgemm_q8_0(a[0][:7].contiguous(), a[1][:7].contiguous(), a[2], a[3]))
+    assert np.array_equal(y3.view(np.uint32), y4.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# the benchmark workloads at full size
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def decode_weights():
+    s = W.DECODE[0]
+    w = W.weights("decode", s.n, s.k)
+    qw_g, dw_g, qw, dw = check_quantize(w, "decode W")
+    return qw_g, dw_g, qw, dw
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_decode_workload_full(decode_weights, m):
+    log("decode M=%d" % m)
+    qw_g, dw_g, qw, dw = decode_weights
+    k = W.DECODE[0].k
+    a = W.activations("decode", m, k)
+    qa_g, da_g, qa, da = check_quantize(a, "decode A m=%d" % m)
+    y = host(bqi.qgemm_q8_0(qa_g, da_g, qw_g, dw_g))
+    yr, asum = oracle.qgemm_q8_0(qa, da, qw, dw, nthreads=oracle_threads())
+    assert_within_bound(y, yr, asum, k // 32, "decode m=%d" % m)
+
+
+def sampled_check(y, qa, da, qw, dw, k, seed, what, n_samples=4096):
+    g = np.random.default_rng(seed)
+    m, n = y.shape
+    mi = np.concatenate([g.integers(0, m, n_samples), np.full(n, m - 1), np.zeros(n, np.int64),
+                         np.arange(m), np.arange(m)])
+    nj = np.concatenate([g.integers(0, n, n_samples), np.arange(n), np.arange(n),
+                         np.zeros(m, np.int64), np.full(m, n - 1)])
+    yr, asum = oracle.qgemm_q8_0_at(qa, da, qw, dw, mi, nj)
+    assert_within_bound(y[mi, nj], yr, asum, k // 32, what)
+    assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("name", ["prefill", "long"])
+def test_prefill_workloads_sampled(name):
+    s = W.PREFILL if name == "prefill" else W.LONG
+    log("%s M=%d K=%d N=%d: generating" % (name, s.m, s.k, s.n))
+    qa_g, da_g, qa, da = check_quantize(W.activations(name, s.m, s.k), name + " A")
+    qw_g, dw_g, qw, dw = check_quantize(W.weights(name, s.n, s.k), name + " W")
+    log("%s: gemm" % name)
+    y = host(bqi.qgemm_q8_0(qa_g, da_g, qw_g, dw_g))
+    sampled_check(y, qa, da, qw, dw, s.k, 7, name)
+    # run-to-run determinism at full size
+    y2 = host(bqi.qgemm_q8_0(qa_g, da_g, qw_g, dw_g))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# routing and grouped W4A8
+# ---------------------------------------------------------------------------
+
+def check_route(ids, E):
+    counts, offsets, rows = bqi.route_topk(dev_tensor(ids), E)
+    cr, orr, rr, _ = oracle.route_topk(ids, E)
+    assert np.array_equal(host(counts), cr)
+    assert np.array_equal(host(offsets), orr)
+    assert np.array_equal(host(rows)[: len(rr)], rr)
+
+
+def test_route_topk_bitexact():
+    m = W.MOE
+    check_route(W.topk_ids(m.tokens, m.top_k, m.experts), m.experts)
+    ids = W.topk_ids(301, 4, 12, seed=5)
+    ids[3, 1] = -7
+    ids[10, 0] = 12
+    ids[11, 2] = ids[11, 1]
+    check_route(ids, 12)
+    check_route(np.zeros((1000, 1), np.int32), 3)          # one expert takes all
+    check_route(np.full((5, 2), 99, np.int32), 4)          # all invalid
+    check_route(np.zeros((0, 8), np.int32).reshape(0, 8), 16)
+
+
+def run_grouped(qa, da, ids, packed, wsc):
+    y = bqi.qgemm_w4a8_grouped(dev_tensor(qa), dev_tensor(da), dev_tensor(ids),
+                               dev_tensor(packed), dev_tensor(wsc))
+    return host(y)
+
+
+@pytest.mark.parametrize("case", ["small", "invalid_and_dups", "one_hot_expert", "big_expert",
+                                  "single"])
+def test_grouped_w4a8_cases(case):
+    g = np.random.default_rng(zlib.crc32(case.encode()))
+    if case == "small":
+        T, tk, E, K, N = 37, 4, 8, 128, 96
+        ids = W.topk_ids(T, tk, E, seed=2)
+    elif case == "invalid_and_dups":
+        T, tk, E, K, N = 50, 3, 6, 96, 130
+        ids = g.integers(0, E, (T, tk)).astype(np.int32)
+        ids[::7, 1] = -1
+        ids[::5, 2] = E + 2
+        ids[::3, 0] = ids[::3, 1]
+    elif case == "one_hot_expert":
+        T, tk, E, K, N = 64, 2, 16, 256, 64   # experts 0 and 1 only; 14 idle experts
+        ids = np.stack([np.zeros(T), np.ones(T)], 1).astype(np.int32)
+    elif case == "big_expert":
+        T, tk, E, K, N = 300, 1, 2, 160, 200  # 300 rows on one expert: several token chunks
+        ids = np.zeros((T, tk), np.int32)
+        ids[::4] = 1
+    else:
+        T, tk, E, K, N = 19, 1, 1, 64, 40
+        ids = np.zeros((T, tk), np.int32)
+    qa = W.random_int8("moe", 700, (T, K), seed=K)
+    da = W.random_scales("moe", 701, (T, K // 32), seed=K)
+    packed = g.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    wsc = W.random_scales("moe", 702, (E, N, K // 32), seed=K)
+    y = run_grouped(qa, da, ids, packed, wsc)
+    yr, asum = oracle.qgemm_w4a8_grouped(qa, da, ids, packed, wsc, nthreads=oracle_threads())
+    assert_within_bound(y, yr, asum, K // 32, case)
+    bad = (ids < 0) | (ids >= E)
+    assert (y[bad] == 0).all()
+
+
+@pytest.mark.parametrize("weights", ["quantized_normal", "uniform_codes"])
+def test_grouped_w4a8_moe_workload_full(weights):
+    m = W.MOE
+    log("moe workload (%s)" % weights)
+    ids = W.topk_ids(m.tokens, m.top_k, m.experts)
+    qa_g, da_g, qa, da = check_quantize(W.activations("moe", m.tokens, m.k), "moe A")
+    if weights == "quantized_normal":
+        w = W.weights("moe", m.n, m.k, experts=m.experts)
+        packed, wsc = oracle.quantize_w4(w.reshape(-1, m.k))
+        packed = packed.reshape(m.experts, m.n, m.k // 2)
+        wsc = wsc.reshape(m.experts, m.n, m.k // 32)
+    else:
+        packed, wsc = W.random_w4_codes(m.experts, m.n, m.k)
+    y = host(bqi.qgemm_w4a8_grouped(qa_g, da_g, dev_tensor(ids), dev_tensor(packed),
+                                    dev_tensor(wsc)))
+    log("moe: oracle")
+    yr, asum = oracle.qgemm_w4a8_grouped(qa, da, ids, packed, wsc, nthreads=oracle_threads())
+    assert_within_bound(y, yr, asum, m.k // 32, "moe " + weights)
+    y2 = host(bqi.qgemm_w4a8_grouped(qa_g, da_g, dev_tensor(ids), dev_tensor(packed),
+                                     dev_tensor(wsc)))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
