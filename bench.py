@@ -16,8 +16,12 @@ channels), the grouped W4A8 MoE GEMM (947 tokens, top-8 of 128 experts,
 K=2048, N=768) and the activation quantizer, each with its own roofline.
 
 "roofline" describes the dominant kernel of the step (the GEMV): achieved =
-algorithmic bytes per launch / mean launch duration, measured with HIP events
-recorded on the launch stream around each launch.
+algorithmic bytes per launch / mean launch duration, from HIP events recorded
+on the launch stream around a timed region of back-to-back launches.  Timed
+loops are captured once in a HIP graph and replayed (so Python launch
+overhead is not counted); each graph's output is first checked bit for bit
+against an eager run.  "eager_ms_per_step" is the same step launched from
+Python one call at a time.
 
 "cpu_baseline" times the CPU oracle (plain C, all host cores) on the same step
 for ~10 s; it is a reported baseline, not a target.
@@ -59,34 +63,51 @@ def log(msg):
 
 
 class Timer:
-    """Mean duration of one callable per launch, from HIP events recorded on
-    the current (launch) stream around every launch."""
+    """Mean duration per launch from HIP events recorded on the launch stream
+    around a timed region of back-to-back launches.  Launch-bound loops are
+    captured once in a HIP graph (torch.cuda.CUDAGraph) and replayed, so the
+    figure is GPU time, not Python launch overhead; every graph is first
+    replayed against an eager run and its output compared bit for bit."""
 
     def __init__(self, torch):
         self.torch = torch
 
-    def per_launch(self, fn, iters):
-        torch = self.torch
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(iters)]
-        torch.cuda.synchronize()
-        for i in range(iters):
-            ev[i][0].record()
-            fn(i)
-            ev[i][1].record()
-        torch.cuda.synchronize()
-        ms = np.array([a.elapsed_time(b) for a, b in ev])
-        return float(ms.mean()), float(np.median(ms)), ms
-
-    def loop(self, fn, iters):
+    def loop(self, fn, iters, graph=True, check=None):
         torch = self.torch
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if not graph:
+            torch.cuda.synchronize()
+            a.record()
+            for i in range(iters):
+                fn(i)
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / iters
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(3):
+                fn(i)              # warm up on the capture stream
+            fn(iters - 1)          # eager run of the graph's last launch
+        torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
+        if check is not None:
+            ref = check().clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(iters):
+                fn(i)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            g.replay()
+            torch.cuda.synchronize()
+            if check is not None and not torch.equal(check(), ref):
+                raise RuntimeError("graph replay %d differs from the eager result" % rep)
         a.record()
-        for i in range(iters):
-            fn(i)
+        g.replay()
         b.record()
         torch.cuda.synchronize()
+        del g
         return a.elapsed_time(b) / iters
 
 
@@ -133,10 +154,12 @@ def bench_headline(bqi, torch, W, args):
 
     for i in range(args.warmup):
         step(i)
+    torch.cuda.synchronize()
     T = Timer(torch)
-    ms_step = T.loop(step, args.steps)
-    gemv_mean, gemv_med, _ = T.per_launch(gemv, args.steps)
-    gemv_loop = T.loop(gemv, args.steps)
+    ms_step = T.loop(step, args.steps, check=lambda: y)
+    ms_step_eager = T.loop(step, args.steps, graph=False)
+    gemv_loop = T.loop(gemv, args.steps, check=lambda: y)
+    gemv_mean = gemv_loop
 
     w_bytes = s.n * s.k + s.n * (s.k // 32) * 2
     a_bytes = s.m * s.k + s.m * (s.k // 32) * 2
@@ -163,13 +186,14 @@ def bench_headline(bqi, torch, W, args):
                    "m": s.m, "k": s.k, "n": s.n, "weights": "Q8_0 of N(0,0.02)",
                    "activations": "N(0,1) fp32 quantized to Q8_0 in the step",
                    "weight_copies_rotated": copies, "bytes_per_step": step_bytes},
-        "roofline": {"bound": "hbm", "kernel": "k_gemv_thin<1>",
+        "roofline": {"bound": "hbm", "kernel": "k_gemv_reg<1,4>",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": gemv_bytes,
                      "mean_launch_us": round(gemv_mean * 1e3, 3),
-                     "median_launch_us": round(gemv_med * 1e3, 3),
-                     "back_to_back_us": round(gemv_loop * 1e3, 3)},
+                     "timing": "HIP events around %d back-to-back launches replayed "
+                               "from a HIP graph" % args.steps},
+        "eager_ms_per_step": round(ms_step_eager, 6),
     }
     ctx = dict(s=s, wq=wq, wd=wd, x=x, step_bytes=step_bytes)
     return res, ctx
@@ -188,10 +212,8 @@ def bench_gemm(bqi, torch, W, name, iters):
     _, wq, wd = device_q8(bqi, torch, s.n, s.k, 0.02, gen)
     y = torch.empty((s.m, s.n), dtype=torch.float32, device="cuda")
     T = Timer(torch)
-    for _ in range(3):
-        bqi.qgemm_q8_0(aq, ad, wq, wd, y)
-    mean, med, _ = T.per_launch(lambda i: bqi.qgemm_q8_0(aq, ad, wq, wd, y), iters)
-    qmean, _, _ = T.per_launch(lambda i: bqi.quantize_q8_0(xa, aq, ad), max(3, iters // 2))
+    mean = T.loop(lambda i: bqi.qgemm_q8_0(aq, ad, wq, wd, y), iters, check=lambda: y)
+    qmean = T.loop(lambda i: bqi.quantize_q8_0(xa, aq, ad), max(3, iters // 2), check=lambda: aq)
     ops = 2.0 * s.m * s.n * s.k
     tops = ops / (mean * 1e-3) / 1e12
     out_blocks = s.m * s.n * (s.k // 32)
@@ -202,7 +224,7 @@ def bench_gemm(bqi, torch, W, name, iters):
     return {
         "workload": "%s GEMM M=%d K=%d N=%d" % (name, s.m, s.k, s.n),
         "kernel": "k_gemm_mfma", "value": round(tops, 2), "unit": "int8-equiv TOPS",
-        "mean_launch_us": round(mean * 1e3, 2), "median_launch_us": round(med * 1e3, 2),
+        "mean_launch_us": round(mean * 1e3, 2),
         "frac_int8_mfma_peak": round(tops / INT8_PEAK_TOPS, 4),
         "epilogue_valu_frac": round(valu_ops / (mean * 1e-3) / VALU_LANE_OPS_PEAK, 4),
         "hbm_bytes_algorithmic": byt,
@@ -232,10 +254,8 @@ def bench_moe(bqi, torch, W, iters):
     ws = torch.empty(bqi.workspace_size(m.tokens, m.top_k, m.experts), dtype=torch.uint8,
                      device="cuda")
     fn = lambda i: bqi.qgemm_w4a8_grouped(aq, ad, ids, wq[i % copies], wd[i % copies], y, ws)
-    for i in range(3):
-        fn(i)
     T = Timer(torch)
-    mean, med, _ = T.per_launch(fn, iters)
+    mean = T.loop(fn, iters, check=lambda: y)
     R = m.tokens * m.top_k
     byt = (m.experts * m.n * (m.k // 2 + m.k // 32 * 2) + m.tokens * (m.k + m.k // 32 * 2)
            + R * 4 + R * m.n * 4)
@@ -244,7 +264,7 @@ def bench_moe(bqi, torch, W, iters):
     return {"workload": "grouped W4A8 T=%d top-%d E=%d K=%d N=%d" % (m.tokens, m.top_k, m.experts,
                                                                     m.k, m.n),
             "kernel": "k_route + k_grouped_w4a8", "value": round(gbs, 1), "unit": "GB/s",
-            "mean_call_us": round(mean * 1e3, 2), "median_call_us": round(med * 1e3, 2),
+            "mean_call_us": round(mean * 1e3, 2),
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "int8_equiv_TOPS": round(ops / (mean * 1e-3) / 1e12, 2),
             "weight_copies_rotated": copies, "hbm_bytes_algorithmic": byt}

@@ -5,16 +5,26 @@
 // inference engine...", Features; axbrief.com, "DP4A kernels and 3-bit KV
 // cache"), here v_dot4_i32_i8 on gfx950.
 //
-// The weights are streamed from HBM exactly once.  A group of LPR lanes (LPR =
-// 64 when k >= 4096) shares one weight row; each lane owns two consecutive
-// 32-element blocks (64 bytes = four 16-byte loads) per pass, so one wave-wide
-// load instruction covers 1 KB of a row and a row of 4 KB takes four.  Every
-// wave keeps R rows in flight.  The m <= 16 activation rows of the current
-// K chunk sit in LDS and are read once per R weight rows.
+// The weights are streamed from HBM exactly once, and the kernel is shaped
+// like a plain streaming read: every wave-wide load instruction fetches 1 KB
+// of one weight row (lane l takes bytes 16l..16l+15 of each 1 KB chunk), all
+// of a wave's weight loads are issued before any arithmetic, and nothing
+// waits on LDS or a barrier first.
 //
-// Per (row, block) the lane forms P = sum of 32 int8 products exactly (eight
-// dot4 ops), then acc = fma((float)P, da * dw, acc): the scale product of two
-// fp16 values is exact in fp32, so each term is rounded once, inside the fma.
+// k_gemv_reg (m <= 4, m * k <= 16 K codes): each wave owns two weight rows;
+// the activation rows are staged once per workgroup in LDS while the weight
+// loads are in flight, and read with the weights' lane mapping.  A lane
+// holds half of a 32-element block per chunk; it forms the half-block dot
+// product with four dot4 ops, and one DPP lane swap adds the partner half,
+// so every block's int32 P is exact before it is scaled.  Only even lanes
+// carry the block's scale (odd lanes scale by zero),
+// acc = fma((float)P, da * dw, acc) with the exact fp16 x fp16 product, and
+// each half-wave reduces one of the two rows with DPP steps.
+//
+// k_gemv_lds (larger m or k): the m <= 16 activation rows of the current K
+// chunk sit in LDS; a group of LPR lanes shares one weight row and each lane
+// owns two consecutive blocks (64 bytes) per pass.
+//
 // Lanes reduce their fp32 partials with a fixed butterfly, so results are
 // deterministic.
 #include "bqi_device.h"
@@ -31,7 +41,7 @@ struct ThinCfg {
 };
 
 template <int MT>
-__global__ __launch_bounds__(256) void k_gemv_thin(
+__global__ __launch_bounds__(256) void k_gemv_lds(
     const int8_t *__restrict__ aq, const uint16_t *__restrict__ ad, int m,
     const int8_t *__restrict__ wq, const uint16_t *__restrict__ wd, int n,
     int k, float *__restrict__ y, int lpr_log2) {
@@ -154,6 +164,183 @@ __global__ __launch_bounds__(256) void k_gemv_thin(
   }
 }
 
+
+// ---- m <= 4: coalesced 1 KB loads, two rows per wave -------------------------
+
+constexpr int REG_RPW = 2;             // weight rows per wave
+constexpr int REG_ACT_BYTES = 16384;   // m * k bytes of activation codes staged in LDS
+
+// v + (v from lane ^ 1): the DPP quad permutation [1,0,3,2]
+__device__ __forceinline__ int32_t add_partner_i32(int32_t v) {
+  return v + __builtin_amdgcn_mov_dpp(v, 0xb1, 0xf, 0xf, false);
+}
+
+// Sum over the 32 lanes of each half-wave; the result is valid in lanes 0
+// and 32.  Fixed order: four DPP steps inside rows of 16 lanes, then one
+// cross-row shuffle.
+__device__ __forceinline__ float half_wave_sum(float v) {
+  v += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, v), 0xb1, 0xf, 0xf, false));  // lane ^ 1
+  v += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, v), 0x4e, 0xf, 0xf, false));  // lane ^ 2
+  v += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, v), 0x141, 0xf, 0xf, false)); // half-row mirror
+  v += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, v), 0x140, 0xf, 0xf, false)); // row mirror
+  v += __shfl_xor(v, 16);
+  return v;
+}
+
+// (no __restrict__ on the inputs: with it the compiler may move the scale
+// loads across the memory clobber below, behind the barrier)
+template <int MT, int CH>
+__global__ __launch_bounds__(256) void k_gemv_reg(
+    const int8_t *aq, const uint16_t *ad, int m, const int8_t *wq,
+    const uint16_t *wd, int n, int k, float *y) {
+  static_assert(MT * CH * 1024 <= REG_ACT_BYTES, "activation stage too small");
+  // one spare 16-byte slot (and scale slot) takes the stores of lanes with
+  // nothing to stage, so the staging stores stay unconditional
+  __shared__ __attribute__((aligned(16))) int8_t sA[MT * CH * 1024 + 16];
+  __shared__ uint16_t sAd[MT * CH * 32 + 1];
+  const int lane = threadIdx.x & 63;
+  const int row0 = ((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * REG_RPW;
+  const int nbk = k / QK;
+  const bool even = (lane & 1) == 0;
+
+  // Load order matters: loads retire in order, so the activation codes (L2
+  // hits) are requested first, then all weight loads (HBM); writing the
+  // activations to LDS then waits only for the former.  Every load is
+  // unconditional (lanes past k re-read a valid address) so that none waits
+  // on another; values are masked afterwards.
+  constexpr int STAGE = MT * CH * 64 / 256;  // 16-byte activation chunks per thread
+  static_assert(STAGE >= 1 || MT * CH * 64 < 256, "");
+  constexpr int STAGE_N = STAGE > 0 ? STAGE : 1;
+  i32x4 st[STAGE_N];
+  uint16_t st_d[MT * CH * 32 / 256 > 0 ? MT * CH * 32 / 256 : 1];
+  constexpr int SD_N = MT * CH * 32 / 256 > 0 ? MT * CH * 32 / 256 : 1;
+#pragma unroll
+  for (int q = 0; q < STAGE_N; ++q) {
+    const int c = (int)threadIdx.x + 256 * q;
+    const int i = c / (CH * 64), cc = c % (CH * 64);
+    const bool ok = i < m && cc < k / 16;
+    st[q] = *reinterpret_cast<const i32x4 *>(aq + (ok ? (int64_t)i * k + 16 * cc : 0));
+  }
+#pragma unroll
+  for (int q = 0; q < SD_N; ++q) {
+    const int c = (int)threadIdx.x + 256 * q;
+    const int i = c / (CH * 32), b = c % (CH * 32);
+    const bool ok = i < m && b < nbk;
+    st_d[q] = ad[ok ? (int64_t)i * nbk + b : 0];
+  }
+
+  i32x4 w[REG_RPW][CH];
+  uint16_t dwh[REG_RPW][CH];
+#pragma unroll
+  for (int r = 0; r < REG_RPW; ++r) {
+    const int row = min(row0 + r, n - 1);
+    const i32x4 *src = reinterpret_cast<const i32x4 *>(wq + (int64_t)row * k);
+    const uint16_t *ws = wd + (int64_t)row * nbk;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const bool ok = 1024 * j + 16 * lane < k;
+      w[r][j] = __builtin_nontemporal_load(src + (ok ? 64 * j + lane : 0));
+      dwh[r][j] = __builtin_nontemporal_load(ws + (ok ? 32 * j + (lane >> 1) : 0));
+    }
+  }
+  // keep every weight load ahead of the LDS staging and the barrier (the
+  // memory clobber stops the compiler from sinking them to their uses)
+  __asm__ volatile("" ::: "memory");
+
+#pragma unroll
+  for (int q = 0; q < STAGE_N; ++q) {
+    const int c = (int)threadIdx.x + 256 * q;
+    const int i = c / (CH * 64), cc = c % (CH * 64);
+    const bool ok = c < MT * CH * 64 && i < m && cc < k / 16;
+    *reinterpret_cast<i32x4 *>(sA + (ok ? i * (CH * 1024) + 16 * cc : MT * CH * 1024)) = st[q];
+  }
+#pragma unroll
+  for (int q = 0; q < SD_N; ++q) {
+    const int c = (int)threadIdx.x + 256 * q;
+    const int i = c / (CH * 32), b = c % (CH * 32);
+    const bool ok = c < MT * CH * 32 && i < m && b < nbk;
+    sAd[ok ? i * (CH * 32) + b : MT * CH * 32] = st_d[q];
+  }
+  __syncthreads();
+
+  float acc[REG_RPW][MT];
+#pragma unroll
+  for (int r = 0; r < REG_RPW; ++r)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[r][i] = 0.0f;
+
+  // rows i >= m compute on whatever the stage holds and are never stored;
+  // keeping the loop unconditional keeps the weight loads where they are
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    {
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const bool ok = 1024 * j + 16 * lane < k;
+        // lanes past k read chunk 0 and scale by zero
+        const i32x4 a = *reinterpret_cast<const i32x4 *>(sA + i * (CH * 1024) + (ok ? 1024 * j + 16 * lane : 0));
+        const float das = half_bits_to_float(sAd[i * (CH * 32) + (ok ? 32 * j + (lane >> 1) : 0)]);
+        // odd lanes hold the second half of a block: they scale by zero so
+        // that each block is counted once
+        const float da = (ok && even) ? das : 0.0f;
+#pragma unroll
+        for (int r = 0; r < REG_RPW; ++r) {
+          int32_t ph = 0;
+          ph = dot4_i8(a.x, w[r][j].x, ph);
+          ph = dot4_i8(a.y, w[r][j].y, ph);
+          ph = dot4_i8(a.z, w[r][j].z, ph);
+          ph = dot4_i8(a.w, w[r][j].w, ph);
+          // the partner lane (l ^ 1) holds the other half of the same block
+          const int32_t p = add_partner_i32(ph);
+          const float dw = ok ? half_bits_to_float(dwh[r][j]) : 0.0f;
+          acc[r][i] = fmaf((float)p, da * dw, acc[r][i]);
+        }
+      }
+    }
+  }
+
+  // lanes 0..31 finish row 0, lanes 32..63 row 1
+  const bool lo = lane < 32;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    if (i < m) {
+      const float keep = lo ? acc[0][i] : acc[1][i];
+      const float give = lo ? acc[1][i] : acc[0][i];
+      const float v = half_wave_sum(keep + __shfl_xor(give, 32));
+      const int row = row0 + (lane >> 5);
+      if ((lane & 31) == 0 && row < n) y[(int64_t)i * n + row] = v;
+    }
+  }
+}
+
+template <int MT, int CH>
+hipError_t launch_reg(const int8_t *aq, const uint16_t *ad, int64_t m,
+                      const int8_t *wq, const uint16_t *wd, int64_t n, int64_t k,
+                      float *y, hipStream_t stream) {
+  const int64_t rows_per_wg = 4 * REG_RPW;
+  const int64_t wgs = (n + rows_per_wg - 1) / rows_per_wg;
+  hipLaunchKernelGGL((k_gemv_reg<MT, CH>), dim3((unsigned)wgs), dim3(256), 0,
+                     stream, aq, ad, (int)m, wq, wd, (int)n, (int)k, y);
+  return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_reg_ch(const int8_t *aq, const uint16_t *ad, int64_t m,
+                         const int8_t *wq, const uint16_t *wd, int64_t n,
+                         int64_t k, float *y, hipStream_t stream) {
+  const int64_t ch = (k + 1023) / 1024;
+  if (ch <= 1) return launch_reg<MT, 1>(aq, ad, m, wq, wd, n, k, y, stream);
+  if (ch <= 2) return launch_reg<MT, 2>(aq, ad, m, wq, wd, n, k, y, stream);
+  if (ch <= 4) return launch_reg<MT, 4>(aq, ad, m, wq, wd, n, k, y, stream);
+  if constexpr (MT <= 2) {
+    if (ch <= 8) return launch_reg<MT, 8>(aq, ad, m, wq, wd, n, k, y, stream);
+  }
+  if constexpr (MT <= 1) {
+    if (ch <= 16) return launch_reg<MT, 16>(aq, ad, m, wq, wd, n, k, y, stream);
+  }
+  return hipErrorInvalidValue;  // not reached: the dispatcher checks the size
+}
+
 template <int MT>
 hipError_t launch_mt(const int8_t *aq, const uint16_t *ad, int64_t m,
                      const int8_t *wq, const uint16_t *wd, int64_t n, int64_t k,
@@ -165,7 +352,7 @@ hipError_t launch_mt(const int8_t *aq, const uint16_t *ad, int64_t m,
   while ((1 << lpr_log2) < pairs && lpr_log2 < 6) ++lpr_log2;
   const int64_t rows_per_wg = 4 * (int64_t)ThinCfg<MT>::R * (64 >> lpr_log2);
   const int64_t wgs = (n + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL((k_gemv_thin<MT>), dim3((unsigned)wgs), dim3(256), 0,
+  hipLaunchKernelGGL((k_gemv_lds<MT>), dim3((unsigned)wgs), dim3(256), 0,
                      stream, aq, ad, (int)m, wq, wd, (int)n, (int)k, y,
                      lpr_log2);
   return hipGetLastError();
@@ -176,6 +363,12 @@ hipError_t launch_mt(const int8_t *aq, const uint16_t *ad, int64_t m,
 hipError_t launch_gemv_thin(const int8_t *aq, const uint16_t *ad, int64_t m,
                             const int8_t *wq, const uint16_t *wd, int64_t n,
                             int64_t k, float *y, hipStream_t stream) {
+  // register kernel while the activation slice fits in 64 VGPRs per lane
+  // register kernel while m * k activation codes fit its LDS stage
+  const int64_t ch = (k + 1023) / 1024;
+  if (m <= 1 && ch <= 16) return launch_reg_ch<1>(aq, ad, m, wq, wd, n, k, y, stream);
+  if (m <= 2 && ch <= 8) return launch_reg_ch<2>(aq, ad, m, wq, wd, n, k, y, stream);
+  if (m <= 4 && ch <= 4) return launch_reg_ch<4>(aq, ad, m, wq, wd, n, k, y, stream);
   if (m <= 1) return launch_mt<1>(aq, ad, m, wq, wd, n, k, y, stream);
   if (m <= 2) return launch_mt<2>(aq, ad, m, wq, wd, n, k, y, stream);
   if (m <= 4) return launch_mt<4>(aq, ad, m, wq, wd, n, k, y, stream);

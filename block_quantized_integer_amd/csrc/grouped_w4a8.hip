@@ -6,11 +6,12 @@
 // products with SSSE3 pmaddubsw; here the nibbles are unpacked in registers
 // straight into int8 MFMA operands.
 //
-// Routing (k_route): one workgroup per expert scans all routed ids; each
-// thread owns a contiguous slice, counts matches, and a single workgroup scan
-// places its matches in increasing row order.  The expert's offset is the
-// number of valid ids below it, so no cross-workgroup pass and no atomics are
-// needed and the result is deterministic.
+// Routing (k_route): one workgroup per expert reads all routed ids twice from
+// L2 with coalesced loads: first to count the valid ids below the expert (its
+// offset) and equal to it, then, staged in LDS, to place its rows: each
+// thread owns a contiguous slice and one workgroup scan orders the matches,
+// so rows come out in increasing row order.  No cross-workgroup pass and no
+// atomics are needed, and the result is deterministic.
 //
 // GEMM (k_grouped_w4a8): one workgroup per (expert, 128-column tile); each of
 // its 4 waves owns 32 output columns and loads those weight rows straight
@@ -52,43 +53,63 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int *s_tmp, int &total) 
   return wave_base + incl - v;
 }
 
+constexpr int ROUTE_CHUNK = 8192;  // ids staged in LDS per pass (32 KB)
+
 __global__ __launch_bounds__(ROUTE_THREADS) void k_route(
     const int32_t *__restrict__ ids, int rows_total, int n_experts,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ rows, float *__restrict__ y, int n) {
+  __shared__ int s_ids[ROUTE_CHUNK];
   __shared__ int s_tmp[ROUTE_THREADS / 64];
   const int e = blockIdx.x;
-  const int per = (rows_total + ROUTE_THREADS - 1) / ROUTE_THREADS;
-  const int r0 = min(rows_total, (int)threadIdx.x * per);
-  const int r1 = min(rows_total, r0 + per);
-  int eq = 0, below = 0;
-  for (int r = r0; r < r1; ++r) {
+  const int tid = threadIdx.x;
+
+  // pass 1: rows routed to experts below e (this expert's offset) and to e,
+  // with coalesced loads
+  int below = 0, eq = 0;
+  for (int r = tid; r < rows_total; r += ROUTE_THREADS) {
     const int v = ids[r];
-    eq += (v == e);
     below += (v >= 0 && v < e);
+    eq += (v == e);
   }
-  int n_eq, n_below;
-  int pos = wg_exclusive_scan(eq, s_tmp, n_eq);
+  int n_below, n_eq;
   (void)wg_exclusive_scan(below, s_tmp, n_below);
-  for (int r = r0; r < r1 && eq > 0; ++r) {
-    if (ids[r] == e) {
-      rows[n_below + pos] = r;
-      ++pos;
-      --eq;
-    }
-  }
-  if (threadIdx.x == 0) {
+  (void)wg_exclusive_scan(eq, s_tmp, n_eq);
+  if (tid == 0) {
     counts[e] = n_eq;
     offsets[e] = n_below;
     if (e == n_experts - 1) offsets[n_experts] = n_below + n_eq;
   }
-  // zero the output rows of invalid ids; workgroup e takes rows r = e (mod E)
-  if (y != nullptr) {
-    for (int r = e; r < rows_total; r += n_experts) {
-      const int v = ids[r];
-      if (v < 0 || v >= n_experts) {
-        for (int c = threadIdx.x; c < n; c += ROUTE_THREADS) y[(int64_t)r * n + c] = 0.0f;
+
+  // pass 2: stage ids chunk by chunk in LDS; each thread scans a contiguous
+  // slice, one workgroup scan orders the matches, so rows come out in
+  // increasing row index
+  int base = n_below;
+  for (int c0 = 0; c0 < rows_total; c0 += ROUTE_CHUNK) {
+    const int len = min(ROUTE_CHUNK, rows_total - c0);
+    for (int i = tid; i < len; i += ROUTE_THREADS) s_ids[i] = ids[c0 + i];
+    __syncthreads();
+    const int per = (len + ROUTE_THREADS - 1) / ROUTE_THREADS;
+    const int r0 = min(len, tid * per), r1 = min(len, r0 + per);
+    int mine = 0;
+    for (int r = r0; r < r1; ++r) mine += (s_ids[r] == e);
+    int total;
+    int pos = base + wg_exclusive_scan(mine, s_tmp, total);
+    for (int r = r0; r < r1 && mine > 0; ++r)
+      if (s_ids[r] == e) {
+        rows[pos++] = c0 + r;
+        --mine;
       }
+    base += total;
+    __syncthreads();
+  }
+
+  // zero the output rows of invalid ids; workgroup e checks rows r = e (mod E)
+  if (y != nullptr) {
+    for (int r = e + tid * n_experts; r < rows_total; r += ROUTE_THREADS * n_experts) {
+      const int v = ids[r];
+      if (v < 0 || v >= n_experts)
+        for (int c = 0; c < n; ++c) y[(int64_t)r * n + c] = 0.0f;
     }
   }
 }
