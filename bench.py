@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--only-headline", action="store_true", help="skip the secondary workloads")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--workloads", default="decode,prefill,long,moe",
+                   help="comma list of workloads to run (profiling); the JSON line "
+                        "is printed only when decode is among them")
     return p.parse_args()
 
 
@@ -308,19 +311,27 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     bqi.lib()
-    res, ctx = bench_headline(bqi, torch, W, args)
-    log("headline: %.1f GB/s per step, GEMV %.2f us (%.1f%% of HBM peak)" % (
-        res["value"], res["roofline"]["mean_launch_us"], 100 * res["roofline"]["frac"]))
-    del ctx["wq"], ctx["wd"]
-    torch.cuda.empty_cache()
+    wl = set(args.workloads.split(","))
+    res, ctx = None, None
+    if "decode" in wl:
+        res, ctx = bench_headline(bqi, torch, W, args)
+        log("headline: %.1f GB/s per step, GEMV %.2f us (%.1f%% of HBM peak)" % (
+            res["value"], res["roofline"]["mean_launch_us"], 100 * res["roofline"]["frac"]))
+        del ctx["wq"], ctx["wd"]
+        torch.cuda.empty_cache()
+    also = []
     if not args.only_headline:
-        also = []
         for name in ("prefill", "long"):
-            also.append(bench_gemm(bqi, torch, W, name, 20))
+            if name in wl:
+                also.append(bench_gemm(bqi, torch, W, name, 20))
+                log(json.dumps(also[-1]))
+                torch.cuda.empty_cache()
+        if "moe" in wl:
+            also.append(bench_moe(bqi, torch, W, 50))
             log(json.dumps(also[-1]))
-            torch.cuda.empty_cache()
-        also.append(bench_moe(bqi, torch, W, 50))
-        log(json.dumps(also[-1]))
+    if res is None:
+        return
+    if also:
         res["also"] = also
     if not args.no_cpu:
         log("cpu baseline (~%.0f s)" % args.cpu_seconds)

@@ -87,8 +87,10 @@ int qgemm_q8_0(const int8_t *aq, const uint16_t *ad, int64_t m,
   if (m <= 16)
     return hip_status(
         bqi::launch_gemv_thin(aq, ad, m, wq, wd, n, k, y, as_stream(stream)));
-  // the MFMA kernel indexes tiles and rows in 32-bit
-  if ((m + 127) / 128 * ((n + 127) / 128) > kI32Max) return BQI_ESHAPE;
+  // the MFMA kernel indexes tiles, rows and element offsets in 32-bit
+  if ((m + 127) / 128 * ((n + 127) / 128) > kI32Max || m * k > kI32Max ||
+      n * k > kI32Max)
+    return BQI_ESHAPE;
   return hip_status(
       bqi::launch_gemm_mfma(aq, ad, m, wq, wd, n, k, y, as_stream(stream)));
 }

@@ -6,19 +6,25 @@
 // tile for exactly one 32-element Q8_0 block.
 //
 // Tiling: a workgroup of 4 waves owns a 128x128 output tile; each wave a 64x64
-// quarter as 2x2 MFMA tiles.  K advances 64 elements (two Q8_0 blocks) per
-// stage; both operand tiles and their scales go through double-buffered,
-// XOR-swizzled LDS, with the next stage's global loads in flight while the
-// current stage computes.
+// quarter as 2x2 MFMA tiles.  K advances NBS = 4 blocks per stage through two
+// LDS buffers.  The operand tiles travel HBM -> LDS with gfx950's direct
+// loads (global_load_lds_dwordx4: each wave instruction fills 1 KB of LDS, 16
+// bytes per lane), so they occupy no registers and need no LDS stores; lane L
+// fetches the global chunk that the XOR swizzle assigns to LDS slot L.  Only
+// the scales pass through registers, where they are converted to fp32 once.
+// The loads of stage s+1 are in flight while stage s computes.
 //
-// Scale epilogue (per 32x32 tile and block), two fp32 VALU ops per output:
+// Scale epilogue (per 32x32 tile and block), two fp32 FMAs per output:
 //   the MFMA accumulator is seeded with the bit pattern of 1.5*2^23, so its
 //   int32 result reads as the fp32 value F = 1.5*2^23 + P exactly;
 //   t   = fma(F, dw, -1.5*2^23*dw)  = round(dw * P)   (dw is lane-uniform)
 //   acc = fma(t, da, acc)                               (da per register)
 // -1.5*2^23*dw is exact in fp32, so every term carries one rounding before
 // it joins the fp32 sum, and the result stays within
-// (nb + 1) * 2^-24 * sum|terms| of the exact value (nb = k/32).
+// (nb + 1) * 2^-24 * sum|terms| of the exact value (nb = k/32).  Both FMAs
+// are plain v_fma_f32 (the fp16-reading v_fma_mix_f32 issues at about half
+// the rate on gfx950).  The epilogue, not the MFMA, bounds this kernel: two
+// VALU ops per output and block against one MFMA per 32 MACs.
 //
 // Workgroup -> tile order: consecutive workgroup ids go to different XCDs, so
 // the ids are first remapped so each XCD walks a contiguous range of tiles,
@@ -32,25 +38,41 @@ namespace bqi {
 namespace {
 
 constexpr int BM = 128, BN = 128;  // output tile
-constexpr int BK = 64;             // K elements per stage (two blocks)
-constexpr int NBS = BK / QK;       // blocks per stage
+constexpr int NBS = 4;             // Q8_0 blocks per stage
+constexpr int BK = NBS * QK;       // K bytes per tile row per stage (128)
+constexpr int CPR = BK / 16;       // 16-byte chunks per tile row per stage (8)
 constexpr int GROUP_M = 8;
 constexpr int NUM_XCD = 8;
+constexpr int THREADS = 256;
+constexpr int ROWS_PER_LOAD = 64 / CPR;                      // rows filled by one wave load (8)
+constexpr int LOADS_PER_WAVE = BM / ROWS_PER_LOAD / 4;       // per operand tile (4)
+constexpr int SCALES_PER_THREAD = BM * NBS / THREADS;        // per operand (2)
 
-struct Stage {
-  i32x4 a[2];       // two 16-byte chunks of the A tile
-  i32x4 w[2];       // two 16-byte chunks of the W tile
-  uint16_t sa, sw; // one scale each
+static_assert(CPR == 8, "the swizzle assumes 8 chunks per row");
+
+// Physical 16-byte chunk of logical chunk c in tile row r.  Rows are 128 B
+// (32 of the 64 LDS banks); a fragment read has 16 lanes on 16 consecutive
+// rows at one logical chunk, and this swizzle spreads them over all banks.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void load_lds16(const void *gsrc, void *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void *)lds_wave_base, 16, 0, 0);
+}
+
+struct Tiles {
+  int8_t a[BM * BK];
+  int8_t w[BN * BK];
+  float ad[NBS][BM];  // [block][row]
+  float wd[BN][NBS];  // [col][block]
 };
 
-__global__ __launch_bounds__(256, 2) void k_gemm_mfma(
+__global__ __launch_bounds__(THREADS, 2) void k_gemm_mfma(
     const int8_t *__restrict__ aq, const uint16_t *__restrict__ ad, int m,
     const int8_t *__restrict__ wq, const uint16_t *__restrict__ wd, int n,
     int k, float *__restrict__ y, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) int8_t sA[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) int8_t sW[2][BN * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t sAd[2][NBS][BM];  // [block][row]
-  __shared__ __attribute__((aligned(16))) uint16_t sWd[2][BN][NBS];  // [col][block]
+  __shared__ __attribute__((aligned(16))) Tiles T[2];
 
   // ---- tile selection: XCD-contiguous ranges, grouped along M -------------
   const int tiles = tiles_m * tiles_n;
@@ -77,48 +99,42 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(
   const int nbk = k / QK;
   const int stages = (nbk + NBS - 1) / NBS;
 
-  // ---- global -> register staging assignment ------------------------------
-  // A/W tiles: 128 rows x 64 B = 512 chunks of 16 B; thread t takes chunks t
-  // and t+256 (row = c/4, column chunk = c%4).  Scales: 128 rows x 2 blocks
-  // = 256 values; thread t takes row t/2, block t%2.
-  const int8_t *a_src[2], *w_src[2];
-  int chunk_row[2], chunk_col[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = tid + 256 * h;
-    chunk_row[h] = c >> 2;
-    chunk_col[h] = c & 3;
-    const int ar = min(m0 + chunk_row[h], m - 1);
-    const int wr = min(n0 + chunk_row[h], n - 1);
-    a_src[h] = aq + (int64_t)ar * k + chunk_col[h] * 16;
-    w_src[h] = wq + (int64_t)wr * k + chunk_col[h] * 16;
-  }
-  const int s_row = tid >> 1, s_blk = tid & 1;
-  const uint16_t *ad_src = ad + (int64_t)min(m0 + s_row, m - 1) * nbk + s_blk;
-  const uint16_t *wd_src = wd + (int64_t)min(n0 + s_row, n - 1) * nbk + s_blk;
-
-  auto load_stage = [&](int s, Stage &st) {
+  // ---- stage loads -----------------------------------------------------------
+  // Wave load q fills tile rows rt .. rt+7 (rt = 8*(4*wave + q)); lane L lands
+  // in LDS slot L: row rt + L/8, physical chunk L%8, which holds logical chunk
+  // (L%8) ^ swizzle(row).  Rows past m (n) re-read the last row and chunks
+  // past k re-read chunk 0 (such blocks are never used), so every load stays
+  // in bounds.  Offsets are 32-bit (the ABI layer guarantees m*k, n*k < 2^31)
+  // and recomputed per stage rather than kept in registers.
+  uint16_t sa_reg[SCALES_PER_THREAD], sw_reg[SCALES_PER_THREAD];
+  auto issue_stage = [&](int s, int buf) {
     const int k0 = s * BK;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const bool ok = k0 + chunk_col[h] * 16 < k;
-      st.a[h] = ok ? *reinterpret_cast<const i32x4 *>(a_src[h] + k0) : i32x4{0, 0, 0, 0};
-      st.w[h] = ok ? *reinterpret_cast<const i32x4 *>(w_src[h] + k0) : i32x4{0, 0, 0, 0};
+    for (int q = 0; q < LOADS_PER_WAVE; ++q) {
+      const int rt = ROWS_PER_LOAD * (LOADS_PER_WAVE * wave + q);  // wave-uniform
+      const int r = rt + lane / CPR;
+      const int c = (lane % CPR) ^ ((r >> 1) & 7);
+      const int kk = k0 + 16 * c < k ? k0 + 16 * c : 0;
+      load_lds16(aq + (min(m0 + r, m - 1) * k + kk), &T[buf].a[rt * BK]);
+      load_lds16(wq + (min(n0 + r, n - 1) * k + kk), &T[buf].w[rt * BK]);
     }
-    const bool sok = s * NBS + s_blk < nbk;
-    st.sa = sok ? ad_src[s * NBS] : (uint16_t)0;
-    st.sw = sok ? wd_src[s * NBS] : (uint16_t)0;
-  };
-  auto store_stage = [&](int buf, const Stage &st) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = chunk_row[h];
-      const int pc = swz64(r, chunk_col[h]);
-      *reinterpret_cast<i32x4 *>(&sA[buf][r * BK + pc * 16]) = st.a[h];
-      *reinterpret_cast<i32x4 *>(&sW[buf][r * BK + pc * 16]) = st.w[h];
+    for (int h = 0; h < SCALES_PER_THREAD; ++h) {
+      const int c = tid + THREADS * h;
+      const int row = c / NBS, blk = c % NBS;
+      const int kb = s * NBS + blk < nbk ? s * NBS + blk : 0;
+      sa_reg[h] = ad[min(m0 + row, m - 1) * nbk + kb];
+      sw_reg[h] = wd[min(n0 + row, n - 1) * nbk + kb];
     }
-    sAd[buf][s_blk][s_row] = st.sa;
-    sWd[buf][s_row][s_blk] = st.sw;
+  };
+  auto store_scales = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < SCALES_PER_THREAD; ++h) {
+      const int c = tid + THREADS * h;
+      const int row = c / NBS, blk = c % NBS;
+      T[buf].ad[blk][row] = half_bits_to_float(sa_reg[h]);
+      T[buf].wd[row][blk] = half_bits_to_float(sw_reg[h]);
+    }
   };
 
   float acc[2][2][16];
@@ -133,68 +149,74 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(
 #pragma unroll
   for (int r = 0; r < 16; ++r) seed[r] = MAGIC_BITS;
 
-  Stage st;
-  load_stage(0, st);
-  store_stage(0, st);
+  issue_stage(0, 0);
+  store_scales(0);
+  __builtin_amdgcn_s_waitcnt(0);  // direct loads of stage 0 have landed
   __syncthreads();
 
   for (int s = 0; s < stages; ++s) {
     const int buf = s & 1;
-    if (s + 1 < stages) load_stage(s + 1, st);
+    const Tiles &TB = T[buf];
+    if (s + 1 < stages) issue_stage(s + 1, buf ^ 1);
 
-    // scales for this stage: lane-uniform dw of the lane's two columns
     float dwf[2][NBS];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int col = wn * 64 + j * 32 + l32;
-      const uint32_t two = *reinterpret_cast<const uint32_t *>(&sWd[buf][col][0]);
-      dwf[j][0] = half_bits_to_float((uint16_t)(two & 0xffffu));
-      dwf[j][1] = half_bits_to_float((uint16_t)(two >> 16));
+      const f32x4 four = *reinterpret_cast<const f32x4 *>(&TB.wd[wn * 64 + j * 32 + l32][0]);
+      dwf[j][0] = four.x;
+      dwf[j][1] = four.y;
+      dwf[j][2] = four.z;
+      dwf[j][3] = four.w;
     }
     const int nb_here = min(NBS, nbk - s * NBS);
+
+    i32x4 af[2], wf[2];
+    float da[2][16];
+    for (int b = 0; b < nb_here; ++b) {
 #pragma unroll
-    for (int b = 0; b < NBS; ++b) {
-      if (b < nb_here) {
-        i32x4 af[2], wf[2];
-        uint16_t dah[2][16];
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + l32;
+        af[i] = *reinterpret_cast<const i32x4 *>(&TB.a[r * BK + swz(r, 2 * b + g) * 16]);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int r = wm * 64 + i * 32 + l32;
-          af[i] = *reinterpret_cast<const i32x4 *>(&sA[buf][r * BK + swz64(r, 2 * b + g) * 16]);
-          // rows of this lane's 16 outputs: 8*q + 4*g + (0..3), q = 0..3
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint2 v = *reinterpret_cast<const uint2 *>(
-                &sAd[buf][b][wm * 64 + i * 32 + 8 * q + 4 * g]);
-            dah[i][4 * q + 0] = (uint16_t)(v.x & 0xffffu);
-            dah[i][4 * q + 1] = (uint16_t)(v.x >> 16);
-            dah[i][4 * q + 2] = (uint16_t)(v.y & 0xffffu);
-            dah[i][4 * q + 3] = (uint16_t)(v.y >> 16);
-          }
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = *reinterpret_cast<const f32x4 *>(&TB.ad[b][wm * 64 + i * 32 + 8 * q + 4 * g]);
+          da[i][4 * q + 0] = v.x;
+          da[i][4 * q + 1] = v.y;
+          da[i][4 * q + 2] = v.z;
+          da[i][4 * q + 3] = v.w;
         }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = wn * 64 + j * 32 + l32;
+        wf[j] = *reinterpret_cast<const i32x4 *>(&TB.w[c * BK + swz(c, 2 * b + g) * 16]);
+      }
+      // lane-uniform weight scale of this block (b is a runtime value here)
+      float dwb[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        dwb[j] = dwf[j][0];
+#pragma unroll
+        for (int bb = 1; bb < NBS; ++bb)
+          if (b == bb) dwb[j] = dwf[j][bb];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int c = wn * 64 + j * 32 + l32;
-          wf[j] = *reinterpret_cast<const i32x4 *>(&sW[buf][c * BK + swz64(c, 2 * b + g) * 16]);
-        }
+          const i32x16 d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], wf[j], seed, 0, 0, 0);
+          const float dw = dwb[j];
+          const float ncd = -MAGIC_F * dw;  // exact
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const i32x16 d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], wf[j], seed, 0, 0, 0);
-            const float dw = dwf[j][b];
-            const float ncd = -MAGIC_F * dw;  // exact
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float t = fmaf(bits_to_float(d[r]), dw, ncd);
-              acc[i][j][r] = fmaf(t, half_bits_to_float(dah[i][r]), acc[i][j][r]);
-            }
+          for (int r = 0; r < 16; ++r) {
+            const float t = fmaf(bits_to_float(d[r]), dw, ncd);
+            acc[i][j][r] = fmaf(t, da[i][r], acc[i][j][r]);
           }
-      }
+        }
     }
-    if (s + 1 < stages) {
-      store_stage(buf ^ 1, st);
-    }
+
+    if (s + 1 < stages) store_scales(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
     __syncthreads();
   }
 
@@ -221,7 +243,7 @@ hipError_t launch_gemm_mfma(const int8_t *aq, const uint16_t *ad, int64_t m,
                             int64_t k, float *y, hipStream_t stream) {
   const int tiles_m = (int)((m + BM - 1) / BM);
   const int tiles_n = (int)((n + BN - 1) / BN);
-  hipLaunchKernelGGL(k_gemm_mfma, dim3((unsigned)(tiles_m * tiles_n)), dim3(256),
+  hipLaunchKernelGGL(k_gemm_mfma, dim3((unsigned)(tiles_m * tiles_n)), dim3(THREADS),
                      0, stream, aq, ad, (int)m, wq, wd, (int)n, (int)k, y,
                      tiles_m, tiles_n);
   return hipGetLastError();
