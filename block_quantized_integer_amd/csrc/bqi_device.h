@@ -45,4 +45,28 @@ constexpr float MAGIC_F = 12582912.0f;
 // per 8 lanes.
 __device__ __forceinline__ int swz64(int r, int c) { return c ^ ((r >> 1) & 3); }
 
+// Direct global -> LDS load (gfx950 LDS DMA, 16 bytes per lane).  Lane L's
+// 16 bytes land at lds_wave_base + 16 * L
+// (lds_wave_base must be wave-uniform).  Issued through inline asm so that the
+// compiler does not track them: every kernel that uses them waits for them
+// explicitly (s_waitcnt vmcnt(0) and a barrier) before any wave reads the
+// destination.  Compiler-visible loads issued around them may then be waited
+// on more than necessary, never less.  M0 carries the LDS base; the leading
+// s_nop is the one wait state GFX9 requires between an SALU write of M0 and
+// an LDS DMA that reads it (the compiler places that write just before the
+// asm and cannot see the DMA inside it).
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ uint32_t lds_addr(const void *generic_lds_ptr) {
+  return (uint32_t)(uintptr_t)(const lds_char *)generic_lds_ptr;
+}
+
+__device__ __forceinline__ void dma_lds16(const void *gsrc, uint32_t lds_wave_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_wave_base))
+               : "memory");
+}
+
+
 }  // namespace bqi

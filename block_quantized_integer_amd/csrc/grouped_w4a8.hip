@@ -115,10 +115,18 @@ __global__ __launch_bounds__(ROUTE_THREADS) void k_route(
 }
 
 constexpr int GBN = 128;        // output columns per workgroup (4 waves x 32)
-constexpr int GBK = 128;        // K elements per stage (4 groups)
-constexpr int GNB = GBK / QK;   // groups per stage
+constexpr int GNB = 4;          // 32-element groups per stage
+constexpr int GBK = GNB * QK;   // activation bytes per row per stage (128)
 constexpr int MT_MAX = 3;       // 32-row token tiles per chunk
 constexpr int CHUNK = 32 * MT_MAX;
+constexpr int NSTAGE = 2;       // LDS double buffer; loads run one stage ahead
+constexpr int GTHREADS = 256;
+
+// Physical slot of the 16-byte activation chunk c of staged row r (rows of
+// 128 B; spreads a 16-lane fragment read over all 64 LDS banks).
+__device__ __forceinline__ int aswz(int r, int c) { return c ^ ((r >> 1) & 7); }
+// Physical slot of group b of weight column c (columns of 64 B = 4 groups).
+__device__ __forceinline__ int wswz(int c, int b) { return b ^ ((c >> 2) & 3); }
 
 // Unpack the 16 codes this lane feeds to the MFMA (low nibbles for lanes
 // 0..31 = elements 0..15 of the group, high nibbles for lanes 32..63 =
@@ -132,14 +140,57 @@ __device__ __forceinline__ i32x4 unpack_w4(const i32x4 p, int shift) {
   return r;
 }
 
-__global__ __launch_bounds__(256, 2) void k_grouped_w4a8(
+struct GStage {
+  int8_t a[CHUNK * GBK];      // gathered activation rows, swizzled 16-byte chunks
+  uint8_t w[GBN * GNB * 16];  // packed 4-bit weights: [col][group] 16 B, swizzled
+  float wd[GBN][GNB];         // weight scales, fp32, [col][group]
+  float ad[GNB][CHUNK];       // activation scales, fp32, [group][row]
+};
+
+// The MFMA work of one stage, read from LDS.
+__device__ __forceinline__ void grouped_stage_compute(
+    const GStage *__restrict__ SB, int nb_here, int mtiles, int col_l, int l32,
+    int g, const i32x16 &seed, float (&acc)[MT_MAX][16]) {
+#pragma unroll
+  for (int b = 0; b < GNB; ++b) {
+    if (b >= nb_here) break;
+    const int c = col_l;
+    const i32x4 packed = *reinterpret_cast<const i32x4 *>(&SB->w[c * (GNB * 16) + 16 * wswz(c, b)]);
+    const i32x4 wf = unpack_w4(packed, 4 * g);
+    const float dw = SB->wd[c][b];
+    const float ncd = -MAGIC_F * dw;
+#pragma unroll
+    for (int t = 0; t < MT_MAX; ++t) {
+      if (t < mtiles) {
+        const int r = t * 32 + l32;
+        const i32x4 af = *reinterpret_cast<const i32x4 *>(&SB->a[r * GBK + 16 * aswz(r, 2 * b + g)]);
+        const i32x16 d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, seed, 0, 0, 0);
+        float da[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = *reinterpret_cast<const f32x4 *>(&SB->ad[b][t * 32 + 8 * q + 4 * g]);
+          da[4 * q + 0] = v.x;
+          da[4 * q + 1] = v.y;
+          da[4 * q + 2] = v.z;
+          da[4 * q + 3] = v.w;
+        }
+#pragma unroll
+        for (int r2 = 0; r2 < 16; ++r2) {
+          const float tt = fmaf(bits_to_float(d[r2]), dw, ncd);
+          acc[t][r2] = fmaf(tt, da[r2], acc[t][r2]);
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(GTHREADS, 2) void k_grouped_w4a8(
     const int8_t *__restrict__ aq, const uint16_t *__restrict__ ad, int top_k,
     const uint8_t *__restrict__ wq4, const uint16_t *__restrict__ wd,
     int n_experts, int n, int k, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ rows,
     float *__restrict__ y) {
-  __shared__ __attribute__((aligned(16))) int8_t sA[2][CHUNK * GBK];  // [row][128 B], 16B chunks XOR-swizzled
-  __shared__ __attribute__((aligned(16))) uint16_t sAd[2][GNB][CHUNK];
+  __shared__ __attribute__((aligned(16))) GStage S[NSTAGE];
   __shared__ int s_tok[CHUNK];   // token index of each staged row
   __shared__ int s_row[CHUNK];   // routed row index (output row)
 
@@ -155,10 +206,9 @@ __global__ __launch_bounds__(256, 2) void k_grouped_w4a8(
   const int l32 = lane & 31, g = lane >> 5;
   const int nbk = k / QK;
   const int stages = (nbk + GNB - 1) / GNB;
-  const int col = tn * GBN + wave * 32 + l32;           // this lane's output column
-  const int wrow = min(col, n - 1);
-  const uint8_t *wsrc = wq4 + ((int64_t)e * n + wrow) * (k / 2);
-  const uint16_t *wdsrc = wd + ((int64_t)e * n + wrow) * nbk;
+  const int n0 = tn * GBN;
+  const int col_l = wave * 32 + l32;  // this lane's output column within the tile
+  const int64_t wrow0 = (int64_t)e * n;
 
   i32x16 seed;
 #pragma unroll
@@ -169,55 +219,65 @@ __global__ __launch_bounds__(256, 2) void k_grouped_w4a8(
     const int mtiles = (crows + 31) / 32;
     __syncthreads();
     if (tid < CHUNK) {
-      const int rr = tid < crows ? rows[off + c0 + tid] : rows[off + c0];
+      const int rr = rows[off + c0 + min(tid, crows - 1)];
       s_row[tid] = rr;
       s_tok[tid] = rr / top_k;
     }
     __syncthreads();
 
-    // staging: activation rows (CHUNK x 128 B = 768 chunks of 16 B), scales
-    // (CHUNK x 4 groups), and this lane's weight bytes (4 groups x 16 B)
-    i32x4 a_st[3];
-    uint16_t s_st[2];
-    i32x4 w_st[GNB];
-    uint16_t wd_st[GNB];
-    auto load_stage = [&](int s) {
-      const int k0 = s * GBK;
+    // ---- stage loads ------------------------------------------------------
+    // activations: 96 rows x 8 chunks = 12 wave loads (3 per wave); lane L of
+    // load q fills row 8*(3*wave+q) + L/8, slot L%8 = chunk (L%8)^swizzle.
+    // weights: 128 columns x 4 groups = 8 wave loads (2 per wave); lane L of
+    // load q fills column 16*(2*wave+q) + L/4, slot L%4 = group (L%4)^swizzle.
+    // scales (activation: 96 rows x 4 groups, weight: 128 columns x 4
+    // groups) go through registers, 2 + 2 fp16 per thread, and are stored to
+    // LDS as fp32.  Per stage each wave issues 4 scale loads into registers
+    // (issue_scales) and 5 direct LDS loads (issue_direct).
+    uint16_t sa_reg[2], sw_reg[2];
+    auto issue_scales = [&](int s) {
+      const int g0 = min(s, stages - 1) * GNB;
 #pragma unroll
-      for (int h = 0; h < 3; ++h) {
-        const int c = tid + 256 * h;
-        const int r = c >> 3, cc = c & 7;
-        const bool ok = r < crows && k0 + cc * 16 < k;
-        a_st[h] = ok ? *reinterpret_cast<const i32x4 *>(aq + (int64_t)s_tok[r] * k + k0 + cc * 16)
-                     : i32x4{0, 0, 0, 0};
+      for (int h = 0; h < 2; ++h) {
+        const int idx = tid + GTHREADS * h;  // CHUNK*GNB = 384 entries
+        const int r = min(idx / GNB, CHUNK - 1), b = idx % GNB;
+        const int gb = g0 + b < nbk ? g0 + b : 0;
+        sa_reg[h] = ad[(int64_t)s_tok[r] * nbk + gb];
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int c = tid + 256 * h;  // CHUNK*GNB = 384 scale slots
-        const int r = c >> 2, b = c & 3;
-        const bool ok = c < CHUNK * GNB && r < crows && s * GNB + b < nbk;
-        s_st[h] = ok ? ad[(int64_t)s_tok[r] * nbk + s * GNB + b] : (uint16_t)0;
-      }
-#pragma unroll
-      for (int b = 0; b < GNB; ++b) {
-        const bool ok = s * GNB + b < nbk;
-        w_st[b] = ok ? __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(
-                           wsrc + (int64_t)(s * GNB + b) * (QK / 2)))
-                     : i32x4{0, 0, 0, 0};
-        wd_st[b] = ok ? wdsrc[s * GNB + b] : (uint16_t)0;
+        const int idx = tid + GTHREADS * h;  // GBN*GNB = 512 entries
+        const int c = idx / GNB, b = idx % GNB;
+        const int gb = g0 + b < nbk ? g0 + b : 0;
+        sw_reg[h] = wd[(wrow0 + min(n0 + c, n - 1)) * nbk + gb];
       }
     };
-    auto store_stage = [&](int buf) {
-#pragma unroll
-      for (int h = 0; h < 3; ++h) {
-        const int c = tid + 256 * h;
-        const int r = c >> 3, cc = c & 7;
-        *reinterpret_cast<i32x4 *>(&sA[buf][r * GBK + ((cc ^ (r & 7)) * 16)]) = a_st[h];
-      }
+    auto store_scales = [&](int slot) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int c = tid + 256 * h;
-        if (c < CHUNK * GNB) sAd[buf][c & 3][c >> 2] = s_st[h];
+        const int idx = tid + GTHREADS * h;
+        if (idx < CHUNK * GNB) S[slot].ad[idx % GNB][idx / GNB] = half_bits_to_float(sa_reg[h]);
+        S[slot].wd[idx / GNB][idx % GNB] = half_bits_to_float(sw_reg[h]);
+      }
+    };
+    auto issue_direct = [&](int s, int slot) {
+      const int g0 = min(s, stages - 1) * GNB;
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        const int rt = 8 * (3 * wave + q);
+        const int r = rt + lane / 8;
+        const int c = (lane % 8) ^ ((r >> 1) & 7);
+        const int kk = 32 * g0 + 16 * c < k ? 32 * g0 + 16 * c : 0;
+        dma_lds16(aq + ((int64_t)s_tok[r] * k + kk), lds_addr(&S[slot].a[rt * GBK]));
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int ct = 16 * (2 * wave + q);
+        const int c = ct + lane / 4;
+        const int b = (lane % 4) ^ ((c >> 2) & 3);
+        const int gb = g0 + b < nbk ? g0 + b : 0;
+        const int64_t wr = wrow0 + min(n0 + c, n - 1);
+        dma_lds16(wq4 + (wr * (k / 2) + 16 * gb), lds_addr(&S[slot].w[ct * (GNB * 16)]));
       }
     };
 
@@ -227,64 +287,37 @@ __global__ __launch_bounds__(256, 2) void k_grouped_w4a8(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
 
-    load_stage(0);
-    store_stage(0);
-    i32x4 w_cur[GNB];
-    uint16_t wd_cur[GNB];
-#pragma unroll
-    for (int b = 0; b < GNB; ++b) {
-      w_cur[b] = w_st[b];
-      wd_cur[b] = wd_st[b];
-    }
+    // prologue: stage 0 in LDS
+    issue_scales(0);
+    issue_direct(0, 0);
+    store_scales(0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int s = 0; s < stages; ++s) {
       const int buf = s & 1;
-      if (s + 1 < stages) load_stage(s + 1);
-      const int nb_here = min(GNB, nbk - s * GNB);
-#pragma unroll
-      for (int b = 0; b < GNB; ++b) {
-        if (b < nb_here) {
-          const i32x4 wf = unpack_w4(w_cur[b], 4 * g);
-          const float dw = half_bits_to_float(wd_cur[b]);
-          const float ncd = -MAGIC_F * dw;
-#pragma unroll
-          for (int t = 0; t < MT_MAX; ++t) {
-            if (t < mtiles) {
-              const int r = t * 32 + l32;
-              const i32x4 af = *reinterpret_cast<const i32x4 *>(
-                  &sA[buf][r * GBK + (((2 * b + g) ^ (r & 7)) * 16)]);
-              const i32x16 d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, seed, 0, 0, 0);
-              uint16_t dah[16];
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const uint2 v = *reinterpret_cast<const uint2 *>(&sAd[buf][b][t * 32 + 8 * q + 4 * g]);
-                dah[4 * q + 0] = (uint16_t)(v.x & 0xffffu);
-                dah[4 * q + 1] = (uint16_t)(v.x >> 16);
-                dah[4 * q + 2] = (uint16_t)(v.y & 0xffffu);
-                dah[4 * q + 3] = (uint16_t)(v.y >> 16);
-              }
-#pragma unroll
-              for (int r2 = 0; r2 < 16; ++r2) {
-                const float tt = fmaf(bits_to_float(d[r2]), dw, ncd);
-                acc[t][r2] = fmaf(tt, half_bits_to_float(dah[r2]), acc[t][r2]);
-              }
-            }
-          }
-        }
+      // stage s+1: scale loads first (loads retire in order, so storing the
+      // scales waits only for them), then the direct loads, which run while
+      // stage s computes
+      // (Ordering rests on the explicit wait and barrier below: stage s reads
+      // buffer buf, loaded and waited for one iteration earlier, while these
+      // direct loads fill buf ^ 1.)
+      const bool more = s + 1 < stages;
+      if (more) {
+        issue_scales(s + 1);
+        issue_direct(s + 1, buf ^ 1);
       }
-      if (s + 1 < stages) {
-        store_stage(buf ^ 1);
-#pragma unroll
-        for (int b = 0; b < GNB; ++b) {
-          w_cur[b] = w_st[b];
-          wd_cur[b] = wd_st[b];
-        }
-      }
+      grouped_stage_compute(&S[buf], min(GNB, nbk - s * GNB), mtiles, col_l, l32, g, seed, acc);
+      if (more) store_scales(buf ^ 1);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of stage s+1 have landed
       __syncthreads();
     }
+    // drain: no direct load may still target LDS when the next chunk (or the
+    // next workgroup on this CU) reuses it
+    __builtin_amdgcn_s_waitcnt(0);
 
-    // store: lane's column `col`, rows t*32 + 8q + 4g + (0..3) of the chunk
+    // store: lane's column, rows t*32 + 8q + 4g + (0..3) of the chunk
+    const int col = n0 + col_l;
     if (col < n) {
 #pragma unroll
       for (int t = 0; t < MT_MAX; ++t) {
