@@ -56,7 +56,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--workloads", default="decode,prefill,long,moe",
                    help="comma list of workloads to run (profiling); the JSON line "
-                        "is printed only when decode is among them")
+                        "is printed only when decode is among them.  'copy' (never a "
+                        "default) runs a plain device copy of known size, the "
+                        "reference that HBM byte counters are scaled by")
     return p.parse_args()
 
 
@@ -112,6 +114,49 @@ class Timer:
         torch.cuda.synchronize()
         del g
         return a.elapsed_time(b) / iters
+
+
+CSRC = os.path.join(ROOT, "block_quantized_integer_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def sources_sha256(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic(key):
+    """Measured HBM bytes per launch of one kernel on one workload, from the
+    rocprofv3 FETCH_SIZE and WRITE_SIZE passes recorded in profiles/traffic.json
+    (each scaled by the factor that a plain copy of known size gives the same
+    counter).  None when no record exists or when the kernel's sources have
+    changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("sources_sha256") != sources_sha256(rec["sources"]):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def bench_copy(torch):
+    """A plain device copy of known size (512 MiB read + 512 MiB written per
+    launch): the calibration that FETCH_SIZE / WRITE_SIZE are scaled by."""
+    n = 128 << 20
+    x = torch.randn(n, device="cuda", dtype=torch.float32)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    log("copy calibration: 5 launches of neg over %d fp32 (%d bytes read, %d written each)"
+        % (n, 4 * n, 4 * n))
 
 
 def device_q8(bqi, torch, rows, k, std, gen, t_dist=False, outlier_cols=None):
@@ -191,7 +236,8 @@ def bench_headline(bqi, torch, W, args):
                    "weight_copies_rotated": copies, "bytes_per_step": step_bytes},
         "roofline": {"bound": "hbm", "kernel": "k_gemv_reg<1,4>",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic("k_gemv_reg<1,4> decode M=1"),
                      "bytes_per_launch": gemv_bytes,
                      "mean_launch_us": round(gemv_mean * 1e3, 3),
                      "timing": "HIP events around %d back-to-back launches replayed "
@@ -231,6 +277,7 @@ def bench_gemm(bqi, torch, W, name, iters):
         "frac_int8_mfma_peak": round(tops / INT8_PEAK_TOPS, 4),
         "epilogue_valu_frac": round(valu_ops / (mean * 1e-3) / VALU_LANE_OPS_PEAK, 4),
         "hbm_bytes_algorithmic": byt,
+        "hbm_bytes_measured": traffic("k_gemm_mfma %s" % name),
         "quantize": {"kernel": "k_quantize_q8_0", "mean_launch_us": round(qmean * 1e3, 2),
                      "GB/s": round(qbytes / (qmean * 1e-3) / 1e9, 1),
                      "frac_hbm_peak": round(qbytes / (qmean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
@@ -270,7 +317,8 @@ def bench_moe(bqi, torch, W, iters):
             "mean_call_us": round(mean * 1e3, 2),
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "int8_equiv_TOPS": round(ops / (mean * 1e-3) / 1e12, 2),
-            "weight_copies_rotated": copies, "hbm_bytes_algorithmic": byt}
+            "weight_copies_rotated": copies, "hbm_bytes_algorithmic": byt,
+            "hbm_bytes_measured": traffic("k_grouped_w4a8 moe")}
 
 
 def cpu_baseline(W, step_bytes, seconds):
@@ -313,6 +361,8 @@ def main():
     bqi.lib()
     wl = set(args.workloads.split(","))
     res, ctx = None, None
+    if "copy" in wl:
+        bench_copy(torch)
     if "decode" in wl:
         res, ctx = bench_headline(bqi, torch, W, args)
         log("headline: %.1f GB/s per step, GEMV %.2f us (%.1f%% of HBM peak)" % (
