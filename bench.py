@@ -301,7 +301,7 @@ def bench_moe(bqi, torch, W, iters):
         mant = torch.rand((m.experts, m.n, m.k // 32), generator=gen, device="cuda") + 1.0
         wd.append(torch.ldexp(mant, e.float()).half().view(torch.int16))
     y = torch.empty((m.tokens, m.top_k, m.n), dtype=torch.float32, device="cuda")
-    ws = torch.empty(bqi.workspace_size(m.tokens, m.top_k, m.experts), dtype=torch.uint8,
+    ws = torch.empty(bqi.workspace_size(m.tokens, m.top_k, m.experts, m.k), dtype=torch.uint8,
                      device="cuda")
     fn = lambda i: bqi.qgemm_w4a8_grouped(aq, ad, ids, wq[i % copies], wd[i % copies], y, ws)
     T = Timer(torch)

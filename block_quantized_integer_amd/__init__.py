@@ -59,7 +59,7 @@ def lib() -> C.CDLL:
     L.route_topk.restype = I32
     L.route_topk.argtypes = [P, I64, I64, I64, P, P, P, P]
     L.qgemm_w4a8_grouped_workspace_size.restype = C.c_size_t
-    L.qgemm_w4a8_grouped_workspace_size.argtypes = [I64, I64, I64]
+    L.qgemm_w4a8_grouped_workspace_size.argtypes = [I64, I64, I64, I64]
     L.qgemm_w4a8_grouped.restype = I32
     L.qgemm_w4a8_grouped.argtypes = [P, P, I64, P, I64, P, P, I64, I64, I64, P, P,
                                      C.c_size_t, P]
@@ -166,8 +166,8 @@ def route_topk(topk_ids, n_experts, counts=None, offsets=None, rows=None, stream
     return counts, offsets, rows
 
 
-def workspace_size(n_tokens, top_k, n_experts) -> int:
-    return int(lib().qgemm_w4a8_grouped_workspace_size(n_tokens, top_k, n_experts))
+def workspace_size(n_tokens, top_k, n_experts, k) -> int:
+    return int(lib().qgemm_w4a8_grouped_workspace_size(n_tokens, top_k, n_experts, k))
 
 
 def qgemm_w4a8_grouped(aq, ad, topk_ids, wq4, wd, y=None, workspace=None, stream=None):
@@ -188,7 +188,7 @@ def qgemm_w4a8_grouped(aq, ad, topk_ids, wq4, wd, y=None, workspace=None, stream
     if y is None:
         y = torch.empty((T, top_k, N), dtype=torch.float32, device=aq.device)
     _check(y, torch.float32, 3, "y")
-    need = workspace_size(T, top_k, E)
+    need = workspace_size(T, top_k, E, K)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=aq.device)
     if workspace.numel() < need:

@@ -2,13 +2,15 @@
 // argument validation, then dispatch to the gfx950 kernels.  Validation runs
 // before any HIP call, so a rejected call touches neither the device nor the
 // stream and can be exercised on a machine without a GPU.
-#include "../../include/bqi.h"
+#include "bqi.h"
 #include "bqi_launch.h"
 
 namespace {
 
 constexpr int64_t kQK = 32;
 constexpr int64_t kI32Max = 0x7fffffffLL;
+// routed rows (n_tokens * top_k) accepted by route_topk and the grouped GEMM
+constexpr int64_t kMaxRouted = 1LL << 30;
 
 bool aligned(const void *p, uintptr_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
@@ -19,19 +21,22 @@ int hip_status(hipError_t e) { return e == hipSuccess ? BQI_OK : BQI_EHIP; }
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
 // Workspace layout of qgemm_w4a8_grouped: counts[E], offsets[E+1],
-// rows[T*top_k] (int32), each section starting on a 256-byte boundary.
+// rows[T*top_k] (int32), then the expert-ordered fp32 activation-scale table
+// [k/32][grouped_ad32_rows(T*top_k)]; each section starts on a 256-byte
+// boundary.
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t counts, offsets, rows, total;
+  size_t counts, offsets, rows, ad32t, total;
 };
 
-WsLayout ws_layout(int64_t rows_total, int64_t n_experts) {
+WsLayout ws_layout(int64_t rows_total, int64_t n_experts, int64_t k) {
   WsLayout L;
   L.counts = 0;
   L.offsets = round256((size_t)n_experts * 4);
   L.rows = L.offsets + round256((size_t)(n_experts + 1) * 4);
-  L.total = L.rows + round256((size_t)rows_total * 4);
+  L.ad32t = L.rows + round256((size_t)rows_total * 4);
+  L.total = L.ad32t + round256((size_t)(k / kQK) * (size_t)bqi::grouped_ad32_rows(rows_total) * 4);
   return L;
 }
 
@@ -50,7 +55,7 @@ const char *bqi_status_string(int status) {
   }
 }
 
-int bqi_abi_version(void) { return 100; }
+int bqi_abi_version(void) { return 200; }
 
 int quantize_q8_0(const void *x, int x_dtype, int64_t rows, int64_t k,
                   int64_t ldx, int8_t *q, uint16_t *d, void *stream) {
@@ -99,7 +104,7 @@ int route_topk(const int32_t *topk_ids, int64_t n_tokens, int64_t top_k,
                int64_t n_experts, int32_t *counts, int32_t *offsets,
                int32_t *rows, void *stream) {
   if (n_tokens < 0 || top_k < 0 || n_experts < 0) return BQI_ESHAPE;
-  if (n_experts > 65536 || n_tokens * top_k > kI32Max - 1) return BQI_ESHAPE;
+  if (n_experts > 65536 || n_tokens * top_k > kMaxRouted) return BQI_ESHAPE;
   if (n_experts == 0) return BQI_OK;
   if (!counts || !offsets) return BQI_EINVAL;
   if (n_tokens * top_k > 0 && (!topk_ids || !rows)) return BQI_EINVAL;
@@ -107,14 +112,18 @@ int route_topk(const int32_t *topk_ids, int64_t n_tokens, int64_t top_k,
       !aligned(rows, 4))
     return BQI_EALIGN;
   return hip_status(bqi::launch_route_topk(topk_ids, n_tokens * top_k,
-                                           n_experts, counts, offsets, rows,
-                                           nullptr, 0, as_stream(stream)));
+                                           n_experts, top_k, counts, offsets,
+                                           rows, nullptr, 0, nullptr, nullptr,
+                                           0, as_stream(stream)));
 }
 
 size_t qgemm_w4a8_grouped_workspace_size(int64_t n_tokens, int64_t top_k,
-                                         int64_t n_experts) {
-  if (n_tokens < 0 || top_k < 0 || n_experts < 0) return 0;
-  return ws_layout(n_tokens * top_k, n_experts).total;
+                                         int64_t n_experts, int64_t k) {
+  if (n_tokens < 0 || top_k < 0 || n_experts < 0 || k < 0 || k % kQK != 0)
+    return 0;
+  if (n_experts > 65536 || n_tokens * top_k > kMaxRouted || k > kI32Max)
+    return 0;
+  return ws_layout(n_tokens * top_k, n_experts, k).total;
 }
 
 int qgemm_w4a8_grouped(const int8_t *aq, const uint16_t *ad, int64_t n_tokens,
@@ -125,7 +134,7 @@ int qgemm_w4a8_grouped(const int8_t *aq, const uint16_t *ad, int64_t n_tokens,
   if (n_tokens < 0 || top_k < 0 || n_experts < 0 || n < 0 || k < 0 ||
       k % kQK != 0)
     return BQI_ESHAPE;
-  if (n_experts > 65536 || n_tokens * top_k > kI32Max - 1 || n > kI32Max ||
+  if (n_experts > 65536 || n_tokens * top_k > kMaxRouted || n > kI32Max ||
       k > kI32Max)
     return BQI_ESHAPE;
   const int64_t rows_total = n_tokens * top_k;
@@ -143,18 +152,21 @@ int qgemm_w4a8_grouped(const int8_t *aq, const uint16_t *ad, int64_t n_tokens,
     // every valid row is an empty sum, or every row is invalid: y = 0
     return hip_status(bqi::launch_zero_f32(y, rows_total * n, s));
   }
-  const WsLayout L = ws_layout(rows_total, n_experts);
+  const WsLayout L = ws_layout(rows_total, n_experts, k);
   if (!workspace || workspace_bytes < L.total) return BQI_EINVAL;
   if (!aligned(workspace, 256)) return BQI_EALIGN;
   char *ws = static_cast<char *>(workspace);
   int32_t *counts = reinterpret_cast<int32_t *>(ws + L.counts);
   int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
   int32_t *rows = reinterpret_cast<int32_t *>(ws + L.rows);
-  hipError_t e = bqi::launch_route_topk(topk_ids, rows_total, n_experts, counts,
-                                        offsets, rows, y, n, s);
+  float *ad32t = reinterpret_cast<float *>(ws + L.ad32t);
+  hipError_t e = bqi::launch_route_topk(topk_ids, rows_total, n_experts, top_k,
+                                        counts, offsets, rows, ad, k, ad32t, y,
+                                        n, s);
   if (e != hipSuccess) return BQI_EHIP;
-  return hip_status(bqi::launch_grouped_w4a8(aq, ad, top_k, wq4, wd, n_experts,
-                                             n, k, counts, offsets, rows, y, s));
+  return hip_status(bqi::launch_grouped_w4a8(aq, ad32t, rows_total, top_k, wq4,
+                                             wd, n_experts, n, k, counts,
+                                             offsets, rows, y, s));
 }
 
 }  // extern "C"

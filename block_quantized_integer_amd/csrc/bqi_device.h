@@ -45,28 +45,95 @@ constexpr float MAGIC_F = 12582912.0f;
 // per 8 lanes.
 __device__ __forceinline__ int swz64(int r, int c) { return c ^ ((r >> 1) & 3); }
 
-// Direct global -> LDS load (gfx950 LDS DMA, 16 bytes per lane).  Lane L's
-// 16 bytes land at lds_wave_base + 16 * L
-// (lds_wave_base must be wave-uniform).  Issued through inline asm so that the
-// compiler does not track them: every kernel that uses them waits for them
-// explicitly (s_waitcnt vmcnt(0) and a barrier) before any wave reads the
-// destination.  Compiler-visible loads issued around them may then be waited
-// on more than necessary, never less.  M0 carries the LDS base; the leading
-// s_nop is the one wait state GFX9 requires between an SALU write of M0 and
-// an LDS DMA that reads it (the compiler places that write just before the
-// asm and cannot see the DMA inside it).
+// Direct global -> LDS loads (gfx950 LDS DMA).  Lane L's 16 (or 4) bytes
+// land at lds_wave_base + 16 * L (4 * L); lds_wave_base must be wave-uniform
+// (it travels in M0).  The compiler counts these loads in vmcnt like any other
+// global load, so its own waits for register loads issued around them stay
+// exact, but it does not see their LDS writes: every kernel waits for them
+// explicitly (s_waitcnt vmcnt and a barrier) before any wave reads the
+// destination.
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void load_lds16(const void *gsrc, void *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void *)lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void load_lds4(const void *gsrc, void *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void *)lds_wave_base, 4, 0, 0);
+}
+
+// The same loads issued through inline asm, invisible to the compiler: it
+// neither counts them in vmcnt nor sees their LDS writes.  A kernel whose
+// loop keeps several stages of such loads in flight uses these instead of the
+// builtin, because the compiler, seeing a builtin direct load, conservatively
+// waits for all of them (vmcnt(0)) before the next LDS read, which would drain
+// the pipeline every stage.  Every kernel that uses them waits for them
+// explicitly (wait_vmcnt and a barrier) before any wave reads the destination.
+// M0 carries the LDS base; the leading s_nop is the wait state GFX9 requires
+// between an SALU write of M0 and an LDS DMA that reads it (the compiler
+// places that write just before the asm and cannot see the DMA inside it).
 typedef __attribute__((address_space(3))) char lds_char;
 
 __device__ __forceinline__ uint32_t lds_addr(const void *generic_lds_ptr) {
   return (uint32_t)(uintptr_t)(const lds_char *)generic_lds_ptr;
 }
 
-__device__ __forceinline__ void dma_lds16(const void *gsrc, uint32_t lds_wave_base) {
+__device__ __forceinline__ void dma_lds16(const void *gsrc, void *lds_wave_base) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
-               : "v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_wave_base))
+               : "v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base)))
                : "memory");
 }
 
+__device__ __forceinline__ void dma_lds4(const void *gsrc, void *lds_wave_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base)))
+               : "memory");
+}
+
+// 2 bytes per lane, zero-extended: lane L's value lands in the 4-byte slot
+// lds_wave_base + 4 * L.
+__device__ __forceinline__ void dma_lds_u16(const void *gsrc, void *lds_wave_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_ushort %0, off"
+               :
+               : "v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base)))
+               : "memory");
+}
+
+// A 16-bit register load through inline asm (zero-extended), likewise
+// invisible to the compiler's wait counting: its value may be used only after
+// wait_vmcnt_for() has named the register.
+__device__ __forceinline__ uint32_t load_u16_async(const uint16_t *p) {
+  uint32_t v;
+  asm volatile("global_load_ushort %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+
+// s_waitcnt vmcnt(N) that the compiler treats as producing a and b, so no use
+// of them (loaded by load_u16_async) can be scheduled before it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_for(uint32_t &a, uint32_t &b) {
+  static_assert(N >= 0 && N < 16, "immediate vmcnt");
+  asm volatile("s_waitcnt vmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N) : "memory");
+}
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima), in the
+// GFX9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's own LDS
+// operations (lgkmcnt(0)), then s_barrier.  Unlike __syncthreads() it does
+// not wait for outstanding global loads, so direct-to-LDS loads of later
+// stages stay in flight across it; kernels wait for the ones they need with
+// wait_vmcnt first.  The memory clobber keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 }  // namespace bqi

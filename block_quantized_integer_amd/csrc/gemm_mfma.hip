@@ -55,12 +55,6 @@ static_assert(CPR == 8, "the swizzle assumes 8 chunks per row");
 // rows at one logical chunk, and this swizzle spreads them over all banks.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void load_lds16(const void *gsrc, void *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void *)lds_wave_base, 16, 0, 0);
-}
-
 struct Tiles {
   int8_t a[BM * BK];
   int8_t w[BN * BK];

@@ -6,21 +6,30 @@
 // products with SSSE3 pmaddubsw; here the nibbles are unpacked in registers
 // straight into int8 MFMA operands.
 //
-// Routing (k_route): one workgroup per expert reads all routed ids twice from
-// L2 with coalesced loads: first to count the valid ids below the expert (its
-// offset) and equal to it, then, staged in LDS, to place its rows: each
-// thread owns a contiguous slice and one workgroup scan orders the matches,
-// so rows come out in increasing row order.  No cross-workgroup pass and no
-// atomics are needed, and the result is deterministic.
+// Routing (k_route): one workgroup of 1024 threads per expert.  Each thread
+// owns a contiguous slice of 8 routed ids; one pass counts the valid ids below
+// the expert (its offset) and equal to it, a second pass places the matches:
+// one workgroup scan orders them, so rows come out in increasing row order.
+// No atomics, deterministic.  For the grouped GEMM the same kernel also
+// copies the activation scales of the routed rows, converted to fp32, into a
+// block-major table in expert order (one 4-byte entry per routed row and
+// block), which the GEMM then streams into LDS without conversion.
 //
-// GEMM (k_grouped_w4a8): one workgroup per (expert, 128-column tile); each of
-// its 4 waves owns 32 output columns and loads those weight rows straight
-// from HBM into registers (every weight byte is read once per token chunk of
-// up to 96 routed rows).  The routed activation rows are gathered into LDS.
-// Per 32-element group a lane unpacks 16 codes (low or high nibbles, by lane
-// half) and maps c -> c - 8 bytewise with (c + 0x78) ^ 0x80, which gives the
-// int8 value c - 8 without cross-byte carries.  The scale epilogue is the one
-// of the Q8_0 MFMA GEMM (one rounding per term).
+// GEMM (k_grouped_w4a8): one workgroup of 12 waves per (expert, 384-column
+// tile); each wave owns 32 output columns.  K advances 4 groups (128
+// elements) per stage through three LDS buffers, two stages in flight.  Every
+// operand travels HBM/L2 -> LDS through gfx950's direct loads: the packed
+// weights (64 bytes per column and stage), their fp16 scales, the routed
+// activation rows (gathered by token, 128 bytes per row and stage) and the
+// fp32 activation scales.  The products run on v_mfma_i32_32x32x32_i8 (one
+// instruction = one 32x32 tile for exactly one group); on gfx950 it costs
+// about as many cycles as the 16x16x32 form while doing four times the MACs,
+// and MFMA and VALU time largely add up in this kernel.  Per group a lane
+// unpacks its 16 codes (low or high nibbles by lane half) into the int8
+// values 16*(c - 8) with a shift, a mask and an xor; the factor 16 is folded
+// into the weight scale.  The scale epilogue is the one of the Q8_0
+// MFMA GEMM (one rounding per term).  Routed rows are taken 96 at a time (six
+// 16-row tiles), so an expert's weights are streamed once per 96 rows.
 #include "bqi_device.h"
 #include "bqi_launch.h"
 
@@ -28,10 +37,14 @@ namespace bqi {
 
 namespace {
 
-constexpr int ROUTE_THREADS = 256;
+// ---------------------------------------------------------------- routing --
+constexpr int RT = 1024;          // threads per routing workgroup
+constexpr int RPT = 8;            // ids per thread per pass
+constexpr int RCHUNK = RT * RPT;  // ids per pass
 
-__device__ __forceinline__ int wg_exclusive_scan(int v, int *s_tmp, int &total) {
-  // two-level scan: wave prefix via shuffles, then across the 4 waves in LDS
+// Exclusive workgroup scan of one int per thread (RT threads); `total` gets
+// the sum.  Contains two barriers.
+__device__ __forceinline__ int route_scan(int v, int *s_tmp, int &total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = v;
 #pragma unroll
@@ -43,7 +56,7 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int *s_tmp, int &total) 
   __syncthreads();
   int wave_base = 0, sum = 0;
 #pragma unroll
-  for (int w = 0; w < ROUTE_THREADS / 64; ++w) {
+  for (int w = 0; w < RT / 64; ++w) {
     const int x = s_tmp[w];
     if (w < wave) wave_base += x;
     sum += x;
@@ -53,60 +66,73 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int *s_tmp, int &total) 
   return wave_base + incl - v;
 }
 
-constexpr int ROUTE_CHUNK = 8192;  // ids staged in LDS per pass (32 KB)
-
-__global__ __launch_bounds__(ROUTE_THREADS) void k_route(
-    const int32_t *__restrict__ ids, int rows_total, int n_experts,
+__global__ __launch_bounds__(RT) void k_route(
+    const int32_t *__restrict__ ids, int rows_total, int n_experts, int top_k,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ rows, float *__restrict__ y, int n) {
-  __shared__ int s_ids[ROUTE_CHUNK];
-  __shared__ int s_tmp[ROUTE_THREADS / 64];
+    int32_t *__restrict__ rows, const uint16_t *__restrict__ ad, int nbk,
+    float *__restrict__ ad32t, int rpad, float *__restrict__ y, int n) {
+  __shared__ int s_tmp[RT / 64];
+  __shared__ int s_match[RCHUNK];  // (position - chunk base) -> routed row
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
 
-  // pass 1: rows routed to experts below e (this expert's offset) and to e,
-  // with coalesced loads
+  // pass 1: valid ids below this expert (its offset) and equal to it
   int below = 0, eq = 0;
-  for (int r = tid; r < rows_total; r += ROUTE_THREADS) {
-    const int v = ids[r];
-    below += (v >= 0 && v < e);
-    eq += (v == e);
+  for (int c0 = 0; c0 < rows_total; c0 += RCHUNK) {
+    const int r0 = c0 + tid * RPT;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int r = r0 + j;
+      const int v = r < rows_total ? ids[r] : -1;
+      below += (v >= 0 && v < e);
+      eq += (v == e);
+    }
   }
   int n_below, n_eq;
-  (void)wg_exclusive_scan(below, s_tmp, n_below);
-  (void)wg_exclusive_scan(eq, s_tmp, n_eq);
+  (void)route_scan(below, s_tmp, n_below);
+  (void)route_scan(eq, s_tmp, n_eq);
   if (tid == 0) {
     counts[e] = n_eq;
     offsets[e] = n_below;
     if (e == n_experts - 1) offsets[n_experts] = n_below + n_eq;
   }
 
-  // pass 2: stage ids chunk by chunk in LDS; each thread scans a contiguous
-  // slice, one workgroup scan orders the matches, so rows come out in
-  // increasing row index
+  // pass 2: place the matches in increasing row order; with ad32t, also copy
+  // their activation scales (fp16 -> fp32) into the block-major table
   int base = n_below;
-  for (int c0 = 0; c0 < rows_total; c0 += ROUTE_CHUNK) {
-    const int len = min(ROUTE_CHUNK, rows_total - c0);
-    for (int i = tid; i < len; i += ROUTE_THREADS) s_ids[i] = ids[c0 + i];
-    __syncthreads();
-    const int per = (len + ROUTE_THREADS - 1) / ROUTE_THREADS;
-    const int r0 = min(len, tid * per), r1 = min(len, r0 + per);
+  for (int c0 = 0; c0 < rows_total && base < n_below + n_eq; c0 += RCHUNK) {
+    const int r0 = c0 + tid * RPT;
+    int v[RPT];
     int mine = 0;
-    for (int r = r0; r < r1; ++r) mine += (s_ids[r] == e);
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      v[j] = r0 + j < rows_total ? ids[r0 + j] : -1;
+      mine += (v[j] == e);
+    }
     int total;
-    int pos = base + wg_exclusive_scan(mine, s_tmp, total);
-    for (int r = r0; r < r1 && mine > 0; ++r)
-      if (s_ids[r] == e) {
-        rows[pos++] = c0 + r;
-        --mine;
+    int pos = route_scan(mine, s_tmp, total);
+#pragma unroll
+    for (int j = 0; j < RPT; ++j)
+      if (v[j] == e) {
+        rows[base + pos] = r0 + j;
+        s_match[pos] = r0 + j;
+        ++pos;
       }
+    if (ad32t != nullptr) {
+      __syncthreads();
+      for (int64_t idx = tid; idx < (int64_t)total * nbk; idx += RT) {
+        const int i = (int)(idx % total), b = (int)(idx / total);
+        const int tok = s_match[i] / top_k;
+        ad32t[(int64_t)b * rpad + base + i] = half_bits_to_float(ad[(int64_t)tok * nbk + b]);
+      }
+      __syncthreads();
+    }
     base += total;
-    __syncthreads();
   }
 
   // zero the output rows of invalid ids; workgroup e checks rows r = e (mod E)
   if (y != nullptr) {
-    for (int r = e + tid * n_experts; r < rows_total; r += ROUTE_THREADS * n_experts) {
+    for (int r = e + tid * n_experts; r < rows_total; r += RT * n_experts) {
       const int v = ids[r];
       if (v < 0 || v >= n_experts)
         for (int c = 0; c < n; ++c) y[(int64_t)r * n + c] = 0.0f;
@@ -114,13 +140,27 @@ __global__ __launch_bounds__(ROUTE_THREADS) void k_route(
   }
 }
 
-constexpr int GBN = 128;        // output columns per workgroup (4 waves x 32)
-constexpr int GNB = 4;          // 32-element groups per stage
-constexpr int GBK = GNB * QK;   // activation bytes per row per stage (128)
-constexpr int MT_MAX = 3;       // 32-row token tiles per chunk
-constexpr int CHUNK = 32 * MT_MAX;
-constexpr int NSTAGE = 2;       // LDS double buffer; loads run one stage ahead
-constexpr int GTHREADS = 256;
+// ------------------------------------------------------------ grouped GEMM --
+constexpr int GW = 12;             // waves per workgroup
+constexpr int GT = GW * 64;        // threads per workgroup
+constexpr int GBN = GW * 32;       // output columns per workgroup (32 per wave)
+constexpr int GNB = 4;             // 32-element groups per stage
+constexpr int GBK = GNB * QK;      // activation bytes per row per stage
+constexpr int GRT = 3;             // 32-row MFMA tiles per chunk
+constexpr int GCH = 32 * GRT;      // routed rows per chunk
+constexpr int GNS = 3;             // LDS stage buffers (two stages in flight)
+constexpr int G_AD_WAVES = GNB * GCH / 64;  // waves issuing activation-scale loads
+
+static_assert(GNB * GCH % 64 == 0 && G_AD_WAVES <= GW, "scale loads map to whole waves");
+static_assert(GBN * GNB == 2 * GT, "two weight-scale loads per wave and stage");
+static_assert(GCH == 8 * GW, "one activation-row load per wave and stage");
+
+struct GBuf {
+  uint8_t w[GBN * GNB * 16];  // packed weights: [column][4 groups x 16 B], swizzled
+  int8_t a[GCH * GBK];        // gathered activation rows: [row][8 x 16 B], swizzled
+  float ad[GNB][GCH];         // activation scales, fp32, [group][row]
+  uint32_t wd[GBN][GNB];      // weight scales, fp16 bits zero-extended, [column][group]
+};
 
 // Physical slot of the 16-byte activation chunk c of staged row r (rows of
 // 128 B; spreads a 16-lane fragment read over all 64 LDS banks).
@@ -128,232 +168,262 @@ __device__ __forceinline__ int aswz(int r, int c) { return c ^ ((r >> 1) & 7); }
 // Physical slot of group b of weight column c (columns of 64 B = 4 groups).
 __device__ __forceinline__ int wswz(int c, int b) { return b ^ ((c >> 2) & 3); }
 
-// Unpack the 16 codes this lane feeds to the MFMA (low nibbles for lanes
-// 0..31 = elements 0..15 of the group, high nibbles for lanes 32..63 =
-// elements 16..31) and map each code c to the int8 value c - 8.
-__device__ __forceinline__ i32x4 unpack_w4(const i32x4 p, int shift) {
+// v_mfma_i32_32x32x32_i8 takes, in lane L, the 16 consecutive K elements
+// 16*(L/32) .. +15 of row (A) or column (B) L%32.  For one 32-element group
+// of 4-bit codes (16 bytes: byte i holds element i in its low nibble and
+// element i+16 in its high nibble) that is the low nibbles of all 16 bytes
+// for lanes 0..31 and the high nibbles for lanes 32..63.  Each code c becomes
+// the int8 16*(c - 8): (nibble << 4) ^ 0x80 is the byte (c ^ 8) * 16, which
+// read as a signed byte is 16 * (c - 8).  The factor 16 is folded into the
+// weight scale (exact); |16 * P| <= 16 * 32 * 8 * 128 < 2^22 keeps the
+// accumulator-seed conversion exact.
+__device__ __forceinline__ i32x4 unpack_w4x16(i32x4 p, int shl) {
   i32x4 r;
-  r.x = (int32_t)(((((uint32_t)p.x >> shift) & 0x0f0f0f0fu) + 0x78787878u) ^ 0x80808080u);
-  r.y = (int32_t)(((((uint32_t)p.y >> shift) & 0x0f0f0f0fu) + 0x78787878u) ^ 0x80808080u);
-  r.z = (int32_t)(((((uint32_t)p.z >> shift) & 0x0f0f0f0fu) + 0x78787878u) ^ 0x80808080u);
-  r.w = (int32_t)(((((uint32_t)p.w >> shift) & 0x0f0f0f0fu) + 0x78787878u) ^ 0x80808080u);
+  r.x = (int32_t)((((uint32_t)p.x << shl) & 0xf0f0f0f0u) ^ 0x80808080u);
+  r.y = (int32_t)((((uint32_t)p.y << shl) & 0xf0f0f0f0u) ^ 0x80808080u);
+  r.z = (int32_t)((((uint32_t)p.z << shl) & 0xf0f0f0f0u) ^ 0x80808080u);
+  r.w = (int32_t)((((uint32_t)p.w << shl) & 0xf0f0f0f0u) ^ 0x80808080u);
   return r;
 }
 
-struct GStage {
-  int8_t a[CHUNK * GBK];      // gathered activation rows, swizzled 16-byte chunks
-  uint8_t w[GBN * GNB * 16];  // packed 4-bit weights: [col][group] 16 B, swizzled
-  float wd[GBN][GNB];         // weight scales, fp32, [col][group]
-  float ad[GNB][CHUNK];       // activation scales, fp32, [group][row]
-};
-
-// The MFMA work of one stage, read from LDS.
+// The MFMA work of one stage for one wave: 32 columns x R 32-row tiles,
+// groups 0 .. nb_here-1 of the stage, read from LDS.  The group loop is
+// rolled and R is a compile-time constant, so the code per group is
+// straight-line: the group's fragment reads first, then all R MFMAs, then the
+// R epilogues, so that the matrix core works while the epilogues run.
+// Output register r of tile t in lane L is row 32t + 8(r/4) + 4(L/32) + r%4,
+// column L%32 of the wave's tile.
+template <int R>
 __device__ __forceinline__ void grouped_stage_compute(
-    const GStage *__restrict__ SB, int nb_here, int mtiles, int col_l, int l32,
-    int g, const i32x16 &seed, float (&acc)[MT_MAX][16]) {
+    const GBuf &B, int nb_here, int wave, int lane, const i32x16 &seed,
+    float (&acc)[R][16]) {
+  const int l32 = lane & 31, g = lane >> 5;
+  const int shl = g ? 0 : 4;
+  const int cl = wave * 32 + l32;
+#pragma unroll 1
+  for (int b = 0; b < nb_here; ++b) {
+    const i32x4 p = *reinterpret_cast<const i32x4 *>(&B.w[cl * (GNB * 16) + 16 * wswz(cl, b)]);
+    const uint32_t sw = B.wd[cl][b];
+    i32x4 af[R];
 #pragma unroll
-  for (int b = 0; b < GNB; ++b) {
-    if (b >= nb_here) break;
-    const int c = col_l;
-    const i32x4 packed = *reinterpret_cast<const i32x4 *>(&SB->w[c * (GNB * 16) + 16 * wswz(c, b)]);
-    const i32x4 wf = unpack_w4(packed, 4 * g);
-    const float dw = SB->wd[c][b];
-    const float ncd = -MAGIC_F * dw;
+    for (int t = 0; t < R; ++t) {
+      const int r = 32 * t + l32;
+      af[t] = *reinterpret_cast<const i32x4 *>(&B.a[r * GBK + 16 * aswz(r, 2 * b + g)]);
+    }
+    // keep the reads above ahead of the math (the scheduler would otherwise
+    // sink each next to its first use and expose the LDS latency per tile)
+    __builtin_amdgcn_sched_barrier(0);
+    const i32x4 wf = unpack_w4x16(p, shl);
+    const float dw16 = half_bits_to_float((uint16_t)sw) * 0.0625f;  // exact
+    const float ncd = -MAGIC_F * dw16;                              // exact
+    i32x16 d[R];
 #pragma unroll
-    for (int t = 0; t < MT_MAX; ++t) {
-      if (t < mtiles) {
-        const int r = t * 32 + l32;
-        const i32x4 af = *reinterpret_cast<const i32x4 *>(&SB->a[r * GBK + 16 * aswz(r, 2 * b + g)]);
-        const i32x16 d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf, seed, 0, 0, 0);
-        float da[16];
+    for (int t = 0; t < R; ++t) d[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[t], wf, seed, 0, 0, 0);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = *reinterpret_cast<const f32x4 *>(&SB->ad[b][t * 32 + 8 * q + 4 * g]);
-          da[4 * q + 0] = v.x;
-          da[4 * q + 1] = v.y;
-          da[4 * q + 2] = v.z;
-          da[4 * q + 3] = v.w;
-        }
+    for (int t = 0; t < R; ++t) {
 #pragma unroll
-        for (int r2 = 0; r2 < 16; ++r2) {
-          const float tt = fmaf(bits_to_float(d[r2]), dw, ncd);
-          acc[t][r2] = fmaf(tt, da[r2], acc[t][r2]);
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(&B.ad[b][32 * t + 8 * q + 4 * g]);
+        const float da[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r2 = 4 * q + j;
+          const float tt = fmaf(bits_to_float(d[t][r2]), dw16, ncd);
+          acc[t][r2] = fmaf(tt, da[j], acc[t][r2]);
         }
       }
     }
   }
 }
 
-__global__ __launch_bounds__(GTHREADS, 2) void k_grouped_w4a8(
-    const int8_t *__restrict__ aq, const uint16_t *__restrict__ ad, int top_k,
-    const uint8_t *__restrict__ wq4, const uint16_t *__restrict__ wd,
-    int n_experts, int n, int k, const int32_t *__restrict__ counts,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ rows,
-    float *__restrict__ y) {
-  __shared__ __attribute__((aligned(16))) GStage S[NSTAGE];
-  __shared__ int s_tok[CHUNK];   // token index of each staged row
-  __shared__ int s_row[CHUNK];   // routed row index (output row)
+struct GArgs {
+  const int8_t *aq;
+  const float *ad32t;
+  int rpad, top_k;
+  const uint8_t *wq4;
+  const uint16_t *wd;
+  int n, k;
+  float *y;
+};
 
-  // all column tiles of one expert share (blockIdx % n_experts), hence one XCD
-  // when n_experts is a multiple of 8
-  const int e = blockIdx.x % n_experts;
-  const int tn = blockIdx.x / n_experts;
-  const int cnt = counts[e];
-  if (cnt == 0) return;
-  const int off = offsets[e];
-
+// One chunk of up to 16*R routed rows of expert e against the workgroup's
+// column tile: the whole K pipeline, then the stores.
+template <int R>
+__device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS],
+                                              const int *s_tok, const int *s_row,
+                                              int64_t wrow0, int n0, int off,
+                                              int c0, int crows) {
+  const int n = A.n, k = A.k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, g = lane >> 5;
   const int nbk = k / QK;
   const int stages = (nbk + GNB - 1) / GNB;
-  const int n0 = tn * GBN;
-  const int col_l = wave * 32 + l32;  // this lane's output column within the tile
-  const int64_t wrow0 = (int64_t)e * n;
+  const bool wave_active = n0 + wave * 32 < n;
+  const int64_t kh = k / 2;  // packed bytes per weight row
 
   i32x16 seed;
 #pragma unroll
   for (int r = 0; r < 16; ++r) seed[r] = MAGIC_BITS;
 
-  for (int c0 = 0; c0 < cnt; c0 += CHUNK) {
-    const int crows = min(CHUNK, cnt - c0);
-    const int mtiles = (crows + 31) / 32;
+  // Issue the direct loads of stage s into buffer s % GNS (5 per wave, plus
+  // one activation-scale load in waves 0 .. G_AD_WAVES-1).  They go through
+  // inline asm, invisible to the compiler's wait counting (see dma_lds16);
+  // the waits below are explicit.  Group indices past the last group of k
+  // re-read the last group (never used); columns past n re-read column n-1;
+  // rows past the chunk re-read its last row.  Addresses are rebuilt per
+  // stage from the thread index, laundered through an empty asm, so that the
+  // compiler does not hoist a dozen 64-bit addresses out of the stage loop
+  // and hold them in registers across it.
+  auto issue = [&](int s) {
+    int tl = tid;
+    asm volatile("" : "+v"(tl));
+    const int ln = tl & 63, wv = tl >> 6;
+    const int g0 = s * GNB;
+    GBuf &D = S[s % GNS];
+    // weights: wave load h (two per wave) fills columns ct .. ct+15,
+    // ct = 16 * (2w + h); lane L lands in column ct + L/4, slot L%4, which
+    // holds group (L%4) ^ swizzle(column)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int cl = 16 * (2 * wv + h) + (ln >> 2);
+      const int lg = (ln & 3) ^ ((cl >> 2) & 3);
+      const int c = min(n0 + cl, n - 1);
+      dma_lds16(A.wq4 + (wrow0 + c) * kh + 16 * min(g0 + lg, nbk - 1),
+                &D.w[16 * (2 * wave + h) * (GNB * 16)]);
+    }
+    // weight scales: wave load h fills table entries e = 64 (2w + h) + L,
+    // column e / 4, group e % 4 (one fp16, zero-extended, per 4-byte slot)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = 64 * (2 * wv + h) + ln;
+      const int c = min(n0 + (e >> 2), n - 1);
+      dma_lds_u16(A.wd + (wrow0 + c) * nbk + min(g0 + (e & 3), nbk - 1),
+                  &D.wd[0][0] + 64 * (2 * wave + h));
+    }
+    // activation rows: wave w fills staged rows 8w .. 8w+7; lane L lands in
+    // row 8w + L/8, physical chunk L%8, which holds logical chunk
+    // (L%8) ^ swizzle(row)
+    {
+      const int ra = 8 * wv + (ln >> 3);
+      const int lc = (ln & 7) ^ ((ra >> 1) & 7);
+      const int kb = min(g0 + (lc >> 1), nbk - 1);
+      dma_lds16(A.aq + (int64_t)s_tok[ra] * k + 32 * kb + 16 * (lc & 1), &D.a[8 * wave * GBK]);
+    }
+    // activation scales (waves 0 .. G_AD_WAVES-1): flat entry f = 64w + L of
+    // the stage's [group][row] table
+    if (wave < G_AD_WAVES) {
+      const int f = 64 * wv + ln;
+      dma_lds4(A.ad32t + (int64_t)min(g0 + f / GCH, nbk - 1) * A.rpad + (off + c0 + f % GCH),
+               &D.ad[0][0] + 64 * wave);
+    }
+  };
+
+  float acc[R][16];
+#pragma unroll
+  for (int t = 0; t < R; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
+
+  issue(0);
+  if (stages > 1) issue(1);
+  for (int s = 0; s < stages; ++s) {
+    // this wave's loads of stage s have landed (only stage s+1's, issued
+    // after them, may still be in flight)
+    if (s + 1 < stages) {
+      if (wave < G_AD_WAVES) wait_vmcnt<6>();
+      else wait_vmcnt<5>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    // every wave's loads of stage s have landed, and every wave is done with
+    // stage s-1, whose buffer the loads below refill
+    lds_barrier();
+    if (s + 2 < stages) issue(s + 2);
+    if (wave_active)
+      grouped_stage_compute<R>(S[s % GNS], min(GNB, nbk - s * GNB), wave, lane, seed, acc);
+  }
+
+  // store: lane's column L%32, rows 32t + 8(r/4) + 4(L/32) + r%4 of the chunk
+  const int col = n0 + wave * 32 + (lane & 31);
+  if (wave_active && col < n) {
+#pragma unroll
+    for (int t = 0; t < R; ++t)
+#pragma unroll
+      for (int r2 = 0; r2 < 16; ++r2) {
+        const int rr = 32 * t + 8 * (r2 >> 2) + 4 * (lane >> 5) + (r2 & 3);
+        if (rr < crows) A.y[(int64_t)s_row[rr] * n + col] = acc[t][r2];
+      }
+  }
+}
+
+__global__ __launch_bounds__(GT, 1) void k_grouped_w4a8(
+    const int8_t *__restrict__ aq, const float *__restrict__ ad32t, int rpad,
+    int top_k, const uint8_t *__restrict__ wq4, const uint16_t *__restrict__ wd,
+    int n_experts, int n, int k, const int32_t *__restrict__ counts,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ rows,
+    float *__restrict__ y) {
+  __shared__ __attribute__((aligned(16))) GBuf S[GNS];
+  __shared__ int s_tok[GCH];  // token of each staged row
+  __shared__ int s_row[GCH];  // routed row (output row) of each staged row
+
+  // both column tiles of one expert share (blockIdx % n_experts), hence one
+  // XCD when n_experts is a multiple of 8, and so the expert's activation rows
+  // in that XCD's L2
+  const int e = blockIdx.x % n_experts;
+  const int tn = blockIdx.x / n_experts;
+  const int cnt = counts[e];
+  if (cnt == 0) return;
+  const int off = offsets[e];
+  const GArgs A{aq, ad32t, rpad, top_k, wq4, wd, n, k, y};
+  const int tid = threadIdx.x;
+  const int n0 = tn * GBN;
+  const int64_t wrow0 = (int64_t)e * n;
+
+  for (int c0 = 0; c0 < cnt; c0 += GCH) {
+    const int crows = min(GCH, cnt - c0);
+    // the previous chunk is done with s_tok, s_row and S (and its direct
+    // loads have all landed: each chunk ends with vmcnt(0))
     __syncthreads();
-    if (tid < CHUNK) {
+    if (tid < GCH) {
       const int rr = rows[off + c0 + min(tid, crows - 1)];
       s_row[tid] = rr;
       s_tok[tid] = rr / top_k;
     }
     __syncthreads();
-
-    // ---- stage loads ------------------------------------------------------
-    // activations: 96 rows x 8 chunks = 12 wave loads (3 per wave); lane L of
-    // load q fills row 8*(3*wave+q) + L/8, slot L%8 = chunk (L%8)^swizzle.
-    // weights: 128 columns x 4 groups = 8 wave loads (2 per wave); lane L of
-    // load q fills column 16*(2*wave+q) + L/4, slot L%4 = group (L%4)^swizzle.
-    // scales (activation: 96 rows x 4 groups, weight: 128 columns x 4
-    // groups) go through registers, 2 + 2 fp16 per thread, and are stored to
-    // LDS as fp32.  Per stage each wave issues 4 scale loads into registers
-    // (issue_scales) and 5 direct LDS loads (issue_direct).
-    uint16_t sa_reg[2], sw_reg[2];
-    auto issue_scales = [&](int s) {
-      const int g0 = min(s, stages - 1) * GNB;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int idx = tid + GTHREADS * h;  // CHUNK*GNB = 384 entries
-        const int r = min(idx / GNB, CHUNK - 1), b = idx % GNB;
-        const int gb = g0 + b < nbk ? g0 + b : 0;
-        sa_reg[h] = ad[(int64_t)s_tok[r] * nbk + gb];
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int idx = tid + GTHREADS * h;  // GBN*GNB = 512 entries
-        const int c = idx / GNB, b = idx % GNB;
-        const int gb = g0 + b < nbk ? g0 + b : 0;
-        sw_reg[h] = wd[(wrow0 + min(n0 + c, n - 1)) * nbk + gb];
-      }
-    };
-    auto store_scales = [&](int slot) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int idx = tid + GTHREADS * h;
-        if (idx < CHUNK * GNB) S[slot].ad[idx % GNB][idx / GNB] = half_bits_to_float(sa_reg[h]);
-        S[slot].wd[idx / GNB][idx % GNB] = half_bits_to_float(sw_reg[h]);
-      }
-    };
-    auto issue_direct = [&](int s, int slot) {
-      const int g0 = min(s, stages - 1) * GNB;
-#pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        const int rt = 8 * (3 * wave + q);
-        const int r = rt + lane / 8;
-        const int c = (lane % 8) ^ ((r >> 1) & 7);
-        const int kk = 32 * g0 + 16 * c < k ? 32 * g0 + 16 * c : 0;
-        dma_lds16(aq + ((int64_t)s_tok[r] * k + kk), lds_addr(&S[slot].a[rt * GBK]));
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int ct = 16 * (2 * wave + q);
-        const int c = ct + lane / 4;
-        const int b = (lane % 4) ^ ((c >> 2) & 3);
-        const int gb = g0 + b < nbk ? g0 + b : 0;
-        const int64_t wr = wrow0 + min(n0 + c, n - 1);
-        dma_lds16(wq4 + (wr * (k / 2) + 16 * gb), lds_addr(&S[slot].w[ct * (GNB * 16)]));
-      }
-    };
-
-    float acc[MT_MAX][16];
-#pragma unroll
-    for (int t = 0; t < MT_MAX; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
-
-    // prologue: stage 0 in LDS
-    issue_scales(0);
-    issue_direct(0, 0);
-    store_scales(0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int s = 0; s < stages; ++s) {
-      const int buf = s & 1;
-      // stage s+1: scale loads first (loads retire in order, so storing the
-      // scales waits only for them), then the direct loads, which run while
-      // stage s computes
-      // (Ordering rests on the explicit wait and barrier below: stage s reads
-      // buffer buf, loaded and waited for one iteration earlier, while these
-      // direct loads fill buf ^ 1.)
-      const bool more = s + 1 < stages;
-      if (more) {
-        issue_scales(s + 1);
-        issue_direct(s + 1, buf ^ 1);
-      }
-      grouped_stage_compute(&S[buf], min(GNB, nbk - s * GNB), mtiles, col_l, l32, g, seed, acc);
-      if (more) store_scales(buf ^ 1);
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of stage s+1 have landed
-      __syncthreads();
-    }
-    // drain: no direct load may still target LDS when the next chunk (or the
-    // next workgroup on this CU) reuses it
-    __builtin_amdgcn_s_waitcnt(0);
-
-    // store: lane's column, rows t*32 + 8q + 4g + (0..3) of the chunk
-    const int col = n0 + col_l;
-    if (col < n) {
-#pragma unroll
-      for (int t = 0; t < MT_MAX; ++t) {
-        if (t < mtiles) {
-#pragma unroll
-          for (int r2 = 0; r2 < 16; ++r2) {
-            const int rr = t * 32 + 8 * (r2 >> 2) + 4 * g + (r2 & 3);
-            if (rr < crows) y[(int64_t)s_row[rr] * n + col] = acc[t][r2];
-          }
-        }
-      }
+    switch ((crows + 31) / 32) {
+      case 1: grouped_chunk<1>(A, S, s_tok, s_row, wrow0, n0, off, c0, crows); break;
+      case 2: grouped_chunk<2>(A, S, s_tok, s_row, wrow0, n0, off, c0, crows); break;
+      default: grouped_chunk<3>(A, S, s_tok, s_row, wrow0, n0, off, c0, crows); break;
     }
   }
 }
 
 }  // namespace
 
+int64_t grouped_ad32_rows(int64_t rows_total) { return rows_total + GCH; }
+
 hipError_t launch_route_topk(const int32_t *ids, int64_t rows_total,
-                             int64_t n_experts, int32_t *counts,
-                             int32_t *offsets, int32_t *rows, float *y,
-                             int64_t n, hipStream_t stream) {
-  hipLaunchKernelGGL(k_route, dim3((unsigned)n_experts), dim3(ROUTE_THREADS), 0,
-                     stream, ids, (int)rows_total, (int)n_experts, counts,
-                     offsets, rows, y, (int)n);
+                             int64_t n_experts, int64_t top_k, int32_t *counts,
+                             int32_t *offsets, int32_t *rows,
+                             const uint16_t *ad, int64_t k, float *ad32t,
+                             float *y, int64_t n, hipStream_t stream) {
+  hipLaunchKernelGGL(k_route, dim3((unsigned)n_experts), dim3(RT), 0, stream,
+                     ids, (int)rows_total, (int)n_experts, (int)top_k, counts,
+                     offsets, rows, ad, (int)(k / QK), ad32t,
+                     (int)grouped_ad32_rows(rows_total), y, (int)n);
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_w4a8(const int8_t *aq, const uint16_t *ad,
-                               int64_t top_k, const uint8_t *wq4,
-                               const uint16_t *wd, int64_t n_experts,
-                               int64_t n, int64_t k, const int32_t *counts,
-                               const int32_t *offsets, const int32_t *rows,
-                               float *y, hipStream_t stream) {
+hipError_t launch_grouped_w4a8(const int8_t *aq, const float *ad32t,
+                               int64_t rows_total, int64_t top_k,
+                               const uint8_t *wq4, const uint16_t *wd,
+                               int64_t n_experts, int64_t n, int64_t k,
+                               const int32_t *counts, const int32_t *offsets,
+                               const int32_t *rows, float *y,
+                               hipStream_t stream) {
   const int64_t tiles_n = (n + GBN - 1) / GBN;
   hipLaunchKernelGGL(k_grouped_w4a8, dim3((unsigned)(n_experts * tiles_n)),
-                     dim3(256), 0, stream, aq, ad, (int)top_k, wq4, wd,
+                     dim3(GT), 0, stream, aq, ad32t,
+                     (int)grouped_ad32_rows(rows_total), (int)top_k, wq4, wd,
                      (int)n_experts, (int)n, (int)k, counts, offsets, rows, y);
   return hipGetLastError();
 }

@@ -68,7 +68,8 @@ extern "C" {
 /* Human-readable name of a status code (static string, never NULL). */
 BQI_API const char *bqi_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor). */
+/* ABI version of this header (major * 100 + minor): 200.  Version 200 added
+ * the k argument of qgemm_w4a8_grouped_workspace_size. */
 BQI_API int bqi_abi_version(void);
 
 /*
@@ -130,15 +131,18 @@ BQI_API int qgemm_q8_0(const int8_t *aq, const uint16_t *ad, int64_t m,
  *            offsets[n_experts] are left unwritten.
  *
  * Ids outside [0, n_experts) are skipped.  Deterministic (no atomics).
- * Requirements: n_tokens * top_k < 2^31, n_experts <= 65536.
+ * Requirements: n_tokens * top_k <= 2^30, n_experts <= 65536.
  */
 BQI_API int route_topk(const int32_t *topk_ids, int64_t n_tokens, int64_t top_k,
                int64_t n_experts, int32_t *counts, int32_t *offsets,
                int32_t *rows, void *stream);
 
-/* Bytes of device workspace qgemm_w4a8_grouped needs for these sizes. */
+/* Bytes of device workspace qgemm_w4a8_grouped needs for these sizes (0 for
+ * sizes it rejects).  The workspace holds the routing (counts, offsets and
+ * the rows of each expert) and the routed rows' activation scales widened to
+ * fp32 in expert order: about 4 * (n_tokens * top_k + 96) * (k / 32) bytes. */
 BQI_API size_t qgemm_w4a8_grouped_workspace_size(int64_t n_tokens, int64_t top_k,
-                                         int64_t n_experts);
+                                         int64_t n_experts, int64_t k);
 
 /*
  * qgemm_w4a8_grouped -- expert-routed 4-bit-weight x Q8_0-activation GEMM
@@ -160,7 +164,7 @@ BQI_API size_t qgemm_w4a8_grouped_workspace_size(int64_t n_tokens, int64_t top_k
  * within a token are legal and computed independently.
  *
  * Requirements: k % 32 == 0; aq and wq4 16-byte aligned; workspace 256-byte
- * aligned; n_tokens * top_k < 2^31; n_experts <= 65536.
+ * aligned; n_tokens * top_k <= 2^30; n_experts <= 65536.
  */
 BQI_API int qgemm_w4a8_grouped(const int8_t *aq, const uint16_t *ad, int64_t n_tokens,
                        const int32_t *topk_ids, int64_t top_k,

@@ -43,7 +43,7 @@ def test_library_exports_exactly_the_header_symbols():
 
 def test_status_strings():
     L = bqi.lib()
-    assert L.bqi_abi_version() == 100
+    assert L.bqi_abi_version() == 200
     for st in (OK, EINVAL, ESHAPE, EALIGN, bqi.BQI_EHIP):
         assert L.bqi_status_string(st).decode().startswith("BQI_")
     assert L.bqi_status_string(12345)
@@ -96,7 +96,7 @@ def test_route_validation():
     r = lambda ids, T, tk, E, c, o, rows: L.route_topk(P(ids), T, tk, E, P(c), P(o), P(rows), P(0))
     assert r(FAKE, -1, 8, 4, FAKE, FAKE, FAKE) == ESHAPE
     assert r(FAKE, 4, 8, 65537, FAKE, FAKE, FAKE) == ESHAPE
-    assert r(FAKE, 1 << 28, 8, 4, FAKE, FAKE, FAKE) == ESHAPE     # rows >= 2^31
+    assert r(FAKE, 1 << 28, 8, 4, FAKE, FAKE, FAKE) == ESHAPE     # rows > 2^30
     assert r(FAKE, 4, 8, 4, 0, FAKE, FAKE) == EINVAL
     assert r(0, 4, 8, 4, FAKE, FAKE, FAKE) == EINVAL
     assert r(FAKE, 4, 8, 4, FAKE, FAKE + 2, FAKE) == EALIGN
@@ -105,9 +105,11 @@ def test_route_validation():
 
 def test_grouped_validation_and_workspace():
     L = bqi.lib()
-    ws = L.qgemm_w4a8_grouped_workspace_size(947, 8, 128)
-    assert ws >= 4 * (128 + 129 + 947 * 8) and ws % 256 == 0
-    assert L.qgemm_w4a8_grouped_workspace_size(-1, 8, 128) == 0
+    ws = L.qgemm_w4a8_grouped_workspace_size(947, 8, 128, 2048)
+    assert ws >= 4 * (128 + 129 + 947 * 8) + 4 * 64 * (947 * 8) and ws % 256 == 0
+    assert L.qgemm_w4a8_grouped_workspace_size(-1, 8, 128, 2048) == 0
+    assert L.qgemm_w4a8_grouped_workspace_size(947, 8, 128, 48) == 0
+    assert L.qgemm_w4a8_grouped_workspace_size(1 << 28, 8, 128, 2048) == 0
 
     def w(aq=FAKE, ad=FAKE, T=4, ids=FAKE, tk=2, wq=FAKE, wd=FAKE, E=3, n=16, k=64,
           y=FAKE, ws_ptr=FAKE, ws_bytes=1 << 20):
