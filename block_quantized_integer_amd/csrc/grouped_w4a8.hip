@@ -7,10 +7,11 @@
 // straight into int8 MFMA operands.
 //
 // Routing (k_route): one workgroup of 1024 threads per expert.  Each thread
-// owns a contiguous slice of 8 routed ids; one pass counts the valid ids below
-// the expert (its offset) and equal to it, a second pass places the matches:
-// one workgroup scan orders them, so rows come out in increasing row order.
-// No atomics, deterministic.  For the grouped GEMM the same kernel also
+// owns a contiguous slice of 8 routed ids, counts the valid ids below the
+// expert (its offset) and equal to it, and one workgroup scan orders the
+// matches, so rows come out in increasing row order.  Up to 8192 routed rows
+// this is a single pass over ids held in registers; beyond, a counting pass
+// and a placing pass run chunk by chunk.  No atomics, deterministic.  For the grouped GEMM the same kernel also
 // copies the activation scales of the routed rows, converted to fp32, into a
 // block-major table in expert order (one 4-byte entry per routed row and
 // block), which the GEMM then streams into LDS without conversion.
@@ -66,6 +67,46 @@ __device__ __forceinline__ int route_scan(int v, int *s_tmp, int &total) {
   return wave_base + incl - v;
 }
 
+// Copy the activation scales of this expert's `total` matched rows (routed
+// rows s_match[0 .. total)) into the block-major fp32 table at positions
+// base .. base+total-1.  Tiles of 64 rows x 64 groups go through LDS: each
+// wave reads whole 128-byte scale rows (coalesced), and writes 16 consecutive
+// positions of four table rows (coalesced), instead of scattering 2-byte
+// reads over every matched token per table row.
+__device__ __forceinline__ void route_copy_scales(const int *s_match, int total, int base,
+                                                  int top_k, const uint16_t *__restrict__ ad,
+                                                  int nbk, float *__restrict__ ad32t, int rpad,
+                                                  float (*s_t)[65]) {
+  const int tid = threadIdx.x;
+  for (int i0 = 0; i0 < total; i0 += 64) {
+    for (int b0 = 0; b0 < nbk; b0 += 64) {
+      {
+        // thread -> row i0 + tid/16, groups b0 + 4*(tid%16) .. +3
+        const int r = tid >> 4, c = 4 * (tid & 15);
+        const int i = i0 + r;
+        if (i < total) {
+          const uint16_t *src = ad + (int64_t)(s_match[i] / top_k) * nbk;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (b0 + c + u < nbk) s_t[c + u][r] = half_bits_to_float(src[b0 + c + u]);
+        }
+      }
+      __syncthreads();
+      {
+        // thread -> table row b0 + tid/16, positions i0 + (tid%16) + 16*u
+        const int c = tid >> 4, r = tid & 15;
+        if (b0 + c < nbk) {
+          float *dst = ad32t + (int64_t)(b0 + c) * rpad + base + i0;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (i0 + r + 16 * u < total) dst[r + 16 * u] = s_t[c][r + 16 * u];
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 __global__ __launch_bounds__(RT) void k_route(
     const int32_t *__restrict__ ids, int rows_total, int n_experts, int top_k,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
@@ -73,9 +114,54 @@ __global__ __launch_bounds__(RT) void k_route(
     float *__restrict__ ad32t, int rpad, float *__restrict__ y, int n) {
   __shared__ int s_tmp[RT / 64];
   __shared__ int s_match[RCHUNK];  // (position - chunk base) -> routed row
+  __shared__ float s_t[64][65];    // transpose tile of the scale copy
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
 
+  if (rows_total <= RCHUNK) {
+    // one pass: each thread keeps its 8 ids in registers; one workgroup scan
+    // of (below << 16 | eq) gives both this expert's offset (the total of the
+    // high halves) and each thread's first position (the prefix of the low
+    // halves; at most 8192, so no carry reaches the high half)
+    const int r0 = tid * RPT;
+    int v[RPT];
+    int below = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      v[j] = r0 + j < rows_total ? ids[r0 + j] : -1;
+      below += (v[j] >= 0 && v[j] < e);
+      eq += (v[j] == e);
+    }
+    int total;
+    const int excl = route_scan((below << 16) | eq, s_tmp, total);
+    const int n_below = total >> 16, n_eq = total & 0xffff;
+    if (tid == 0) {
+      counts[e] = n_eq;
+      offsets[e] = n_below;
+      if (e == n_experts - 1) offsets[n_experts] = n_below + n_eq;
+    }
+    int pos = excl & 0xffff;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      if (v[j] == e) {
+        rows[n_below + pos] = r0 + j;
+        s_match[pos] = r0 + j;
+        ++pos;
+      }
+      // invalid ids: workgroup (row mod E) zeroes the output row
+      const int r = r0 + j;
+      if (y != nullptr && r < rows_total && (v[j] < 0 || v[j] >= n_experts) &&
+          r % n_experts == e)
+        for (int c = 0; c < n; ++c) y[(int64_t)r * n + c] = 0.0f;
+    }
+    if (ad32t != nullptr && n_eq > 0) {
+      __syncthreads();
+      route_copy_scales(s_match, n_eq, n_below, top_k, ad, nbk, ad32t, rpad, s_t);
+    }
+    return;
+  }
+
+  // general case, several chunks of ids
   // pass 1: valid ids below this expert (its offset) and equal to it
   int below = 0, eq = 0;
   for (int c0 = 0; c0 < rows_total; c0 += RCHUNK) {
@@ -120,11 +206,7 @@ __global__ __launch_bounds__(RT) void k_route(
       }
     if (ad32t != nullptr) {
       __syncthreads();
-      for (int64_t idx = tid; idx < (int64_t)total * nbk; idx += RT) {
-        const int i = (int)(idx % total), b = (int)(idx / total);
-        const int tok = s_match[i] / top_k;
-        ad32t[(int64_t)b * rpad + base + i] = half_bits_to_float(ad[(int64_t)tok * nbk + b]);
-      }
+      route_copy_scales(s_match, total, base, top_k, ad, nbk, ad32t, rpad, s_t);
       __syncthreads();
     }
     base += total;
