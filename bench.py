@@ -5,7 +5,8 @@
 
 One step = the decode hot path on the decode workload (M=1, K=4096, N=12288):
 quantize the fp32 activation row to Q8_0, then the thin-M Q8_0 GEMV against
-Q8_0 weights.  The weights are rotated over 8 resident copies (428 MB, more
+Q8_0 weights, both in one launch (quantize_qgemm_q8_0).  The same step as two
+calls (quantize_q8_0, qgemm_q8_0) and the GEMV alone are reported beside it.  The weights are rotated over 8 resident copies (428 MB, more
 than the 256 MB Infinity Cache) so every step streams its weights from HBM.
 `value` is algorithmic bytes per step / time per step (GB/s); inputs are
 resident in HBM before timing starts.
@@ -15,7 +16,7 @@ long-prefill GEMM (M=18432, K=5120, N=5120, Student-t activations with outlier
 channels), the grouped W4A8 MoE GEMM (947 tokens, top-8 of 128 experts,
 K=2048, N=768) and the activation quantizer, each with its own roofline.
 
-"roofline" describes the dominant kernel of the step (the GEMV): achieved =
+"roofline" describes the step's kernel (the fused quantize + GEMV): achieved =
 algorithmic bytes per launch / mean launch duration, from HIP events recorded
 on the launch stream around a timed region of back-to-back launches.  Timed
 loops are captured once in a HIP graph and replayed (so Python launch
@@ -194,6 +195,10 @@ def bench_headline(bqi, torch, W, args):
     torch.cuda.synchronize()
 
     def step(i):
+        # the whole decode hot path in one launch: quantize x, multiply by W
+        bqi.quantize_qgemm_q8_0(x, wq[i % copies], wd[i % copies], y, aq, ad)
+
+    def step_two_calls(i):
         bqi.quantize_q8_0(x, aq, ad)
         bqi.qgemm_q8_0(aq, ad, wq[i % copies], wd[i % copies], y)
 
@@ -206,8 +211,8 @@ def bench_headline(bqi, torch, W, args):
     T = Timer(torch)
     ms_step = T.loop(step, args.steps, check=lambda: y)
     ms_step_eager = T.loop(step, args.steps, graph=False)
-    gemv_loop = T.loop(gemv, args.steps, check=lambda: y)
-    gemv_mean = gemv_loop
+    ms_two = T.loop(step_two_calls, args.steps, check=lambda: y)
+    gemv_mean = T.loop(gemv, args.steps, check=lambda: y)
 
     w_bytes = s.n * s.k + s.n * (s.k // 32) * 2
     a_bytes = s.m * s.k + s.m * (s.k // 32) * 2
@@ -216,7 +221,7 @@ def bench_headline(bqi, torch, W, args):
     quant_bytes = s.m * s.k * 4 + a_bytes
     step_bytes = gemv_bytes + quant_bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    achieved = gemv_bytes / (gemv_mean * 1e-3) / 1e9
+    achieved = step_bytes / (ms_step * 1e-3) / 1e9
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -230,19 +235,27 @@ def bench_headline(bqi, torch, W, args):
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": "decode GEMV M=1 K=4096 N=12288 (quantize + qgemm_q8_0)",
+        "config": {"workload": "decode GEMV M=1 K=4096 N=12288 (quantize_qgemm_q8_0: "
+                               "quantize + Q8_0 GEMV in one launch)",
                    "m": s.m, "k": s.k, "n": s.n, "weights": "Q8_0 of N(0,0.02)",
-                   "activations": "N(0,1) fp32 quantized to Q8_0 in the step",
+                   "activations": "N(0,1) fp32, quantized to Q8_0 in the step",
                    "weight_copies_rotated": copies, "bytes_per_step": step_bytes},
-        "roofline": {"bound": "hbm", "kernel": "k_gemv_reg<1,4>",
+        "roofline": {"bound": "hbm", "kernel": "k_gemv_reg<1,4,ACT_F32> (quantize + GEMV)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic("k_gemv_reg<1,4> decode M=1"),
-                     "bytes_per_launch": gemv_bytes,
-                     "mean_launch_us": round(gemv_mean * 1e3, 3),
+                     "traffic": traffic("k_gemv_reg<1,4,ACT_F32> decode M=1 fused"),
+                     "bytes_per_launch": step_bytes,
+                     "mean_launch_us": round(ms_step * 1e3, 3),
                      "timing": "HIP events around %d back-to-back launches replayed "
                                "from a HIP graph" % args.steps},
         "eager_ms_per_step": round(ms_step_eager, 6),
+        "two_call_step": {"calls": "quantize_q8_0 + qgemm_q8_0", "ms_per_step": round(ms_two, 6),
+                          "GB/s": round(step_bytes / (ms_two * 1e-3) / 1e9, 2)},
+        "gemv_only": {"kernel": "k_gemv_reg<1,4,ACT_Q8>", "mean_launch_us": round(gemv_mean * 1e3, 3),
+                      "bytes_per_launch": gemv_bytes,
+                      "GB/s": round(gemv_bytes / (gemv_mean * 1e-3) / 1e9, 2),
+                      "frac_hbm_peak": round(gemv_bytes / (gemv_mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "traffic": traffic("k_gemv_reg<1,4> decode M=1")}
     }
     ctx = dict(s=s, wq=wq, wd=wd, x=x, step_bytes=step_bytes)
     return res, ctx
@@ -365,8 +378,11 @@ def main():
         bench_copy(torch)
     if "decode" in wl:
         res, ctx = bench_headline(bqi, torch, W, args)
-        log("headline: %.1f GB/s per step, GEMV %.2f us (%.1f%% of HBM peak)" % (
-            res["value"], res["roofline"]["mean_launch_us"], 100 * res["roofline"]["frac"]))
+        log("headline: %.1f GB/s per step (%.2f us, %.1f%% of HBM peak); two calls %.2f us; "
+            "GEMV alone %.2f us (%.1f%%)" % (
+                res["value"], res["roofline"]["mean_launch_us"], 100 * res["roofline"]["frac"],
+                res["two_call_step"]["ms_per_step"] * 1e3, res["gemv_only"]["mean_launch_us"],
+                100 * res["gemv_only"]["frac_hbm_peak"]))
         del ctx["wq"], ctx["wd"]
         torch.cuda.empty_cache()
     also = []

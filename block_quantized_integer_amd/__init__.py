@@ -9,6 +9,7 @@ missing, importing the library functions raises.
 Entry points (same names as the C ABI):
   quantize_q8_0(x)                       -> (q int8 [R][K], d uint16-as-int16 fp16 bits [R][K/32])
   qgemm_q8_0(aq, ad, wq, wd)             -> y fp32 [M][N] = A W^T
+  quantize_qgemm_q8_0(x, wq, wd)         -> (y, q, d): both of the above, fused for decode
   route_topk(topk_ids, n_experts)        -> (counts, offsets, rows)
   qgemm_w4a8_grouped(aq, ad, topk_ids, wq4, wd) -> y fp32 [T][top_k][N]
 
@@ -27,7 +28,8 @@ BQI_OK, BQI_EINVAL, BQI_ESHAPE, BQI_EALIGN, BQI_EHIP = 0, -1, -2, -3, -4
 BQI_F32, BQI_F16 = 0, 1
 
 SYMBOLS = ("bqi_status_string", "bqi_abi_version", "quantize_q8_0", "qgemm_q8_0",
-           "route_topk", "qgemm_w4a8_grouped_workspace_size", "qgemm_w4a8_grouped")
+           "quantize_qgemm_q8_0", "route_topk", "qgemm_w4a8_grouped_workspace_size",
+           "qgemm_w4a8_grouped")
 
 _lib = None
 
@@ -56,6 +58,8 @@ def lib() -> C.CDLL:
     L.quantize_q8_0.argtypes = [P, I32, I64, I64, I64, P, P, P]
     L.qgemm_q8_0.restype = I32
     L.qgemm_q8_0.argtypes = [P, P, I64, P, P, I64, I64, P, P]
+    L.quantize_qgemm_q8_0.restype = I32
+    L.quantize_qgemm_q8_0.argtypes = [P, I32, I64, I64, I64, P, P, I64, P, P, P, P]
     L.route_topk.restype = I32
     L.route_topk.argtypes = [P, I64, I64, I64, P, P, P, P]
     L.qgemm_w4a8_grouped_workspace_size.restype = C.c_size_t
@@ -146,6 +150,40 @@ def qgemm_q8_0(aq, ad, wq, wd, y=None, stream=None):
                           _stream(stream))
     _raise(st, "qgemm_q8_0")
     return y
+
+
+def quantize_qgemm_q8_0(x, wq, wd, y=None, q=None, d=None, stream=None):
+    """Quantize the rows of x (fp32 or fp16, unit column stride) to Q8_0 and
+    multiply by the Q8_0 weights: returns (y fp32 [M][N], q int8 [M][K],
+    d int16 [M][K/32]), identical to quantize_q8_0 followed by qgemm_q8_0 (one
+    launch for decode-sized M)."""
+    torch = _torch()
+    if x.dtype not in (torch.float32, torch.float16):
+        raise TypeError("x must be float32 or float16")
+    if x.dim() != 2 or x.stride(1) != 1 or not x.is_cuda:
+        raise ValueError("x must be a 2-D GPU tensor with unit column stride")
+    _check(wq, torch.int8, 2, "wq")
+    _check(wd, torch.int16, 2, "wd")
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or tuple(wd.shape) != (N, K // 32):
+        raise ValueError("shape mismatch: x %s wq %s wd %s" % (
+            tuple(x.shape), tuple(wq.shape), tuple(wd.shape)))
+    ldx = x.stride(0) if M > 1 else K
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if d is None:
+        d = torch.empty((M, K // 32), dtype=torch.int16, device=x.device)
+    _check(y, torch.float32, 2, "y")
+    _check(q, torch.int8, 2, "q")
+    _check(d, torch.int16, 2, "d")
+    dt = BQI_F32 if x.dtype == torch.float32 else BQI_F16
+    st = lib().quantize_qgemm_q8_0(_ptr(x), dt, M, K, ldx, _ptr(wq), _ptr(wd), N, _ptr(y),
+                                   _ptr(q), _ptr(d), _stream(stream))
+    _raise(st, "quantize_qgemm_q8_0")
+    return y, q, d
 
 
 def route_topk(topk_ids, n_experts, counts=None, offsets=None, rows=None, stream=None):

@@ -40,6 +40,16 @@ WsLayout ws_layout(int64_t rows_total, int64_t n_experts, int64_t k) {
   return L;
 }
 
+// Launch of a validated Q8_0 GEMM: the thin-M kernel for m <= 16, the MFMA
+// kernel otherwise.
+int qgemm_launch(const int8_t *aq, const uint16_t *ad, int64_t m,
+                 const int8_t *wq, const uint16_t *wd, int64_t n, int64_t k,
+                 float *y, hipStream_t s) {
+  if (m <= 16)
+    return hip_status(bqi::launch_gemv_thin(aq, ad, m, wq, wd, n, k, y, s));
+  return hip_status(bqi::launch_gemm_mfma(aq, ad, m, wq, wd, n, k, y, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -55,7 +65,7 @@ const char *bqi_status_string(int status) {
   }
 }
 
-int bqi_abi_version(void) { return 200; }
+int bqi_abi_version(void) { return 210; }
 
 int quantize_q8_0(const void *x, int x_dtype, int64_t rows, int64_t k,
                   int64_t ldx, int8_t *q, uint16_t *d, void *stream) {
@@ -89,15 +99,48 @@ int qgemm_q8_0(const int8_t *aq, const uint16_t *ad, int64_t m,
   if (!aligned(aq, 16) || !aligned(wq, 16) || !aligned(ad, 2) ||
       !aligned(wd, 2) || !aligned(y, 4))
     return BQI_EALIGN;
-  if (m <= 16)
-    return hip_status(
-        bqi::launch_gemv_thin(aq, ad, m, wq, wd, n, k, y, as_stream(stream)));
   // the MFMA kernel indexes tiles, rows and element offsets in 32-bit
-  if ((m + 127) / 128 * ((n + 127) / 128) > kI32Max || m * k > kI32Max ||
-      n * k > kI32Max)
+  if (m > 16 && ((m + 127) / 128 * ((n + 127) / 128) > kI32Max ||
+                 m * k > kI32Max || n * k > kI32Max))
     return BQI_ESHAPE;
-  return hip_status(
-      bqi::launch_gemm_mfma(aq, ad, m, wq, wd, n, k, y, as_stream(stream)));
+  return qgemm_launch(aq, ad, m, wq, wd, n, k, y, as_stream(stream));
+}
+
+int quantize_qgemm_q8_0(const void *x, int x_dtype, int64_t m, int64_t k,
+                        int64_t ldx, const int8_t *wq, const uint16_t *wd,
+                        int64_t n, float *y, int8_t *q, uint16_t *d,
+                        void *stream) {
+  if (x_dtype != BQI_F32 && x_dtype != BQI_F16) return BQI_EINVAL;
+  if (m < 0 || n < 0 || k < 0 || k % kQK != 0 || ldx < k) return BQI_ESHAPE;
+  if (m == 0) return BQI_OK;
+  if (m > kI32Max || n > kI32Max || k > kI32Max) return BQI_ESHAPE;
+  hipStream_t s = as_stream(stream);
+  if (k == 0) {
+    // nothing to quantize; y is an empty sum
+    if (n == 0) return BQI_OK;
+    if (!y) return BQI_EINVAL;
+    if (!aligned(y, 4)) return BQI_EALIGN;
+    return hip_status(bqi::launch_zero_f32(y, m * n, s));
+  }
+  if (!x || !q || !d) return BQI_EINVAL;
+  if (n > 0 && (!wq || !wd || !y)) return BQI_EINVAL;
+  const int64_t esize = x_dtype == BQI_F32 ? 4 : 2;
+  const int64_t vec = x_dtype == BQI_F32 ? 16 : 8;
+  if (!aligned(x, 16) || (ldx * esize) % vec != 0 || !aligned(q, 16) ||
+      !aligned(d, 2))
+    return BQI_EALIGN;
+  if (n > 0 && (!aligned(wq, 16) || !aligned(wd, 2) || !aligned(y, 4)))
+    return BQI_EALIGN;
+  if (m > 16 && ((m + 127) / 128 * ((n + 127) / 128) > kI32Max ||
+                 m * k > kI32Max || n * k > kI32Max))
+    return BQI_ESHAPE;
+  if (n > 0 && bqi::gemv_fused_supported(m, k) && ldx <= kI32Max)
+    return hip_status(bqi::launch_gemv_fused(x, x_dtype == BQI_F16, ldx, m, wq,
+                                             wd, n, k, y, q, d, s));
+  const int st = hip_status(bqi::launch_quantize_q8_0(x, x_dtype == BQI_F16, m,
+                                                      k, ldx, q, d, s));
+  if (st != BQI_OK || n == 0) return st;
+  return qgemm_launch(q, d, m, wq, wd, n, k, y, s);
 }
 
 int route_topk(const int32_t *topk_ids, int64_t n_tokens, int64_t top_k,

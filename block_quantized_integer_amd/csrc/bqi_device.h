@@ -32,6 +32,37 @@ __device__ __forceinline__ int32_t dot4_i8(int32_t a, int32_t b, int32_t c) {
   return __builtin_amdgcn_sdot4(a, b, c, false);
 }
 
+// Q8_0 quantization of one 32-element block by the 8 consecutive lanes that
+// own it (lane sub = lane % 8 holds elements 4*sub .. 4*sub+3 in v): the
+// block's absmax is reduced across the 8 lanes, d = fp16_rne(amax / 127)
+// with a correctly rounded fp32 division, and each code is
+// clamp(round-half-away(x / d), -127, 127) with the correctly rounded fp32
+// quotient by the stored d (d == 0 gives codes 0 and scale bits 0).  Returns
+// this lane's 4 codes packed (element 4*sub + i in byte i) and sets the
+// block's scale bits.  Every quantizer in the library goes through this
+// function, so all of them produce identical codes.  Never compile with
+// fast-math.
+__device__ __forceinline__ uint32_t q8_0_quantize4(const float (&v)[4], uint16_t &d_bits) {
+  float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  // reduce over the 8 lanes of this block (lanes differ in bits 0..2)
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  const _Float16 dh = (_Float16)(amax / 127.0f);  // IEEE div, then RNE
+  const float dd = (float)dh;
+  uint32_t packed = 0;
+  if (dd != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float t = roundf(v[i] / dd);  // half away from zero
+      t = fminf(fmaxf(t, -127.0f), 127.0f);
+      packed |= ((uint32_t)(int32_t)t & 0xffu) << (8 * i);
+    }
+  }
+  d_bits = dd != 0.0f ? __builtin_bit_cast(uint16_t, dh) : (uint16_t)0;
+  return packed;
+}
+
 // 1.5 * 2^23: an fp32 whose ulp is exactly 1.  An int32 P with |P| < 2^22
 // added to its bit pattern gives the bit pattern of the fp32 value
 // 1.5 * 2^23 + P, exactly.  The MFMA kernels use it as the int32 accumulator

@@ -21,6 +21,13 @@ hipError_t launch_gemv_thin(const int8_t *aq, const uint16_t *ad, int64_t m,
                             const int8_t *wq, const uint16_t *wd, int64_t n,
                             int64_t k, float *y, hipStream_t stream);
 
+// fused quantize + thin-M GEMM (one launch) for the sizes it covers
+bool gemv_fused_supported(int64_t m, int64_t k);
+hipError_t launch_gemv_fused(const void *x, bool f16, int64_t ldx, int64_t m,
+                             const int8_t *wq, const uint16_t *wd, int64_t n,
+                             int64_t k, float *y, int8_t *q_out,
+                             uint16_t *d_out, hipStream_t stream);
+
 // large-M Q8_0 GEMM on int8 MFMA
 hipError_t launch_gemm_mfma(const int8_t *aq, const uint16_t *ad, int64_t m,
                             const int8_t *wq, const uint16_t *wd, int64_t n,

@@ -187,46 +187,85 @@ __device__ __forceinline__ float half_wave_sum(float v) {
   return v;
 }
 
+// Activation source of the register kernel: Q8_0 codes and scales, or fp32 /
+// fp16 values that every workgroup quantizes itself (the fused
+// quantize-and-multiply decode path).
+enum ActSrc { ACT_Q8 = 0, ACT_F32 = 1, ACT_F16 = 2 };
+
+// Threads per workgroup: 4 waves for Q8_0 input; 8 waves when every
+// workgroup quantizes the activations itself, which halves the number of
+// workgroups repeating that work.
+constexpr int reg_threads(int src) { return src == ACT_Q8 ? 256 : 512; }
+
 // (no __restrict__ on the inputs: with it the compiler may move the scale
 // loads across the memory clobber below, behind the barrier)
-template <int MT, int CH>
-__global__ __launch_bounds__(256) void k_gemv_reg(
-    const int8_t *aq, const uint16_t *ad, int m, const int8_t *wq,
-    const uint16_t *wd, int n, int k, float *y) {
+template <int MT, int CH, int SRC>
+__global__ __launch_bounds__(reg_threads(SRC)) void k_gemv_reg(
+    const int8_t *aq, const uint16_t *ad, const void *x, int ldx, int m,
+    const int8_t *wq, const uint16_t *wd, int n, int k, float *y,
+    int8_t *q_out, uint16_t *d_out) {
   static_assert(MT * CH * 1024 <= REG_ACT_BYTES, "activation stage too small");
   // one spare 16-byte slot (and scale slot) takes the stores of lanes with
   // nothing to stage, so the staging stores stay unconditional
   __shared__ __attribute__((aligned(16))) int8_t sA[MT * CH * 1024 + 16];
   __shared__ uint16_t sAd[MT * CH * 32 + 1];
   const int lane = threadIdx.x & 63;
-  const int row0 = ((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * REG_RPW;
+  constexpr int NT = reg_threads(SRC);
+  const int row0 = ((int)blockIdx.x * (NT / 64) + (int)(threadIdx.x >> 6)) * REG_RPW;
   const int nbk = k / QK;
   const bool even = (lane & 1) == 0;
 
-  // Load order matters: loads retire in order, so the activation codes (L2
-  // hits) are requested first, then all weight loads (HBM); writing the
-  // activations to LDS then waits only for the former.  Every load is
+  // Load order matters: loads retire in order, so the activations (L2 hits)
+  // are requested first, then all weight loads (HBM); staging the
+  // activations in LDS then waits only for the former.  Every load is
   // unconditional (lanes past k re-read a valid address) so that none waits
   // on another; values are masked afterwards.
-  constexpr int STAGE = MT * CH * 64 / 256;  // 16-byte activation chunks per thread
-  static_assert(STAGE >= 1 || MT * CH * 64 < 256, "");
+  constexpr int STAGE = MT * CH * 64 / NT;  // 16-byte activation chunks per thread
+  static_assert(STAGE >= 1 || MT * CH * 64 < NT, "");
   constexpr int STAGE_N = STAGE > 0 ? STAGE : 1;
+  constexpr int SD_N = MT * CH * 32 / NT > 0 ? MT * CH * 32 / NT : 1;
+  // fused path: 8 lanes per 32-element block, 4 elements per lane
+  // quantize tasks per thread (tasks past the staged blocks are masked)
+  constexpr int QT = SRC == ACT_Q8 ? 1 : (MT * CH * 256 + NT - 1) / NT;
   i32x4 st[STAGE_N];
-  uint16_t st_d[MT * CH * 32 / 256 > 0 ? MT * CH * 32 / 256 : 1];
-  constexpr int SD_N = MT * CH * 32 / 256 > 0 ? MT * CH * 32 / 256 : 1;
+  uint16_t st_d[SD_N];
+  float xv[QT][4];
+  if constexpr (SRC == ACT_Q8) {
 #pragma unroll
-  for (int q = 0; q < STAGE_N; ++q) {
-    const int c = (int)threadIdx.x + 256 * q;
-    const int i = c / (CH * 64), cc = c % (CH * 64);
-    const bool ok = i < m && cc < k / 16;
-    st[q] = *reinterpret_cast<const i32x4 *>(aq + (ok ? (int64_t)i * k + 16 * cc : 0));
-  }
+    for (int q = 0; q < STAGE_N; ++q) {
+      const int c = (int)threadIdx.x + NT * q;
+      const int i = c / (CH * 64), cc = c % (CH * 64);
+      const bool ok = i < m && cc < k / 16;
+      st[q] = *reinterpret_cast<const i32x4 *>(aq + (ok ? (int64_t)i * k + 16 * cc : 0));
+    }
 #pragma unroll
-  for (int q = 0; q < SD_N; ++q) {
-    const int c = (int)threadIdx.x + 256 * q;
-    const int i = c / (CH * 32), b = c % (CH * 32);
-    const bool ok = i < m && b < nbk;
-    st_d[q] = ad[ok ? (int64_t)i * nbk + b : 0];
+    for (int q = 0; q < SD_N; ++q) {
+      const int c = (int)threadIdx.x + NT * q;
+      const int i = c / (CH * 32), b = c % (CH * 32);
+      const bool ok = i < m && b < nbk;
+      st_d[q] = ad[ok ? (int64_t)i * nbk + b : 0];
+    }
+  } else {
+    // task t = tid + NT u: block t/8 of the staged rows (row i, block b),
+    // elements 4*(t%8) .. +3; tasks past m or k re-read element 0
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      const int t = (int)threadIdx.x + NT * u;
+      const int blk = t >> 3, sub = t & 7;
+      const int i = blk / (CH * 32), b = blk % (CH * 32);
+      const bool ok = i < m && b < nbk;
+      const int64_t off = ok ? (int64_t)i * ldx + QK * b + 4 * sub : 0;
+      if constexpr (SRC == ACT_F32) {
+        const f32x4 r = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(x) + off);
+        xv[u][0] = r.x; xv[u][1] = r.y; xv[u][2] = r.z; xv[u][3] = r.w;
+      } else {
+        const uint2 r = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(x) + off);
+        xv[u][0] = half_bits_to_float((uint16_t)(r.x & 0xffffu));
+        xv[u][1] = half_bits_to_float((uint16_t)(r.x >> 16));
+        xv[u][2] = half_bits_to_float((uint16_t)(r.y & 0xffffu));
+        xv[u][3] = half_bits_to_float((uint16_t)(r.y >> 16));
+      }
+    }
   }
 
   i32x4 w[REG_RPW][CH];
@@ -247,19 +286,40 @@ __global__ __launch_bounds__(256) void k_gemv_reg(
   // memory clobber stops the compiler from sinking them to their uses)
   __asm__ volatile("" ::: "memory");
 
+  if constexpr (SRC == ACT_Q8) {
 #pragma unroll
-  for (int q = 0; q < STAGE_N; ++q) {
-    const int c = (int)threadIdx.x + 256 * q;
-    const int i = c / (CH * 64), cc = c % (CH * 64);
-    const bool ok = c < MT * CH * 64 && i < m && cc < k / 16;
-    *reinterpret_cast<i32x4 *>(sA + (ok ? i * (CH * 1024) + 16 * cc : MT * CH * 1024)) = st[q];
-  }
+    for (int q = 0; q < STAGE_N; ++q) {
+      const int c = (int)threadIdx.x + NT * q;
+      const int i = c / (CH * 64), cc = c % (CH * 64);
+      const bool ok = c < MT * CH * 64 && i < m && cc < k / 16;
+      *reinterpret_cast<i32x4 *>(sA + (ok ? i * (CH * 1024) + 16 * cc : MT * CH * 1024)) = st[q];
+    }
 #pragma unroll
-  for (int q = 0; q < SD_N; ++q) {
-    const int c = (int)threadIdx.x + 256 * q;
-    const int i = c / (CH * 32), b = c % (CH * 32);
-    const bool ok = c < MT * CH * 32 && i < m && b < nbk;
-    sAd[ok ? i * (CH * 32) + b : MT * CH * 32] = st_d[q];
+    for (int q = 0; q < SD_N; ++q) {
+      const int c = (int)threadIdx.x + NT * q;
+      const int i = c / (CH * 32), b = c % (CH * 32);
+      const bool ok = c < MT * CH * 32 && i < m && b < nbk;
+      sAd[ok ? i * (CH * 32) + b : MT * CH * 32] = st_d[q];
+    }
+  } else {
+    // quantize while the weight loads are in flight (same device routine as
+    // quantize_q8_0, so the codes are identical); workgroup 0 also writes the
+    // Q8_0 activations out
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      const int t = (int)threadIdx.x + NT * u;
+      const int blk = t >> 3, sub = t & 7;
+      const int i = blk / (CH * 32), b = blk % (CH * 32);
+      const bool ok = i < m && b < nbk;
+      uint16_t dbits;
+      const uint32_t packed = q8_0_quantize4(xv[u], dbits);
+      *reinterpret_cast<uint32_t *>(sA + (ok ? i * (CH * 1024) + QK * b + 4 * sub : MT * CH * 1024)) = packed;
+      if (sub == 0) sAd[ok ? i * (CH * 32) + b : MT * CH * 32] = dbits;
+      if (ok && blockIdx.x == 0) {
+        *reinterpret_cast<uint32_t *>(q_out + (int64_t)i * k + QK * b + 4 * sub) = packed;
+        if (sub == 0) d_out[(int64_t)i * nbk + b] = dbits;
+      }
+    }
   }
   __syncthreads();
 
@@ -313,30 +373,33 @@ __global__ __launch_bounds__(256) void k_gemv_reg(
   }
 }
 
-template <int MT, int CH>
-hipError_t launch_reg(const int8_t *aq, const uint16_t *ad, int64_t m,
-                      const int8_t *wq, const uint16_t *wd, int64_t n, int64_t k,
-                      float *y, hipStream_t stream) {
-  const int64_t rows_per_wg = 4 * REG_RPW;
+template <int MT, int CH, int SRC>
+hipError_t launch_reg(const int8_t *aq, const uint16_t *ad, const void *x, int64_t ldx,
+                      int64_t m, const int8_t *wq, const uint16_t *wd, int64_t n, int64_t k,
+                      float *y, int8_t *q_out, uint16_t *d_out, hipStream_t stream) {
+  constexpr int NT = reg_threads(SRC);
+  const int64_t rows_per_wg = (NT / 64) * REG_RPW;
   const int64_t wgs = (n + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL((k_gemv_reg<MT, CH>), dim3((unsigned)wgs), dim3(256), 0,
-                     stream, aq, ad, (int)m, wq, wd, (int)n, (int)k, y);
+  hipLaunchKernelGGL((k_gemv_reg<MT, CH, SRC>), dim3((unsigned)wgs), dim3(NT), 0,
+                     stream, aq, ad, x, (int)ldx, (int)m, wq, wd, (int)n, (int)k, y,
+                     q_out, d_out);
   return hipGetLastError();
 }
 
-template <int MT>
-hipError_t launch_reg_ch(const int8_t *aq, const uint16_t *ad, int64_t m,
-                         const int8_t *wq, const uint16_t *wd, int64_t n,
-                         int64_t k, float *y, hipStream_t stream) {
+template <int MT, int SRC>
+hipError_t launch_reg_ch(const int8_t *aq, const uint16_t *ad, const void *x, int64_t ldx,
+                         int64_t m, const int8_t *wq, const uint16_t *wd, int64_t n,
+                         int64_t k, float *y, int8_t *q_out, uint16_t *d_out,
+                         hipStream_t stream) {
   const int64_t ch = (k + 1023) / 1024;
-  if (ch <= 1) return launch_reg<MT, 1>(aq, ad, m, wq, wd, n, k, y, stream);
-  if (ch <= 2) return launch_reg<MT, 2>(aq, ad, m, wq, wd, n, k, y, stream);
-  if (ch <= 4) return launch_reg<MT, 4>(aq, ad, m, wq, wd, n, k, y, stream);
+  if (ch <= 1) return launch_reg<MT, 1, SRC>(aq, ad, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
+  if (ch <= 2) return launch_reg<MT, 2, SRC>(aq, ad, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
+  if (ch <= 4) return launch_reg<MT, 4, SRC>(aq, ad, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
   if constexpr (MT <= 2) {
-    if (ch <= 8) return launch_reg<MT, 8>(aq, ad, m, wq, wd, n, k, y, stream);
+    if (ch <= 8) return launch_reg<MT, 8, SRC>(aq, ad, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
   }
   if constexpr (MT <= 1) {
-    if (ch <= 16) return launch_reg<MT, 16>(aq, ad, m, wq, wd, n, k, y, stream);
+    if (ch <= 16) return launch_reg<MT, 16, SRC>(aq, ad, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
   }
   return hipErrorInvalidValue;  // not reached: the dispatcher checks the size
 }
@@ -363,17 +426,36 @@ hipError_t launch_mt(const int8_t *aq, const uint16_t *ad, int64_t m,
 hipError_t launch_gemv_thin(const int8_t *aq, const uint16_t *ad, int64_t m,
                             const int8_t *wq, const uint16_t *wd, int64_t n,
                             int64_t k, float *y, hipStream_t stream) {
-  // register kernel while the activation slice fits in 64 VGPRs per lane
   // register kernel while m * k activation codes fit its LDS stage
   const int64_t ch = (k + 1023) / 1024;
-  if (m <= 1 && ch <= 16) return launch_reg_ch<1>(aq, ad, m, wq, wd, n, k, y, stream);
-  if (m <= 2 && ch <= 8) return launch_reg_ch<2>(aq, ad, m, wq, wd, n, k, y, stream);
-  if (m <= 4 && ch <= 4) return launch_reg_ch<4>(aq, ad, m, wq, wd, n, k, y, stream);
+  if (m <= 1 && ch <= 16) return launch_reg_ch<1, ACT_Q8>(aq, ad, nullptr, 0, m, wq, wd, n, k, y, nullptr, nullptr, stream);
+  if (m <= 2 && ch <= 8) return launch_reg_ch<2, ACT_Q8>(aq, ad, nullptr, 0, m, wq, wd, n, k, y, nullptr, nullptr, stream);
+  if (m <= 4 && ch <= 4) return launch_reg_ch<4, ACT_Q8>(aq, ad, nullptr, 0, m, wq, wd, n, k, y, nullptr, nullptr, stream);
   if (m <= 1) return launch_mt<1>(aq, ad, m, wq, wd, n, k, y, stream);
   if (m <= 2) return launch_mt<2>(aq, ad, m, wq, wd, n, k, y, stream);
   if (m <= 4) return launch_mt<4>(aq, ad, m, wq, wd, n, k, y, stream);
   if (m <= 8) return launch_mt<8>(aq, ad, m, wq, wd, n, k, y, stream);
   return launch_mt<16>(aq, ad, m, wq, wd, n, k, y, stream);
+}
+
+bool gemv_fused_supported(int64_t m, int64_t k) {
+  const int64_t ch = (k + 1023) / 1024;
+  return (m <= 1 && ch <= 16) || (m <= 2 && ch <= 8) || (m <= 4 && ch <= 4);
+}
+
+hipError_t launch_gemv_fused(const void *x, bool f16, int64_t ldx, int64_t m,
+                             const int8_t *wq, const uint16_t *wd, int64_t n,
+                             int64_t k, float *y, int8_t *q_out,
+                             uint16_t *d_out, hipStream_t stream) {
+  const int64_t ch = (k + 1023) / 1024;
+  if (f16) {
+    if (m <= 1 && ch <= 16) return launch_reg_ch<1, ACT_F16>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
+    if (m <= 2 && ch <= 8) return launch_reg_ch<2, ACT_F16>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
+    return launch_reg_ch<4, ACT_F16>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
+  }
+  if (m <= 1 && ch <= 16) return launch_reg_ch<1, ACT_F32>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
+  if (m <= 2 && ch <= 8) return launch_reg_ch<2, ACT_F32>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
+  return launch_reg_ch<4, ACT_F32>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
 }
 
 }  // namespace bqi

@@ -50,27 +50,10 @@ __global__ __launch_bounds__(256) void k_quantize_q8_0(
       v[2] = raw.z;
       v[3] = raw.w;
     }
-    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])),
-                       fmaxf(fabsf(v[2]), fabsf(v[3])));
-    // reduce over the 8 lanes of this block (lanes differ in bits 0..2)
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    amax = fmaxf(amax, __shfl_xor(amax, 4));
-
-    const _Float16 dh = (_Float16)(amax / 127.0f);  // IEEE div, then RNE
-    const float dd = (float)dh;
-    uint32_t packed = 0;
-    if (dd != 0.0f) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float t = roundf(v[i] / dd);  // half away from zero
-        t = fminf(fmaxf(t, -127.0f), 127.0f);
-        packed |= ((uint32_t)(int32_t)t & 0xffu) << (8 * i);
-      }
-    }
+    uint16_t dbits;
+    const uint32_t packed = q8_0_quantize4(v, dbits);
     *reinterpret_cast<uint32_t *>(q + (size_t)blk * QK + sub * 4) = packed;
-    if (sub == 0)
-      d[blk] = dd != 0.0f ? __builtin_bit_cast(uint16_t, dh) : (uint16_t)0;
+    if (sub == 0) d[blk] = dbits;
   }
 }
 

@@ -68,8 +68,9 @@ extern "C" {
 /* Human-readable name of a status code (static string, never NULL). */
 BQI_API const char *bqi_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor): 200.  Version 200 added
- * the k argument of qgemm_w4a8_grouped_workspace_size. */
+/* ABI version of this header (major * 100 + minor): 210.  Version 200 added
+ * the k argument of qgemm_w4a8_grouped_workspace_size; 210 added
+ * quantize_qgemm_q8_0. */
 BQI_API int bqi_abi_version(void);
 
 /*
@@ -118,6 +119,30 @@ BQI_API int quantize_q8_0(const void *x, int x_dtype, int64_t rows, int64_t k,
 BQI_API int qgemm_q8_0(const int8_t *aq, const uint16_t *ad, int64_t m,
                const int8_t *wq, const uint16_t *wd, int64_t n, int64_t k,
                float *y, void *stream);
+
+/*
+ * quantize_qgemm_q8_0 -- quantize_q8_0 followed by qgemm_q8_0, the decode
+ * step of the Q8_0 path (activation quantization, then the thin-M GEMM that
+ * page 3 "Results" names as the decode bottleneck).
+ *
+ *   x  [m][ldx] fp32 (x_dtype = BQI_F32) or fp16 (BQI_F16) activations
+ *   wq [n][k] int8, wd [n][k/32] fp16 bits   -- Q8_0 weights
+ *   y  [m][n] fp32 (output) = Q8_0(x) * W^T, bit-identical to qgemm_q8_0 on
+ *      the codes below
+ *   q  [m][k] int8, d [m][k/32] fp16 bits (output): the Q8_0 activations,
+ *      bit-identical to quantize_q8_0(x)
+ *
+ * For m <= 4 with k <= 16384 / m (rounded up to 1024) it is one launch: every
+ * workgroup quantizes the activation rows itself while its weight loads are
+ * in flight, which saves the quantizer's launch on the decode path.  Other
+ * sizes run quantize_q8_0 and qgemm_q8_0 back to back on `stream`.
+ * n == 0 only quantizes.  Requirements: those of quantize_q8_0 and
+ * qgemm_q8_0.
+ */
+BQI_API int quantize_qgemm_q8_0(const void *x, int x_dtype, int64_t m, int64_t k,
+                        int64_t ldx, const int8_t *wq, const uint16_t *wd,
+                        int64_t n, float *y, int8_t *q, uint16_t *d,
+                        void *stream);
 
 /*
  * route_topk -- group routed rows by expert (the routing step of the grouped

@@ -43,7 +43,7 @@ def test_library_exports_exactly_the_header_symbols():
 
 def test_status_strings():
     L = bqi.lib()
-    assert L.bqi_abi_version() == 200
+    assert L.bqi_abi_version() == 210
     for st in (OK, EINVAL, ESHAPE, EALIGN, bqi.BQI_EHIP):
         assert L.bqi_status_string(st).decode().startswith("BQI_")
     assert L.bqi_status_string(12345)
@@ -89,6 +89,30 @@ def test_qgemm_validation():
     assert g(0, 0, 0, 0, 0, 8, 32, 0) == OK
     assert g(0, 0, 8, 0, 0, 0, 32, 0) == OK
     assert g(FAKE, FAKE, 1 << 31, FAKE, FAKE, 8, 32, FAKE) == ESHAPE
+
+
+def fq(x=FAKE, dt=0, m=1, k=64, ldx=64, wq=FAKE, wd=FAKE, n=8, y=FAKE, qp=FAKE, dp=FAKE):
+    return bqi.lib().quantize_qgemm_q8_0(P(x), dt, m, k, ldx, P(wq), P(wd), n, P(y), P(qp),
+                                         P(dp), P(0))
+
+
+def test_fused_quantize_qgemm_validation():
+    assert fq(dt=5) == EINVAL
+    assert fq(m=-1) == ESHAPE
+    assert fq(k=48, ldx=48) == ESHAPE
+    assert fq(ldx=32) == ESHAPE
+    assert fq(x=0) == EINVAL
+    assert fq(qp=0) == EINVAL
+    assert fq(dp=0) == EINVAL
+    assert fq(wq=0) == EINVAL
+    assert fq(y=0) == EINVAL
+    assert fq(x=FAKE + 4) == EALIGN
+    assert fq(ldx=66) == EALIGN           # fp32 rows must stay 16-byte aligned
+    assert fq(qp=FAKE + 8) == EALIGN
+    assert fq(wq=FAKE + 8) == EALIGN
+    assert fq(y=FAKE + 2) == EALIGN
+    assert fq(m=0) == OK
+    assert fq(m=1 << 31) == ESHAPE
 
 
 def test_route_validation():

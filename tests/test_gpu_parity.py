@@ -255,6 +255,48 @@ def test_decode_workload_full(decode_weights, m):
     assert_within_bound(y, yr, asum, k // 32, "decode m=%d" % m)
 
 
+@pytest.mark.parametrize("m,k,n,dtype", [
+    (1, 4096, 12288, "f32"),    # the decode workload, fused (one launch)
+    (4, 4096, 12288, "f32"),    # fused, four rows
+    (2, 8192, 300, "f16"),      # fused, fp16 input, ragged N
+    (1, 16384, 77, "f32"),      # fused, largest K of the single-row kernel
+    (3, 96, 40, "f32"),         # fused, K shorter than one 1 KB chunk
+    (16, 4096, 512, "f32"),     # not fused: quantize + thin-M GEMM
+    (40, 256, 130, "f16"),      # not fused: quantize + MFMA GEMM
+])
+def test_fused_quantize_qgemm(decode_weights, m, k, n, dtype):
+    """quantize_qgemm_q8_0: codes and scales bit-exact to the oracle's
+    quantizer, y bit-identical to qgemm_q8_0 on those codes and within the
+    bound of the oracle's exact value."""
+    log("fused m=%d k=%d n=%d %s" % (m, k, n, dtype))
+    if (k, n) == (W.DECODE[0].k, W.DECODE[0].n):
+        qw_g, dw_g, qw, dw = decode_weights
+    else:
+        qw_g, dw_g, qw, dw = check_quantize(W.weights("decode", n, k, seed=k + n), "fused W")
+    a = W.activations("decode", m, k, seed=3 + m)
+    if dtype == "f16":
+        a = a.astype(np.float16)
+    y, q, d = bqi.quantize_qgemm_q8_0(dev_tensor(a), qw_g, dw_g)
+    qr, dr = oracle.quantize_q8_0(a)
+    assert np.array_equal(host(q), qr) and np.array_equal(host(d), dr), "fused codes/scales"
+    y2 = bqi.qgemm_q8_0(q, d, qw_g, dw_g)
+    assert torch.equal(y, y2), "fused y differs from qgemm_q8_0 on the same codes"
+    yr, asum = oracle.qgemm_q8_0(qr, dr, qw, dw, nthreads=oracle_threads())
+    assert_within_bound(host(y), yr, asum, k // 32, "fused m=%d k=%d" % (m, k))
+
+
+def test_fused_quantize_qgemm_strided_rows(decode_weights):
+    """Row stride ldx > k (a column slice of a wider fp32 tensor)."""
+    qw_g, dw_g, qw, dw = decode_weights
+    k = W.DECODE[0].k
+    wide = W.activations("decode", 3, k + 64, seed=11)
+    x = dev_tensor(wide)[:, :k]
+    y, q, d = bqi.quantize_qgemm_q8_0(x, qw_g, dw_g)
+    qr, dr = oracle.quantize_q8_0(np.ascontiguousarray(wide[:, :k]))
+    assert np.array_equal(host(q), qr) and np.array_equal(host(d), dr)
+    assert torch.equal(y, bqi.qgemm_q8_0(q, d, qw_g, dw_g))
+
+
 def sampled_check(y, qa, da, qw, dw, k, seed, what, n_samples=4096):
     g = np.random.default_rng(seed)
     m, n = y.shape
