@@ -66,6 +66,9 @@ def _load():
                                           P, P, C.c_int]),
         "orc_qgemm_w4a8_grouped_at": (None, [P, P, I64, P, I64, P, P, I64, I64,
                                              I64, P, P, I64, P, P]),
+        "orc_moe_combine": (None, [P, P, I64, I64, I64, P, P]),
+        "orc_gguf_q8_0_to_planar": (None, [P, I64, I64, P, P]),
+        "orc_gguf_q4_0_to_planar": (None, [P, I64, I64, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -258,3 +261,39 @@ def qgemm_w4a8_grouped_at(aq, ad, ids, wq4, wd, ri, cj):
                                       _p(wd), E, n, k, _p(ri), _p(cj), ri.size,
                                       _p(y), _p(a))
     return y, a
+
+
+def moe_combine(y: np.ndarray, p: np.ndarray):
+    """out[t][c] = sum_j p[t][j] * y[t][j][c] in fp64 (exact products, slot
+    order), with the tolerance scale sum_j |p y|.  y fp32 [T][top_k][n], p fp32
+    [T][top_k].  Returns (out, asum) fp64 [T][n].  See bq_oracle.h."""
+    y = np.ascontiguousarray(y, np.float32)
+    p = np.ascontiguousarray(p, np.float32)
+    T, top_k, n = y.shape
+    assert p.shape == (T, top_k)
+    out = np.empty((T, n), np.float64)
+    asum = np.empty((T, n), np.float64)
+    _load().orc_moe_combine(_p(y), _p(p), T, top_k, n, _p(out), _p(asum))
+    return out, asum
+
+
+def gguf_q8_0_to_planar(blocks: np.ndarray, rows: int, k: int):
+    """Split a GGUF Q8_0 block array (uint8, rows*k/32*34 bytes) into codes
+    int8 [rows][k] and scale bits uint16 [rows][k/32]."""
+    blocks = np.ascontiguousarray(blocks, np.uint8)
+    assert k % QK == 0 and blocks.size == rows * (k // QK) * 34
+    q = np.empty((rows, k), np.int8)
+    d = np.empty((rows, k // QK), np.uint16)
+    _load().orc_gguf_q8_0_to_planar(_p(blocks), rows, k, _p(q), _p(d))
+    return q, d
+
+
+def gguf_q4_0_to_planar(blocks: np.ndarray, rows: int, k: int):
+    """Split a GGUF Q4_0 block array (uint8, rows*k/32*18 bytes) into packed
+    codes uint8 [rows][k/2] and scale bits uint16 [rows][k/32]."""
+    blocks = np.ascontiguousarray(blocks, np.uint8)
+    assert k % QK == 0 and blocks.size == rows * (k // QK) * 18
+    packed = np.empty((rows, k // 2), np.uint8)
+    d = np.empty((rows, k // QK), np.uint16)
+    _load().orc_gguf_q4_0_to_planar(_p(blocks), rows, k, _p(packed), _p(d))
+    return packed, d

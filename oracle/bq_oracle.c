@@ -397,3 +397,47 @@ void orc_qgemm_w4a8_grouped_at(const int8_t *aq, const uint16_t *ad, int64_t T,
     w4_output(aq, ad, ids, top_k, wq4, wd, E, n, k, ri[c], cj[c],
               y ? y + c : NULL, asum ? asum + c : NULL);
 }
+
+/* ---- MoE combine ---------------------------------------------------------------- */
+
+void orc_moe_combine(const float *y, const float *p, int64_t T, int64_t top_k,
+                     int64_t n, double *out, double *asum) {
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t c = 0; c < n; ++c) {
+      double s = 0.0, a = 0.0;
+      for (int64_t j = 0; j < top_k; ++j) {
+        /* product of two fp32 values: exact in fp64 (24 + 24 bits) */
+        const double term = (double)p[t * top_k + j] * (double)y[(t * top_k + j) * n + c];
+        s += term;
+        a += fabs(term);
+      }
+      out[t * n + c] = s;
+      if (asum) asum[t * n + c] = a;
+    }
+}
+
+/* ---- GGUF block import ---------------------------------------------------------- */
+
+static uint16_t le16(const uint8_t *b) { return (uint16_t)(b[0] | (b[1] << 8)); }
+
+void orc_gguf_q8_0_to_planar(const uint8_t *blocks, int64_t rows, int64_t k,
+                             int8_t *q, uint16_t *d) {
+  const int64_t nb = k / 32;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint8_t *blk = blocks + (r * nb + b) * 34;
+      d[r * nb + b] = le16(blk);
+      for (int i = 0; i < 32; ++i) q[r * k + 32 * b + i] = (int8_t)blk[2 + i];
+    }
+}
+
+void orc_gguf_q4_0_to_planar(const uint8_t *blocks, int64_t rows, int64_t k,
+                             uint8_t *packed, uint16_t *d) {
+  const int64_t nb = k / 32;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint8_t *blk = blocks + (r * nb + b) * 18;
+      d[r * nb + b] = le16(blk);
+      for (int i = 0; i < 16; ++i) packed[r * (k / 2) + 16 * b + i] = blk[2 + i];
+    }
+}

@@ -130,6 +130,36 @@ void orc_qgemm_w4a8_grouped_at(const int8_t *aq, const uint16_t *ad, int64_t T,
                                const int64_t *ri, const int64_t *cj,
                                int64_t count, double *y, double *asum);
 
+/* ---- MoE combine (the step after the grouped GEMM) ---------------------------
+ * "A 35B Hybrid-Attention Mixture-of-Experts Model on a 6GB 2011 GPU"
+ * (gist.science summary), Method 1: the grouped 4-bit GEMM serves the MoE
+ * routing; each token's expert outputs are then weighted by its router
+ * probabilities and summed back in token order (Method 2 names the router
+ * weighting).  For token t and column c:
+ *   out[t][c] = sum_{j < top_k} p[t][j] * y[t][j][c]
+ * Each product of two fp32 values is exact in fp64 and the sum is taken in
+ * fp64 in slot order; asum[t][c] = sum_j |p[t][j] * y[t][j][c]| is the
+ * tolerance scale.  y is [T][top_k][n] (fp32), p is [T][top_k]. */
+void orc_moe_combine(const float *y, const float *p, int64_t T, int64_t top_k,
+                     int64_t n, double *out, double *asum);
+
+/* ---- GGUF block import ----------------------------------------------------------
+ * "I wrote a custom CUDA inference engine to run Qwen3.5-27B on a $130 mining
+ * card", Honest benchmark: the comparison runs on Q8_0 GGUF files.  On disk a
+ * GGUF tensor of R rows x K columns (K % 32 == 0) is a contiguous array of
+ * R*K/32 blocks, row-major, each block holding its fp16 scale (2 bytes,
+ * little-endian) followed by its codes:
+ *   Q8_0: 34 bytes = scale + 32 int8 codes;
+ *   Q4_0: 18 bytes = scale + 16 bytes, byte j holding element j in its low
+ *         nibble and element j+16 in its high nibble (value (nibble-8)*scale).
+ * These split a block array into the planar layout of this library: codes
+ * [R][K] (Q8_0) or packed [R][K/2] (Q4_0, the same nibble order), and scales
+ * [R][K/32]. */
+void orc_gguf_q8_0_to_planar(const uint8_t *blocks, int64_t rows, int64_t k,
+                             int8_t *q, uint16_t *d);
+void orc_gguf_q4_0_to_planar(const uint8_t *blocks, int64_t rows, int64_t k,
+                             uint8_t *packed, uint16_t *d);
+
 #ifdef __cplusplus
 }
 #endif

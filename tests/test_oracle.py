@@ -448,3 +448,121 @@ def test_w4a8_single_expert_is_plain_gemm():
     y, _ = oracle.qgemm_w4a8_grouped(aq, ad, np.zeros((T, 1), np.int32), oracle.pack_w4(codes), wd)
     ref = _dequant(aq, ad) @ _dequant((codes[0].astype(np.int16) - 8).astype(np.int8), wd[0]).T
     assert np.allclose(y[:, 0, :], ref, rtol=1e-12, atol=1e-300)
+
+
+# ---------------------------------------------------------------------------
+# MoE combine (the step after the grouped GEMM)
+# ---------------------------------------------------------------------------
+
+def test_moe_combine_exact_rational_tiny():
+    g = np.random.default_rng(21)
+    T, top_k, n = 3, 4, 5
+    y = (g.standard_normal((T, top_k, n)) * 10).astype(np.float32)
+    p = g.random((T, top_k)).astype(np.float32)
+    out, asum = oracle.moe_combine(y, p)
+    for t in range(T):
+        for c in range(n):
+            terms = [Fraction(float(p[t, j])) * Fraction(float(y[t, j, c])) for j in range(top_k)]
+            exact = sum(terms)
+            a = sum(abs(x) for x in terms)
+            # fp64 sum of exact products: top_k roundings at most
+            assert abs(Fraction(out[t, c]) - exact) <= Fraction(top_k, 2 ** 52) * a
+            assert asum[t, c] == float(a) or abs(Fraction(asum[t, c]) - a) <= Fraction(top_k, 2 ** 52) * a
+
+
+def test_moe_combine_closed_forms_and_numpy():
+    g = np.random.default_rng(22)
+    T, top_k, n = 7, 8, 33
+    y = g.standard_normal((T, top_k, n)).astype(np.float32)
+    # one-hot weights pick one slot exactly
+    p = np.zeros((T, top_k), np.float32)
+    pick = g.integers(0, top_k, T)
+    p[np.arange(T), pick] = 1.0
+    out, _ = oracle.moe_combine(y, p)
+    assert np.array_equal(out, y[np.arange(T), pick].astype(np.float64))
+    # equal slots with power-of-two weights summing to 1 reproduce the slot
+    y_eq = np.repeat(y[:, :1, :], top_k, axis=1)
+    out, _ = oracle.moe_combine(y_eq, np.full((T, top_k), 1.0 / top_k, np.float32))
+    assert np.array_equal(out, y_eq[:, 0, :].astype(np.float64))
+    # numpy einsum in fp64
+    p = g.random((T, top_k)).astype(np.float32)
+    out, asum = oracle.moe_combine(y, p)
+    ref = np.einsum("tj,tjc->tc", p.astype(np.float64), y.astype(np.float64))
+    assert np.all(np.abs(out - ref) <= 1e-13 * asum)
+    # a transposed slot index would not match
+    bad = np.einsum("tj,tjc->tc", p.astype(np.float64)[:, ::-1], y.astype(np.float64))
+    assert not np.allclose(out, bad)
+
+
+# ---------------------------------------------------------------------------
+# GGUF block import
+# ---------------------------------------------------------------------------
+
+def parse_gguf_golden():
+    path = os.path.join(os.path.dirname(__file__), "golden", "gguf_blocks.txt")
+    cases, cur = [], None
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, _, val = line.partition(" ") if line.startswith("block") else line.partition(":")
+        if key == "block":
+            fmt, name = val.split()
+            cur = {"fmt": fmt, "name": name}
+            cases.append(cur)
+        elif key == "bytes":
+            cur["bytes"] = np.array([int(v, 16) for v in val.split()], np.uint8)
+        elif key == "d":
+            cur["d"] = int(val.strip(), 16)
+        elif key == "codes":
+            cur["codes"] = [int(v, 0) for v in val.split()]
+        elif key == "values":
+            cur["values"] = [float(v) for v in val.split()]
+    return cases
+
+
+@pytest.mark.parametrize("case", parse_gguf_golden(), ids=lambda c: c["name"])
+def test_gguf_golden_blocks(case):
+    raw = case["bytes"]
+    if case["fmt"] == "q8_0":
+        assert raw.size == 34
+        q, d = oracle.gguf_q8_0_to_planar(raw, 1, 32)
+        assert d[0, 0] == case["d"]
+        assert q[0].tolist() == case["codes"]
+        vals = q[0].astype(np.float64) * oracle.f16_bits_to_f32(d)[0, 0]
+    else:
+        assert raw.size == 18
+        packed, d = oracle.gguf_q4_0_to_planar(raw, 1, 32)
+        assert d[0, 0] == case["d"]
+        assert packed[0].tolist() == case["codes"]
+        vals = (oracle.unpack_w4(packed)[0].astype(np.float64) - 8) * oracle.f16_bits_to_f32(d)[0, 0]
+    assert vals.tolist() == case["values"]
+
+
+def test_gguf_matches_numpy_structured_dtype_and_roundtrips():
+    g = np.random.default_rng(23)
+    rows, k = 5, 160
+    nb = k // 32
+    q8 = np.dtype([("d", "<u2"), ("qs", "i1", 32)])
+    q4 = np.dtype([("d", "<u2"), ("qs", "u1", 16)])
+    assert q8.itemsize == 34 and q4.itemsize == 18
+    a = np.zeros(rows * nb, q8)
+    a["d"] = g.integers(0, 1 << 16, rows * nb)
+    a["qs"] = g.integers(-128, 128, (rows * nb, 32))
+    q, d = oracle.gguf_q8_0_to_planar(a.view(np.uint8), rows, k)
+    assert np.array_equal(d.reshape(-1), a["d"])
+    assert np.array_equal(q.reshape(rows, nb, 32).reshape(-1, 32), a["qs"])
+    back = np.zeros(rows * nb, q8)
+    back["d"], back["qs"] = d.reshape(-1), q.reshape(-1, 32)
+    assert np.array_equal(back.view(np.uint8), a.view(np.uint8))
+    b = np.zeros(rows * nb, q4)
+    b["d"] = g.integers(0, 1 << 16, rows * nb)
+    b["qs"] = g.integers(0, 256, (rows * nb, 16))
+    packed, d4 = oracle.gguf_q4_0_to_planar(b.view(np.uint8), rows, k)
+    assert np.array_equal(d4.reshape(-1), b["d"])
+    assert np.array_equal(packed.reshape(-1, 16), b["qs"])
+    # the codes of block 1 start at byte 34 + 2: a reader that forgot the
+    # 2-byte scale (stride 32) would take bytes 32 + 2 .. 65 and misread them
+    flat = a.view(np.uint8).reshape(-1)
+    assert np.array_equal(flat[36:68].view(np.int8), q[0, 32:64])
+    assert not np.array_equal(flat[34:66].view(np.int8), q[0, 32:64])
