@@ -14,7 +14,8 @@ resident in HBM before timing starts.
 Also reported (key "also"): the prefill GEMM (M=2048, K=5120, N=17408), the
 long-prefill GEMM (M=18432, K=5120, N=5120, Student-t activations with outlier
 channels), the grouped W4A8 MoE GEMM (947 tokens, top-8 of 128 experts,
-K=2048, N=768) and the activation quantizer, each with its own roofline.
+K=2048, N=768), the activation quantizer, the MoE combine and the GGUF
+import, each with its own roofline.
 
 "roofline" describes the step's kernel (the fused quantize + GEMV): achieved =
 algorithmic bytes per launch / mean launch duration, from HIP events recorded
@@ -55,7 +56,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--only-headline", action="store_true", help="skip the secondary workloads")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--workloads", default="decode,prefill,long,moe",
+    p.add_argument("--workloads", default="decode,prefill,long,moe,combine,gguf",
                    help="comma list of workloads to run (profiling); the JSON line "
                         "is printed only when decode is among them.  'copy' (never a "
                         "default) runs a plain device copy of known size, the "
@@ -334,6 +335,56 @@ def bench_moe(bqi, torch, W, iters):
             "hbm_bytes_measured": traffic("k_grouped_w4a8 moe")}
 
 
+def bench_combine(bqi, torch, W, iters):
+    """MoE combine on the MoE workload's output shape (947 tokens x top-8 x
+    768): an HBM stream; 12 rotated copies of y (280 MB) defeat the 256 MB
+    Infinity Cache."""
+    m = W.MOE
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(6)
+    copies = 12
+    ys = [torch.randn((m.tokens, m.top_k, m.n), generator=gen, device="cuda") for _ in range(copies)]
+    p = torch.softmax(torch.randn((m.tokens, m.top_k), generator=gen, device="cuda"), dim=1)
+    out = torch.empty((m.tokens, m.n), device="cuda")
+    T = Timer(torch)
+    mean = T.loop(lambda i: bqi.moe_combine_f32(ys[i % copies], p, out), iters, check=lambda: out)
+    byt = 4 * (m.tokens * m.top_k * m.n + m.tokens * m.top_k + m.tokens * m.n)
+    gbs = byt / (mean * 1e-3) / 1e9
+    return {"workload": "MoE combine T=%d top-%d N=%d" % (m.tokens, m.top_k, m.n),
+            "kernel": "k_moe_combine", "value": round(gbs, 1), "unit": "GB/s",
+            "mean_launch_us": round(mean * 1e3, 2), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "hbm_bytes_algorithmic": byt, "y_copies_rotated": copies}
+
+
+def bench_gguf(bqi, torch, W, iters):
+    """GGUF import of the prefill weight matrix as Q8_0 (17408 x 5120) and of
+    the MoE expert weights as Q4_0 (128 x 768 x 2048): byte shuffles at HBM
+    rate; two rotated source copies each."""
+    res = []
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    for fmt, rows, k in (("q8_0", W.PREFILL.n, W.PREFILL.k),
+                         ("q4_0", W.MOE.experts * W.MOE.n, W.MOE.k)):
+        per = 34 if fmt == "q8_0" else 18
+        nbytes = rows * (k // 32) * per
+        srcs = [torch.randint(0, 256, (nbytes,), generator=gen, device="cuda", dtype=torch.uint8)
+                for _ in range(2)]
+        codes, scales = (bqi.gguf_q8_0_to_planar if fmt == "q8_0" else bqi.gguf_q4_0_to_planar)(
+            srcs[0], rows, k)
+        f = bqi.gguf_q8_0_to_planar if fmt == "q8_0" else bqi.gguf_q4_0_to_planar
+        T = Timer(torch)
+        mean = T.loop(lambda i: f(srcs[i % 2], rows, k, codes, scales), iters, check=lambda: codes)
+        byt = 2 * nbytes
+        gbs = byt / (mean * 1e-3) / 1e9
+        res.append({"workload": "GGUF %s import %dx%d" % (fmt.upper(), rows, k),
+                    "kernel": "k_gguf_split", "value": round(gbs, 1), "unit": "GB/s",
+                    "mean_launch_us": round(mean * 1e3, 2),
+                    "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "hbm_bytes_algorithmic": byt})
+        del srcs, codes, scales
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(W, step_bytes, seconds):
     """The CPU oracle (test infrastructure, plain C, all host cores) on the
     same decode step: quantize the activation row, then the full GEMV."""
@@ -395,6 +446,15 @@ def main():
         if "moe" in wl:
             also.append(bench_moe(bqi, torch, W, 50))
             log(json.dumps(also[-1]))
+            torch.cuda.empty_cache()
+        if "combine" in wl:
+            also.append(bench_combine(bqi, torch, W, 100))
+            log(json.dumps(also[-1]))
+            torch.cuda.empty_cache()
+        if "gguf" in wl:
+            for r in bench_gguf(bqi, torch, W, 20):
+                also.append(r)
+                log(json.dumps(r))
     if res is None:
         return
     if also:

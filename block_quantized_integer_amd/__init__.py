@@ -29,7 +29,8 @@ BQI_F32, BQI_F16 = 0, 1
 
 SYMBOLS = ("bqi_status_string", "bqi_abi_version", "quantize_q8_0", "qgemm_q8_0",
            "quantize_qgemm_q8_0", "route_topk", "qgemm_w4a8_grouped_workspace_size",
-           "qgemm_w4a8_grouped")
+           "qgemm_w4a8_grouped", "moe_combine_f32", "gguf_q8_0_to_planar",
+           "gguf_q4_0_to_planar")
 
 _lib = None
 
@@ -60,6 +61,12 @@ def lib() -> C.CDLL:
     L.qgemm_q8_0.argtypes = [P, P, I64, P, P, I64, I64, P, P]
     L.quantize_qgemm_q8_0.restype = I32
     L.quantize_qgemm_q8_0.argtypes = [P, I32, I64, I64, I64, P, P, I64, P, P, P, P]
+    L.moe_combine_f32.restype = I32
+    L.moe_combine_f32.argtypes = [P, P, I64, I64, I64, P, P]
+    L.gguf_q8_0_to_planar.restype = I32
+    L.gguf_q8_0_to_planar.argtypes = [P, I64, I64, P, P, P]
+    L.gguf_q4_0_to_planar.restype = I32
+    L.gguf_q4_0_to_planar.argtypes = [P, I64, I64, P, P, P]
     L.route_topk.restype = I32
     L.route_topk.argtypes = [P, I64, I64, I64, P, P, P, P]
     L.qgemm_w4a8_grouped_workspace_size.restype = C.c_size_t
@@ -236,3 +243,52 @@ def qgemm_w4a8_grouped(aq, ad, topk_ids, wq4, wd, y=None, workspace=None, stream
                                   workspace.numel(), _stream(stream))
     _raise(st, "qgemm_w4a8_grouped")
     return y
+
+
+def moe_combine_f32(y, p, out=None, stream=None):
+    """out[t][c] = sum_j p[t][j] * y[t][j][c] for y fp32 [T][top_k][N] and
+    router probabilities p fp32 [T][top_k].  Returns out fp32 [T][N]."""
+    torch = _torch()
+    _check(y, torch.float32, 3, "y")
+    _check(p, torch.float32, 2, "p")
+    T, top_k, N = y.shape
+    if tuple(p.shape) != (T, top_k):
+        raise ValueError("shape mismatch: y %s p %s" % (tuple(y.shape), tuple(p.shape)))
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=y.device)
+    _check(out, torch.float32, 2, "out")
+    st = lib().moe_combine_f32(_ptr(y), _ptr(p), T, top_k, N, _ptr(out), _stream(stream))
+    _raise(st, "moe_combine_f32")
+    return out
+
+
+def _gguf(fmt, blocks, rows, k, codes, scales, stream):
+    torch = _torch()
+    _check(blocks, torch.uint8, 1, "blocks")
+    per = 34 if fmt == "q8_0" else 18
+    if k % 32 or blocks.numel() != rows * (k // 32) * per:
+        raise ValueError("blocks must hold rows * k/32 GGUF %s blocks" % fmt)
+    if codes is None:
+        codes = torch.empty((rows, k) if fmt == "q8_0" else (rows, k // 2),
+                            dtype=torch.int8 if fmt == "q8_0" else torch.uint8,
+                            device=blocks.device)
+    if scales is None:
+        scales = torch.empty((rows, k // 32), dtype=torch.int16, device=blocks.device)
+    _check(codes, torch.int8 if fmt == "q8_0" else torch.uint8, 2, "codes")
+    _check(scales, torch.int16, 2, "scales")
+    f = lib().gguf_q8_0_to_planar if fmt == "q8_0" else lib().gguf_q4_0_to_planar
+    st = f(_ptr(blocks), rows, k, _ptr(codes), _ptr(scales), _stream(stream))
+    _raise(st, "gguf_%s_to_planar" % fmt)
+    return codes, scales
+
+
+def gguf_q8_0_to_planar(blocks, rows, k, q=None, d=None, stream=None):
+    """Split a GGUF Q8_0 block array (uint8 [rows*k/32*34]) into codes int8
+    [rows][k] and scale bits int16 [rows][k/32]."""
+    return _gguf("q8_0", blocks, rows, k, q, d, stream)
+
+
+def gguf_q4_0_to_planar(blocks, rows, k, wq4=None, wd=None, stream=None):
+    """Split a GGUF Q4_0 block array (uint8 [rows*k/32*18]) into packed codes
+    uint8 [rows][k/2] and scale bits int16 [rows][k/32]."""
+    return _gguf("q4_0", blocks, rows, k, wq4, wd, stream)

@@ -65,7 +65,7 @@ const char *bqi_status_string(int status) {
   }
 }
 
-int bqi_abi_version(void) { return 210; }
+int bqi_abi_version(void) { return 220; }
 
 int quantize_q8_0(const void *x, int x_dtype, int64_t rows, int64_t k,
                   int64_t ldx, int8_t *q, uint16_t *d, void *stream) {
@@ -210,6 +210,55 @@ int qgemm_w4a8_grouped(const int8_t *aq, const uint16_t *ad, int64_t n_tokens,
   return hip_status(bqi::launch_grouped_w4a8(aq, ad32t, rows_total, top_k, wq4,
                                              wd, n_experts, n, k, counts,
                                              offsets, rows, y, s));
+}
+
+int moe_combine_f32(const float *y, const float *p, int64_t n_tokens,
+                    int64_t top_k, int64_t n, float *out, void *stream) {
+  if (n_tokens < 0 || top_k < 0 || n < 0) return BQI_ESHAPE;
+  if (n_tokens > kI32Max || top_k > 65536 || n > kI32Max ||
+      n_tokens * top_k > kI32Max || n_tokens * top_k * n > ((int64_t)1 << 40))
+    return BQI_ESHAPE;
+  if (n_tokens == 0 || n == 0) return BQI_OK;
+  if (!out) return BQI_EINVAL;
+  if (!aligned(out, 4)) return BQI_EALIGN;
+  if (top_k == 0)  // empty sum
+    return hip_status(bqi::launch_zero_f32(out, n_tokens * n, as_stream(stream)));
+  if (!y || !p) return BQI_EINVAL;
+  if (!aligned(y, 4) || !aligned(p, 4)) return BQI_EALIGN;
+  return hip_status(bqi::launch_moe_combine(y, p, n_tokens, top_k, n, out,
+                                            as_stream(stream)));
+}
+
+namespace {
+
+int gguf_check(const void *blocks, int64_t rows, int64_t k, const void *codes,
+               const void *scales) {
+  if (rows < 0 || k < 0 || k % kQK != 0) return BQI_ESHAPE;
+  if (rows > kI32Max || k > kI32Max || rows * (k / kQK) > ((int64_t)1 << 36))
+    return BQI_ESHAPE;
+  if (rows == 0 || k == 0) return BQI_OK;
+  if (!blocks || !codes || !scales) return BQI_EINVAL;
+  if (!aligned(blocks, 16) || !aligned(codes, 16) || !aligned(scales, 2))
+    return BQI_EALIGN;
+  return 1;  // valid and non-empty
+}
+
+}  // namespace
+
+int gguf_q8_0_to_planar(const void *blocks, int64_t rows, int64_t k, int8_t *q,
+                        uint16_t *d, void *stream) {
+  const int st = gguf_check(blocks, rows, k, q, d);
+  if (st != 1) return st;
+  return hip_status(bqi::launch_gguf_q8_0(blocks, rows * (k / kQK), q, d,
+                                          as_stream(stream)));
+}
+
+int gguf_q4_0_to_planar(const void *blocks, int64_t rows, int64_t k,
+                        uint8_t *wq4, uint16_t *wd, void *stream) {
+  const int st = gguf_check(blocks, rows, k, wq4, wd);
+  if (st != 1) return st;
+  return hip_status(bqi::launch_gguf_q4_0(blocks, rows * (k / kQK), wq4, wd,
+                                          as_stream(stream)));
 }
 
 }  // extern "C"

@@ -58,4 +58,15 @@ hipError_t launch_grouped_w4a8(const int8_t *aq, const float *ad32t,
                                const int32_t *rows, float *y,
                                hipStream_t stream);
 
+// MoE combine: out[t][c] = sum_j p[t][j] * y[t][j][c]
+hipError_t launch_moe_combine(const float *y, const float *p, int64_t T,
+                              int64_t top_k, int64_t n, float *out,
+                              hipStream_t stream);
+
+// GGUF block arrays -> planar codes + scales (n_blocks = rows * k / 32)
+hipError_t launch_gguf_q8_0(const void *src, int64_t n_blocks, int8_t *q,
+                            uint16_t *d, hipStream_t stream);
+hipError_t launch_gguf_q4_0(const void *src, int64_t n_blocks, uint8_t *wq4,
+                            uint16_t *wd, hipStream_t stream);
+
 }  // namespace bqi

@@ -68,9 +68,9 @@ extern "C" {
 /* Human-readable name of a status code (static string, never NULL). */
 BQI_API const char *bqi_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor): 210.  Version 200 added
+/* ABI version of this header (major * 100 + minor): 220.  Version 200 added
  * the k argument of qgemm_w4a8_grouped_workspace_size; 210 added
- * quantize_qgemm_q8_0. */
+ * quantize_qgemm_q8_0; 220 added moe_combine_f32 and the GGUF import. */
 BQI_API int bqi_abi_version(void);
 
 /*
@@ -196,6 +196,47 @@ BQI_API int qgemm_w4a8_grouped(const int8_t *aq, const uint16_t *ad, int64_t n_t
                        const uint8_t *wq4, const uint16_t *wd,
                        int64_t n_experts, int64_t n, int64_t k, float *y,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * moe_combine_f32 -- the MoE combine after the grouped GEMM: each token's
+ * top-k expert outputs weighted by its router probabilities and summed back
+ * in token order (page 3: the grouped 4-bit GEMM serves the MoE routing,
+ * Method 1; the experts are router-weighted, Method 2).
+ *
+ *   y   [n_tokens][top_k][n] fp32  -- e.g. the output of qgemm_w4a8_grouped
+ *   p   [n_tokens][top_k] fp32     -- router probabilities of the slots
+ *   out [n_tokens][n] fp32 (output) = sum_{j < top_k} p[t][j] * y[t][j][c]
+ *
+ * Slots are accumulated in order with one fma each (one rounding per
+ * product-and-add): |out - exact| <= top_k * 2^-24 * sum_j |p y|;
+ * deterministic.  top_k == 0 writes zeros.  Requirements: y, p, out 4-byte
+ * aligned (16-byte alignment and n % 4 == 0 select wider loads).
+ */
+BQI_API int moe_combine_f32(const float *y, const float *p, int64_t n_tokens,
+                    int64_t top_k, int64_t n, float *out, void *stream);
+
+/*
+ * gguf_q8_0_to_planar, gguf_q4_0_to_planar -- split a GGUF block array into
+ * this library's planar layout, so that weights stored as GGUF (the format of
+ * page 1's "Honest benchmark" comparison) can be consumed.
+ *
+ *   blocks: rows * k/32 contiguous blocks, row-major; each block is a
+ *           little-endian fp16 scale followed by its codes:
+ *           Q8_0: 32 int8 codes (34 bytes);
+ *           Q4_0: 16 bytes, byte j = element j (low nibble) | element j+16
+ *                 (high nibble), value (nibble - 8) * scale (18 bytes).
+ *   q / wq4 (output): codes [rows][k] int8 (Q8_0) or packed [rows][k/2]
+ *           uint8 (Q4_0, same nibble order: the wq4 layout of
+ *           qgemm_w4a8_grouped);
+ *   d / wd  (output): scale bits [rows][k/32].
+ *
+ * A byte shuffle; the output is exactly the blocks' fields.  Requirements:
+ * k % 32 == 0; blocks and codes 16-byte aligned; scales 2-byte aligned.
+ */
+BQI_API int gguf_q8_0_to_planar(const void *blocks, int64_t rows, int64_t k,
+                        int8_t *q, uint16_t *d, void *stream);
+BQI_API int gguf_q4_0_to_planar(const void *blocks, int64_t rows, int64_t k,
+                        uint8_t *wq4, uint16_t *wd, void *stream);
 
 #ifdef __cplusplus
 }

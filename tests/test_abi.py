@@ -43,7 +43,7 @@ def test_library_exports_exactly_the_header_symbols():
 
 def test_status_strings():
     L = bqi.lib()
-    assert L.bqi_abi_version() == 210
+    assert L.bqi_abi_version() == 220
     for st in (OK, EINVAL, ESHAPE, EALIGN, bqi.BQI_EHIP):
         assert L.bqi_status_string(st).decode().startswith("BQI_")
     assert L.bqi_status_string(12345)
@@ -113,6 +113,38 @@ def test_fused_quantize_qgemm_validation():
     assert fq(y=FAKE + 2) == EALIGN
     assert fq(m=0) == OK
     assert fq(m=1 << 31) == ESHAPE
+
+
+def test_moe_combine_validation():
+    L = bqi.lib()
+    c = lambda y=FAKE, p=FAKE, T=4, tk=8, n=16, out=FAKE: L.moe_combine_f32(
+        P(y), P(p), T, tk, n, P(out), P(0))
+    assert c(T=-1) == ESHAPE
+    assert c(tk=-1) == ESHAPE
+    assert c(n=-1) == ESHAPE
+    assert c(out=0) == EINVAL
+    assert c(y=0) == EINVAL
+    assert c(p=0) == EINVAL
+    assert c(y=FAKE + 2) == EALIGN
+    assert c(out=FAKE + 1) == EALIGN
+    assert c(T=0) == OK
+    assert c(n=0) == OK
+
+
+def test_gguf_validation():
+    L = bqi.lib()
+    for f in (L.gguf_q8_0_to_planar, L.gguf_q4_0_to_planar):
+        g = lambda b=FAKE, rows=4, k=64, c=FAKE, d=FAKE: f(P(b), rows, k, P(c), P(d), P(0))
+        assert g(k=48) == ESHAPE
+        assert g(rows=-1) == ESHAPE
+        assert g(b=0) == EINVAL
+        assert g(c=0) == EINVAL
+        assert g(d=0) == EINVAL
+        assert g(b=FAKE + 2) == EALIGN
+        assert g(c=FAKE + 8) == EALIGN
+        assert g(d=FAKE + 1) == EALIGN
+        assert g(rows=0) == OK
+        assert g(k=0) == OK
 
 
 def test_route_validation():

@@ -409,3 +409,78 @@ def test_grouped_w4a8_moe_workload_full(weights):
     y2 = host(bqi.qgemm_w4a8_grouped(qa_g, da_g, dev_tensor(ids), dev_tensor(packed),
                                      dev_tensor(wsc)))
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# MoE combine
+# ---------------------------------------------------------------------------
+
+def combine_bound_ok(out, ref, asum, top_k, what):
+    err = np.abs(np.asarray(out, np.float64) - ref)
+    bound = top_k * 2.0 ** -24 * (1.0 + 1e-3) * asum
+    bad = err > bound
+    assert not bad.any(), "%s: %d outputs outside top_k * 2^-24 * sum|p y|" % (what, int(bad.sum()))
+
+
+@pytest.mark.parametrize("T,top_k,n", [(947, 8, 768), (5, 3, 130), (1, 1, 1), (64, 8, 7), (3, 0, 16)])
+def test_moe_combine(T, top_k, n):
+    g = np.random.default_rng(T * 7 + n)
+    y = g.standard_normal((T, top_k, n)).astype(np.float32)
+    logits = g.standard_normal((T, top_k))
+    p = np.exp(logits - logits.max(axis=1, keepdims=True)) if top_k else logits
+    p = (p / p.sum(axis=1, keepdims=True)).astype(np.float32) if top_k else p.astype(np.float32)
+    out = host(bqi.moe_combine_f32(dev_tensor(y), dev_tensor(p)))
+    if top_k == 0:
+        assert np.all(out == 0)
+        return
+    ref, asum = oracle.moe_combine(y, p)
+    combine_bound_ok(out, ref, asum, top_k, "combine T=%d k=%d n=%d" % (T, top_k, n))
+
+
+def test_moe_combine_after_grouped_gemm():
+    """The grouped GEMM's output, combined, against the oracle chain."""
+    T, top_k, E, K, N = 37, 4, 8, 128, 96
+    ids = W.topk_ids(T, top_k, E, seed=5)
+    packed, wsc = W.random_w4_codes(E, N, K, seed=5)
+    qa, da = oracle.quantize_q8_0(W.activations("moe", T, K, seed=5))
+    y = bqi.qgemm_w4a8_grouped(dev_tensor(qa), dev_tensor(da), dev_tensor(ids), dev_tensor(packed),
+                               dev_tensor(wsc))
+    g = np.random.default_rng(5)
+    p = g.random((T, top_k)).astype(np.float32)
+    out = host(bqi.moe_combine_f32(y, dev_tensor(p)))
+    ref, asum = oracle.moe_combine(host(y), p)
+    combine_bound_ok(out, ref, asum, top_k, "combine after grouped")
+
+
+# ---------------------------------------------------------------------------
+# GGUF import
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt,rows,k", [("q8_0", 1, 32), ("q8_0", 37, 4096), ("q8_0", 300, 96),
+                                        ("q4_0", 1, 32), ("q4_0", 768, 2048), ("q4_0", 33, 160)])
+def test_gguf_import_bitexact(fmt, rows, k):
+    g = np.random.default_rng(rows + k)
+    per = 34 if fmt == "q8_0" else 18
+    blocks = g.integers(0, 256, rows * (k // 32) * per, dtype=np.uint8)
+    if fmt == "q8_0":
+        q, d = bqi.gguf_q8_0_to_planar(dev_tensor(blocks), rows, k)
+        qr, dr = oracle.gguf_q8_0_to_planar(blocks, rows, k)
+    else:
+        q, d = bqi.gguf_q4_0_to_planar(dev_tensor(blocks), rows, k)
+        qr, dr = oracle.gguf_q4_0_to_planar(blocks, rows, k)
+    assert np.array_equal(host(q), qr) and np.array_equal(host(d), dr)
+
+
+def test_gguf_import_feeds_the_gemm():
+    """GGUF Q8_0 weights, split on the GPU, give the same GEMM as the planar
+    weights they were written from."""
+    g = np.random.default_rng(31)
+    n, k, m = 96, 256, 20
+    qw, dw = oracle.quantize_q8_0(W.weights("small", n, k, seed=3))
+    rec = np.zeros(n * (k // 32), np.dtype([("d", "<u2"), ("qs", "i1", 32)]))
+    rec["d"], rec["qs"] = dw.reshape(-1), qw.reshape(-1, 32)
+    q, d = bqi.gguf_q8_0_to_planar(dev_tensor(rec.view(np.uint8)), n, k)
+    qa, da = oracle.quantize_q8_0(g.standard_normal((m, k)).astype(np.float32))
+    y = bqi.qgemm_q8_0(dev_tensor(qa), dev_tensor(da), q, d)
+    y2 = bqi.qgemm_q8_0(dev_tensor(qa), dev_tensor(da), dev_tensor(qw), dev_tensor(dw))
+    assert torch.equal(y, y2)
