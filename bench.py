@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--only-headline", action="store_true", help="skip the secondary workloads")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--workloads", default="decode,prefill,long,moe,combine,gguf",
+    p.add_argument("--workloads", default="decode,prefill,long,moe,moe_decode,combine,gguf",
                    help="comma list of workloads to run (profiling); the JSON line "
                         "is printed only when decode is among them.  'copy' (never a "
                         "default) runs a plain device copy of known size, the "
@@ -335,6 +335,46 @@ def bench_moe(bqi, torch, W, iters):
             "hbm_bytes_measured": traffic("k_grouped_w4a8 moe")}
 
 
+def bench_moe_decode(bqi, torch, W, iters):
+    """Grouped W4A8 decode on the MoE expert shapes: T in {1, 4, 16} tokens,
+    top-8 of 128 experts, K=2048, N=768 (the v_dot4 GEMV path).  Bytes count
+    the weights of the experts that receive rows, read once; 3 rotated weight
+    copies (340 MB) defeat the Infinity Cache."""
+    m = W.MOE
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(8)
+    copies = 3
+    wq, wd = [], []
+    for _ in range(copies):
+        wq.append(torch.randint(0, 256, (m.experts, m.n, m.k // 2), generator=gen,
+                                device="cuda", dtype=torch.uint8))
+        e = torch.randint(-12, -5, (m.experts, m.n, m.k // 32), generator=gen, device="cuda")
+        mant = torch.rand((m.experts, m.n, m.k // 32), generator=gen, device="cuda") + 1.0
+        wd.append(torch.ldexp(mant, e.float()).half().view(torch.int16))
+    res = []
+    for T in (1, 4, 16):
+        _, aq, ad = device_q8(bqi, torch, T, m.k, 1.0, gen)
+        ids_np = W.topk_ids(T, m.top_k, m.experts, seed=T)
+        ids = torch.from_numpy(ids_np).cuda()
+        y = torch.empty((T, m.top_k, m.n), dtype=torch.float32, device="cuda")
+        ws = torch.empty(bqi.workspace_size(T, m.top_k, m.experts, m.k), dtype=torch.uint8,
+                         device="cuda")
+        fn = lambda i: bqi.qgemm_w4a8_grouped(aq, ad, ids, wq[i % copies], wd[i % copies], y, ws)
+        mean = Timer(torch).loop(fn, iters, check=lambda: y)
+        active = len(np.unique(ids_np))
+        R = T * m.top_k
+        byt = (active * m.n * (m.k // 2 + m.k // 32 * 2) + T * (m.k + m.k // 32 * 2)
+               + R * 4 + R * m.n * 4)
+        gbs = byt / (mean * 1e-3) / 1e9
+        res.append({"workload": "grouped W4A8 decode T=%d top-%d E=%d K=%d N=%d (%d active experts)"
+                                % (T, m.top_k, m.experts, m.k, m.n, active),
+                    "kernel": "k_grouped_gemv (no routing pass)", "value": round(gbs, 1), "unit": "GB/s",
+                    "mean_call_us": round(mean * 1e3, 2),
+                    "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                    "hbm_bytes_algorithmic": byt, "weight_copies_rotated": copies})
+    return res
+
+
 def bench_combine(bqi, torch, W, iters):
     """MoE combine on the MoE workload's output shape (947 tokens x top-8 x
     768): an HBM stream; 12 rotated copies of y (280 MB) defeat the 256 MB
@@ -446,6 +486,11 @@ def main():
         if "moe" in wl:
             also.append(bench_moe(bqi, torch, W, 50))
             log(json.dumps(also[-1]))
+            torch.cuda.empty_cache()
+        if "moe_decode" in wl:
+            for r in bench_moe_decode(bqi, torch, W, 100):
+                also.append(r)
+                log(json.dumps(r))
             torch.cuda.empty_cache()
         if "combine" in wl:
             also.append(bench_combine(bqi, torch, W, 100))

@@ -203,6 +203,11 @@ int qgemm_w4a8_grouped(const int8_t *aq, const uint16_t *ad, int64_t n_tokens,
   int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
   int32_t *rows = reinterpret_cast<int32_t *>(ws + L.rows);
   float *ad32t = reinterpret_cast<float *>(ws + L.ad32t);
+  // a few routed rows (decode): the v_dot4 GEMV per routed row, which needs
+  // no routing pass; otherwise route, then the int8-MFMA kernel
+  if (bqi::grouped_gemv_supported(rows_total, k))
+    return hip_status(bqi::launch_grouped_gemv(aq, ad, topk_ids, rows_total, top_k,
+                                               wq4, wd, n_experts, n, k, y, s));
   hipError_t e = bqi::launch_route_topk(topk_ids, rows_total, n_experts, top_k,
                                         counts, offsets, rows, ad, k, ad32t, y,
                                         n, s);

@@ -58,6 +58,15 @@ hipError_t launch_grouped_w4a8(const int8_t *aq, const float *ad32t,
                                const int32_t *rows, float *y,
                                hipStream_t stream);
 
+// grouped W4A8 for a few routed rows (decode): v_dot4 GEMV per routed row,
+// no routing pass
+bool grouped_gemv_supported(int64_t rows_total, int64_t k);
+hipError_t launch_grouped_gemv(const int8_t *aq, const uint16_t *ad,
+                               const int32_t *ids, int64_t rows_total,
+                               int64_t top_k, const uint8_t *wq4,
+                               const uint16_t *wd, int64_t n_experts, int64_t n,
+                               int64_t k, float *y, hipStream_t stream);
+
 // MoE combine: out[t][c] = sum_j p[t][j] * y[t][j][c]
 hipError_t launch_moe_combine(const float *y, const float *p, int64_t T,
                               int64_t top_k, int64_t n, float *out,

@@ -510,4 +510,132 @@ hipError_t launch_grouped_w4a8(const int8_t *aq, const float *ad32t,
   return hipGetLastError();
 }
 
+
+// ------------------------------------------------------- grouped decode GEMV --
+// The decode case of the grouped W4A8 GEMM (a few tokens): the pages run it on
+// the host CPU ("A 35B Hybrid-Attention Mixture-of-Experts Model on a 6GB
+// 2011 GPU", Method 1: CPU decode from RAM with 4-bit weights); here it stays
+// on the GPU, shaped like the thin-M Q8_0 GEMV: HBM-bound, v_dot4 instead of
+// MFMA, and no routing pass.
+//
+// One workgroup of 4 waves per (routed row, 32-column tile): it reads its
+// expert id, and every lane issues all of its loads at once: for lane l, group
+// l (then l + 64, ...) of each of the wave's 8 weight columns (16 packed bytes
+// = the group's 32 codes; one coalesced 1 KB wave load per column and 64
+// groups), its fp16 scale, and the same group of the token's Q8_0 activation
+// row (32 bytes + scale, from L2).  The lane unpacks the codes to int8 (c - 8),
+// forms the exact int32 block dot (8 v_dot4) and accumulates P * (da * dw)
+// with one fma (the fp16 x fp16 product is exact in fp32); each column is then
+// reduced over the wave in a fixed order.  Rows with an invalid expert id are
+// written as zeros.  An expert chosen by several tokens is read once per row,
+// mostly from cache.
+namespace {
+
+constexpr int GV_CPW = 8;     // weight columns per wave
+constexpr int GV_WAVES = 4;
+constexpr int GV_COLS = GV_CPW * GV_WAVES;  // columns per workgroup
+
+// (c + 0x78) ^ 0x80 maps each nibble code c (0..15, in a byte) to the int8
+// value c - 8 with no carry between bytes.
+__device__ __forceinline__ int32_t w4_lo(uint32_t p) {
+  return (int32_t)(((p & 0x0f0f0f0fu) + 0x78787878u) ^ 0x80808080u);
+}
+__device__ __forceinline__ int32_t w4_hi(uint32_t p) {
+  return (int32_t)((((p >> 4) & 0x0f0f0f0fu) + 0x78787878u) ^ 0x80808080u);
+}
+
+// Sum over the 64 lanes in a fixed order (DPP inside rows of 16, then two
+// cross-row shuffles); valid in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, v), 0xb1, 0xf, 0xf, false));
+  v += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, v), 0x4e, 0xf, 0xf, false));
+  v += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, v), 0x141, 0xf, 0xf, false));
+  v += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, v), 0x140, 0xf, 0xf, false));
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__global__ __launch_bounds__(64 * GV_WAVES) void k_grouped_gemv(
+    const int8_t *__restrict__ aq, const uint16_t *__restrict__ ad,
+    const int32_t *__restrict__ ids, int top_k, const uint8_t *__restrict__ wq4,
+    const uint16_t *__restrict__ wd, int n_experts, int n, int k,
+    float *__restrict__ y) {
+  const int tiles = (n + GV_COLS - 1) / GV_COLS;
+  const int r = blockIdx.x / tiles;           // routed row t * top_k + j
+  const int tn = blockIdx.x - r * tiles;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c0 = tn * GV_COLS + wave * GV_CPW;
+  const int e = ids[r];
+  if (e < 0 || e >= n_experts) {
+    if (lane < GV_CPW && c0 + lane < n) y[(int64_t)r * n + c0 + lane] = 0.0f;
+    return;
+  }
+  const int t = r / top_k;
+  const int nbk = k / QK;
+  const int64_t wrow0 = (int64_t)e * n;
+  float acc[GV_CPW];
+#pragma unroll
+  for (int q = 0; q < GV_CPW; ++q) acc[q] = 0.0f;
+
+  for (int g0 = 0; g0 < nbk; g0 += 64) {
+    const int b = g0 + lane;
+    const bool ok = b < nbk;
+    const int bb = ok ? b : 0;  // lanes past k re-read group 0 and add zero
+    // every load first: the weight groups (HBM), then the activation group
+    // and the scales
+    i32x4 w[GV_CPW];
+    uint16_t dwh[GV_CPW];
+#pragma unroll
+    for (int q = 0; q < GV_CPW; ++q) {
+      const int64_t col = wrow0 + min(c0 + q, n - 1);
+      w[q] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(wq4 + col * (k / 2) + 16 * bb));
+      dwh[q] = wd[col * nbk + bb];
+    }
+    const i32x4 a0 = *reinterpret_cast<const i32x4 *>(aq + (int64_t)t * k + 32 * bb);
+    const i32x4 a1 = *reinterpret_cast<const i32x4 *>(aq + (int64_t)t * k + 32 * bb + 16);
+    const float da = ok ? half_bits_to_float(ad[(int64_t)t * nbk + bb]) : 0.0f;
+#pragma unroll
+    for (int q = 0; q < GV_CPW; ++q) {
+      // elements 0..15 of the group pair with the low nibbles, 16..31 with the
+      // high nibbles
+      int32_t p = 0;
+      p = dot4_i8(a0.x, w4_lo((uint32_t)w[q].x), p);
+      p = dot4_i8(a0.y, w4_lo((uint32_t)w[q].y), p);
+      p = dot4_i8(a0.z, w4_lo((uint32_t)w[q].z), p);
+      p = dot4_i8(a0.w, w4_lo((uint32_t)w[q].w), p);
+      p = dot4_i8(a1.x, w4_hi((uint32_t)w[q].x), p);
+      p = dot4_i8(a1.y, w4_hi((uint32_t)w[q].y), p);
+      p = dot4_i8(a1.z, w4_hi((uint32_t)w[q].z), p);
+      p = dot4_i8(a1.w, w4_hi((uint32_t)w[q].w), p);
+      acc[q] = fmaf((float)p, da * half_bits_to_float(dwh[q]), acc[q]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < GV_CPW; ++q) {
+    const float v = wave_sum(acc[q]);
+    if (lane == q && c0 + q < n) y[(int64_t)r * n + c0 + q] = v;
+  }
+}
+
+}  // namespace
+
+bool grouped_gemv_supported(int64_t rows_total, int64_t k) {
+  // a few routed rows (decode)
+  (void)k;
+  return rows_total <= 128;
+}
+
+hipError_t launch_grouped_gemv(const int8_t *aq, const uint16_t *ad,
+                               const int32_t *ids, int64_t rows_total,
+                               int64_t top_k, const uint8_t *wq4,
+                               const uint16_t *wd, int64_t n_experts, int64_t n,
+                               int64_t k, float *y, hipStream_t stream) {
+  const int64_t tiles = (n + GV_COLS - 1) / GV_COLS;
+  hipLaunchKernelGGL(k_grouped_gemv, dim3((unsigned)(rows_total * tiles)), dim3(64 * GV_WAVES),
+                     0, stream, aq, ad, ids, (int)top_k, wq4, wd, (int)n_experts, (int)n,
+                     (int)k, y);
+  return hipGetLastError();
+}
+
 }  // namespace bqi

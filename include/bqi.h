@@ -182,6 +182,11 @@ BQI_API size_t qgemm_w4a8_grouped_workspace_size(int64_t n_tokens, int64_t top_k
  *              qgemm_w4a8_grouped_workspace_size(...) bytes, 256-byte aligned;
  *              its contents on entry do not matter and are overwritten.
  *
+ * Up to 128 routed rows (n_tokens * top_k, the decode case) run a v_dot4
+ * GEMV per routed row with no routing pass (the workspace is then unused);
+ * larger problems route, then run the int8-MFMA kernel.  Both compute the
+ * same function within the same bound.
+ *
  * For routed row r = t*top_k + j with e = topk_ids[t][j]:
  *   y[t][j][c] = sum_b wd[e][c][b] * ad[t][b] * sum_{u<32} (code[e][c][32b+u] - 8) * aq[t][32b+u]
  * with the same per-term rounding and accumulation bound as qgemm_q8_0.

@@ -484,3 +484,56 @@ def test_gguf_import_feeds_the_gemm():
     y = bqi.qgemm_q8_0(dev_tensor(qa), dev_tensor(da), q, d)
     y2 = bqi.qgemm_q8_0(dev_tensor(qa), dev_tensor(da), dev_tensor(qw), dev_tensor(dw))
     assert torch.equal(y, y2)
+
+
+# ---------------------------------------------------------------------------
+# grouped W4A8 decode (few routed rows: the v_dot4 GEMV path)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+@pytest.mark.parametrize("weights", ["quantized_normal", "uniform_codes"])
+def test_grouped_decode_workload(T, weights):
+    """Decode on the MoE expert shapes: T tokens, top-8 of 128 experts,
+    K=2048, N=768 (T * 8 <= 128 routed rows takes the GEMV path)."""
+    m = W.MOE
+    log("grouped decode T=%d %s" % (T, weights))
+    qa, da = oracle.quantize_q8_0(W.activations("moe", T, m.k, seed=40 + T))
+    ids = W.topk_ids(T, m.top_k, m.experts, seed=40 + T)
+    if weights == "quantized_normal":
+        w = W.weights("moe", m.n, m.k, experts=m.experts, seed=1)
+        packed, wsc = oracle.quantize_w4(w.reshape(-1, m.k))
+        packed = packed.reshape(m.experts, m.n, m.k // 2)
+        wsc = wsc.reshape(m.experts, m.n, m.k // 32)
+    else:
+        packed, wsc = W.random_w4_codes(m.experts, m.n, m.k, seed=1)
+    y = run_grouped(qa, da, ids, packed, wsc)
+    yr, asum = oracle.qgemm_w4a8_grouped(qa, da, ids, packed, wsc, nthreads=oracle_threads())
+    assert_within_bound(y, yr, asum, m.k // 32, "decode T=%d" % T)
+
+
+@pytest.mark.parametrize("case", ["crowded", "invalid_and_dups", "ragged", "k_large"])
+def test_grouped_decode_cases(case):
+    g = np.random.default_rng(hash(case) % 1000)
+    if case == "crowded":          # 16 tokens on the same 8 experts: 16 rows each
+        T, tk, E, K, N = 16, 8, 64, 256, 96
+        ids = np.tile(np.arange(8, dtype=np.int32), (T, 1))
+    elif case == "invalid_and_dups":
+        T, tk, E, K, N = 6, 8, 16, 128, 40
+        ids = g.integers(0, E, (T, tk)).astype(np.int32)
+        ids[0, 3], ids[2, 0], ids[5, 7] = -1, E, 10 ** 6
+        ids[4, 1] = ids[4, 2]
+    elif case == "ragged":         # K shorter than 64 groups, N not a multiple of 16
+        T, tk, E, K, N = 3, 4, 9, 96, 130
+        ids = g.integers(0, E, (T, tk)).astype(np.int32)
+    else:                          # K past the GEMV stage limit: the MFMA path on few rows
+        T, tk, E, K, N = 2, 8, 32, 4096, 64
+        ids = W.topk_ids(T, tk, E, seed=9)
+    qa = W.random_int8("moe", 710, (T, K), seed=K)
+    da = W.random_scales("moe", 711, (T, K // 32), seed=K)
+    packed = g.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    wsc = W.random_scales("moe", 712, (E, N, K // 32), seed=K)
+    y = run_grouped(qa, da, ids, packed, wsc)
+    yr, asum = oracle.qgemm_w4a8_grouped(qa, da, ids, packed, wsc, nthreads=oracle_threads())
+    assert_within_bound(y, yr, asum, K // 32, case)
+    bad = (ids < 0) | (ids >= E)
+    assert np.all(y.reshape(T, tk, N)[bad] == 0)
