@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--only-headline", action="store_true", help="skip the secondary workloads")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--workloads", default="decode,prefill,long,moe,moe_decode,combine,gguf",
+    p.add_argument("--workloads", default="decode,prefill,long,moe,moe_decode,combine,gguf,host",
                    help="comma list of workloads to run (profiling); the JSON line "
                         "is printed only when decode is among them.  'copy' (never a "
                         "default) runs a plain device copy of known size, the "
@@ -375,6 +375,48 @@ def bench_moe_decode(bqi, torch, W, iters):
     return res
 
 
+def bench_host_w4a8(bqi, W):
+    """The host-CPU integer-SIMD W4A8 path (AVX2 vpmaddubsw) on the grouped
+    decode workload (T tokens, top-8 of 128 experts, K=2048, N=768, weights in
+    host RAM), against the plain CPU oracle on the same cores.  Synchronous
+    host work: no GPU involved."""
+    import oracle
+    m = W.MOE
+    g = np.random.default_rng(9)
+    wq4 = g.integers(0, 256, (m.experts, m.n, m.k // 2), dtype=np.uint8)
+    wd = W.random_scales("moe", 730, (m.experts, m.n, m.k // 32))
+    threads = oracle.default_threads()
+    res = []
+    for T in (1, 4, 16):
+        qa = W.random_int8("moe", 731, (T, m.k), seed=T)
+        da = W.random_scales("moe", 732, (T, m.k // 32), seed=T)
+        ids = W.topk_ids(T, m.top_k, m.experts, seed=T)
+        active = len(np.unique(ids))
+        wbytes = active * m.n * (m.k // 2 + m.k // 32 * 2)
+
+        def timed(fn, min_s=0.5):
+            fn()
+            n, t0 = 0, time.perf_counter()
+            while True:
+                fn()
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= min_s:
+                    return el / n
+        t_simd = timed(lambda: bqi.qgemm_w4a8_grouped_host(qa, da, ids, wq4, wd, threads))
+        t_orc = timed(lambda: oracle.qgemm_w4a8_grouped(qa, da, ids, wq4, wd, nthreads=threads))
+        res.append({"workload": "host W4A8 decode T=%d top-%d E=%d K=%d N=%d (%d active experts)"
+                                % (T, m.top_k, m.experts, m.k, m.n, active),
+                    "kernel": "qgemm_w4a8_grouped_host (AVX2 vpmaddubsw)",
+                    "value": round(T / t_simd, 1), "unit": "tokens/s",
+                    "ms_per_call": round(t_simd * 1e3, 3),
+                    "weight_GB/s": round(wbytes / t_simd / 1e9, 2),
+                    "cores": threads,
+                    "oracle_ms_per_call": round(t_orc * 1e3, 3),
+                    "speedup_vs_oracle": round(t_orc / t_simd, 2)})
+    return res
+
+
 def bench_combine(bqi, torch, W, iters):
     """MoE combine on the MoE workload's output shape (947 tokens x top-8 x
     768): an HBM stream; 12 rotated copies of y (280 MB) defeat the 256 MB
@@ -498,6 +540,10 @@ def main():
             torch.cuda.empty_cache()
         if "gguf" in wl:
             for r in bench_gguf(bqi, torch, W, 20):
+                also.append(r)
+                log(json.dumps(r))
+        if "host" in wl:
+            for r in bench_host_w4a8(bqi, W):
                 also.append(r)
                 log(json.dumps(r))
     if res is None:

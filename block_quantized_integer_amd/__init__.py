@@ -24,13 +24,13 @@ import os
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libbqi.so")
 
-BQI_OK, BQI_EINVAL, BQI_ESHAPE, BQI_EALIGN, BQI_EHIP = 0, -1, -2, -3, -4
+BQI_OK, BQI_EINVAL, BQI_ESHAPE, BQI_EALIGN, BQI_EHIP, BQI_ENOTSUP = 0, -1, -2, -3, -4, -5
 BQI_F32, BQI_F16 = 0, 1
 
 SYMBOLS = ("bqi_status_string", "bqi_abi_version", "quantize_q8_0", "qgemm_q8_0",
            "quantize_qgemm_q8_0", "route_topk", "qgemm_w4a8_grouped_workspace_size",
            "qgemm_w4a8_grouped", "moe_combine_f32", "gguf_q8_0_to_planar",
-           "gguf_q4_0_to_planar")
+           "gguf_q4_0_to_planar", "qgemm_w4a8_grouped_host")
 
 _lib = None
 
@@ -67,6 +67,8 @@ def lib() -> C.CDLL:
     L.gguf_q8_0_to_planar.argtypes = [P, I64, I64, P, P, P]
     L.gguf_q4_0_to_planar.restype = I32
     L.gguf_q4_0_to_planar.argtypes = [P, I64, I64, P, P, P]
+    L.qgemm_w4a8_grouped_host.restype = I32
+    L.qgemm_w4a8_grouped_host.argtypes = [P, P, I64, P, I64, P, P, I64, I64, I64, P, I32]
     L.route_topk.restype = I32
     L.route_topk.argtypes = [P, I64, I64, I64, P, P, P, P]
     L.qgemm_w4a8_grouped_workspace_size.restype = C.c_size_t
@@ -292,3 +294,27 @@ def gguf_q4_0_to_planar(blocks, rows, k, wq4=None, wd=None, stream=None):
     """Split a GGUF Q4_0 block array (uint8 [rows*k/32*18]) into packed codes
     uint8 [rows][k/2] and scale bits int16 [rows][k/32]."""
     return _gguf("q4_0", blocks, rows, k, wq4, wd, stream)
+
+
+def qgemm_w4a8_grouped_host(aq, ad, topk_ids, wq4, wd, nthreads=0):
+    """The grouped W4A8 GEMM on the host CPU (AVX2 integer SIMD) for numpy
+    arrays: aq int8 [T][K], ad uint16 [T][K/32], topk_ids int32 [T][top_k],
+    wq4 uint8 [E][N][K/2], wd uint16 [E][N][K/32].  Returns y float32
+    [T][top_k][N].  Synchronous; no GPU involved."""
+    import numpy as np
+    aq = np.ascontiguousarray(aq, np.int8)
+    ad = np.ascontiguousarray(ad).view(np.uint16)
+    ids = np.ascontiguousarray(topk_ids, np.int32)
+    wq4 = np.ascontiguousarray(wq4, np.uint8)
+    wd = np.ascontiguousarray(wd).view(np.uint16)
+    T, K = aq.shape
+    top_k = ids.shape[1]
+    E, N, KH = wq4.shape
+    if KH * 2 != K or ad.shape != (T, K // 32) or ids.shape[0] != T or wd.shape != (E, N, K // 32):
+        raise ValueError("shape mismatch")
+    y = np.empty((T, top_k, N), np.float32)
+    p = lambda a: a.ctypes.data_as(C.c_void_p)
+    st = lib().qgemm_w4a8_grouped_host(p(aq), p(ad), T, p(ids), top_k, p(wq4), p(wd), E, N, K,
+                                       p(y), int(nthreads))
+    _raise(st, "qgemm_w4a8_grouped_host")
+    return y

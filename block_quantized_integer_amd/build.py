@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbqi.so")
 SOURCES = ["api.hip", "quantize.hip", "gemv_thin.hip", "gemm_mfma.hip", "grouped_w4a8.hip",
-           "moe_combine.hip", "gguf_import.hip"]
+           "moe_combine.hip", "gguf_import.hip", "host_w4a8.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -61,11 +61,12 @@ const char *bqi_status_string(int status) {
     case BQI_ESHAPE: return "BQI_ESHAPE: bad size (negative, k not a multiple of 32, ldx < k, too large)";
     case BQI_EALIGN: return "BQI_EALIGN: pointer or leading dimension misaligned";
     case BQI_EHIP: return "BQI_EHIP: HIP runtime error at launch";
+    case BQI_ENOTSUP: return "BQI_ENOTSUP: the host CPU lacks AVX2/FMA";
     default: return "unknown bqi status";
   }
 }
 
-int bqi_abi_version(void) { return 220; }
+int bqi_abi_version(void) { return 230; }
 
 int quantize_q8_0(const void *x, int x_dtype, int64_t rows, int64_t k,
                   int64_t ldx, int8_t *q, uint16_t *d, void *stream) {

@@ -60,6 +60,7 @@ extern "C" {
 #define BQI_ESHAPE (-2) /* negative size, K not a multiple of 32, ldx < k, size too large */
 #define BQI_EALIGN (-3) /* a pointer or leading dimension violates the alignment rules */
 #define BQI_EHIP (-4)   /* the HIP runtime reported an error at launch */
+#define BQI_ENOTSUP (-5) /* the host CPU lacks the instructions a host entry point needs */
 
 /* activation dtypes for quantize_q8_0 */
 #define BQI_F32 0
@@ -68,9 +69,10 @@ extern "C" {
 /* Human-readable name of a status code (static string, never NULL). */
 BQI_API const char *bqi_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor): 220.  Version 200 added
+/* ABI version of this header (major * 100 + minor): 230.  Version 200 added
  * the k argument of qgemm_w4a8_grouped_workspace_size; 210 added
- * quantize_qgemm_q8_0; 220 added moe_combine_f32 and the GGUF import. */
+ * quantize_qgemm_q8_0; 220 added moe_combine_f32 and the GGUF import; 230
+ * added qgemm_w4a8_grouped_host. */
 BQI_API int bqi_abi_version(void);
 
 /*
@@ -242,6 +244,24 @@ BQI_API int gguf_q8_0_to_planar(const void *blocks, int64_t rows, int64_t k,
                         int8_t *q, uint16_t *d, void *stream);
 BQI_API int gguf_q4_0_to_planar(const void *blocks, int64_t rows, int64_t k,
                         uint8_t *wq4, uint16_t *wd, void *stream);
+
+/*
+ * qgemm_w4a8_grouped_host -- the grouped W4A8 GEMM on the host CPU, with
+ * integer SIMD (page 3: the CPU decode path with a hand-written W4A8 kernel on
+ * pmaddubsw, Method 1 and Contributions; here AVX2 vpmaddubsw).
+ *
+ * HOST pointers, same layouts and the same function as qgemm_w4a8_grouped
+ * (ids outside [0, n_experts) give zero rows), within the same bound.  Runs
+ * synchronously on `nthreads` threads (<= 0: all hardware threads); the
+ * result does not depend on the thread count.  This is a separate entry
+ * point for data in host memory, never a substitute for the GPU path.
+ * Returns BQI_ENOTSUP on a CPU without AVX2 and FMA.
+ */
+BQI_API int qgemm_w4a8_grouped_host(const int8_t *aq, const uint16_t *ad,
+                            int64_t n_tokens, const int32_t *topk_ids,
+                            int64_t top_k, const uint8_t *wq4,
+                            const uint16_t *wd, int64_t n_experts, int64_t n,
+                            int64_t k, float *y, int nthreads);
 
 #ifdef __cplusplus
 }

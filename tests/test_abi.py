@@ -43,7 +43,7 @@ def test_library_exports_exactly_the_header_symbols():
 
 def test_status_strings():
     L = bqi.lib()
-    assert L.bqi_abi_version() == 220
+    assert L.bqi_abi_version() == 230
     for st in (OK, EINVAL, ESHAPE, EALIGN, bqi.BQI_EHIP):
         assert L.bqi_status_string(st).decode().startswith("BQI_")
     assert L.bqi_status_string(12345)
