@@ -371,7 +371,8 @@ def bench_moe_decode(bqi, torch, W, iters):
                     "kernel": "k_grouped_gemv (no routing pass)", "value": round(gbs, 1), "unit": "GB/s",
                     "mean_call_us": round(mean * 1e3, 2),
                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                    "hbm_bytes_algorithmic": byt, "weight_copies_rotated": copies})
+                    "hbm_bytes_algorithmic": byt, "weight_copies_rotated": copies,
+                    "hbm_bytes_measured": traffic("k_grouped_gemv moe decode T=%d" % T)})
     return res
 
 
@@ -435,7 +436,8 @@ def bench_combine(bqi, torch, W, iters):
     return {"workload": "MoE combine T=%d top-%d N=%d" % (m.tokens, m.top_k, m.n),
             "kernel": "k_moe_combine", "value": round(gbs, 1), "unit": "GB/s",
             "mean_launch_us": round(mean * 1e3, 2), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "hbm_bytes_algorithmic": byt, "y_copies_rotated": copies}
+            "hbm_bytes_algorithmic": byt, "y_copies_rotated": copies,
+            "hbm_bytes_measured": traffic("k_moe_combine moe")}
 
 
 def bench_gguf(bqi, torch, W, iters):
@@ -461,7 +463,8 @@ def bench_gguf(bqi, torch, W, iters):
         res.append({"workload": "GGUF %s import %dx%d" % (fmt.upper(), rows, k),
                     "kernel": "k_gguf_split", "value": round(gbs, 1), "unit": "GB/s",
                     "mean_launch_us": round(mean * 1e3, 2),
-                    "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "hbm_bytes_algorithmic": byt})
+                    "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "hbm_bytes_algorithmic": byt,
+                    "hbm_bytes_measured": traffic("k_gguf_split %s %dx%d" % (fmt, rows, k))})
         del srcs, codes, scales
         torch.cuda.empty_cache()
     return res
