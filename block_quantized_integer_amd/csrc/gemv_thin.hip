@@ -267,6 +267,9 @@ __global__ __launch_bounds__(reg_threads(SRC)) void k_gemv_reg(
       }
     }
   }
+  // every activation load is issued before the first weight load: a later
+  // one would make the quantize wait for the whole weight stream
+  __asm__ volatile("" ::: "memory");
 
   i32x4 w[REG_RPW][CH];
   uint16_t dwh[REG_RPW][CH];
