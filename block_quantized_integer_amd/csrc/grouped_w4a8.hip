@@ -518,22 +518,28 @@ hipError_t launch_grouped_w4a8(const int8_t *aq, const float *ad32t,
 // on the GPU, shaped like the thin-M Q8_0 GEMV: HBM-bound, v_dot4 instead of
 // MFMA, and no routing pass.
 //
-// One workgroup of 4 waves per (routed row, 32-column tile): it reads its
-// expert id, and every lane issues all of its loads at once: for lane l, group
-// l (then l + 64, ...) of each of the wave's 8 weight columns (16 packed bytes
-// = the group's 32 codes; one coalesced 1 KB wave load per column and 64
-// groups), its fp16 scale, and the same group of the token's Q8_0 activation
-// row (32 bytes + scale, from L2).  The lane unpacks the codes to int8 (c - 8),
-// forms the exact int32 block dot (8 v_dot4) and accumulates P * (da * dw)
-// with one fma (the fp16 x fp16 product is exact in fp32); each column is then
-// reduced over the wave in a fixed order.  Rows with an invalid expert id are
-// written as zeros.  An expert chosen by several tokens is read once per row,
-// mostly from cache.
+// One workgroup of 4 waves per (routed row, 32-column tile).  The workgroup
+// of row r reads every routed expert id (at most 128) and ranks r among the
+// rows routed to the same expert: the workgroup of each even-ranked row
+// computes that row and the next one of the same expert, and the others exit
+// at once.  An expert's weights thus leave HBM once per pair of its rows
+// (repeat reads mostly hit the MALL), and no workgroup does more than two
+// rows.  Every lane issues all of its loads at once: for lane l, group l (then
+// l + 64, ...) of each row's Q8_0 activation row (32 bytes + scale, from L2),
+// the fp16 scales, and the same group of each of the wave's 8 weight columns
+// (16 packed bytes = the group's 32 codes; one coalesced 1 KB wave load per
+// column and 64 groups).  The lane unpacks the codes to int8 (c - 8), forms
+// the exact int32 block dot (8 v_dot4) and accumulates P * (da * dw) with one
+// fma (the fp16 x fp16 product is exact in fp32); each column is then reduced
+// over the wave in a fixed order.  Rows with an invalid expert id are written
+// as zeros by their own workgroup.
 namespace {
 
-constexpr int GV_CPW = 8;     // weight columns per wave
+constexpr int GV_CPW = 8;     // weight columns per wave (the column reduction assumes 8)
 constexpr int GV_WAVES = 4;
 constexpr int GV_COLS = GV_CPW * GV_WAVES;  // columns per workgroup
+constexpr int GV_ROWS = 2;    // routed rows per pass over the weights
+constexpr int GV_MAX_ROWS = 128;
 
 // (c + 0x78) ^ 0x80 maps each nibble code c (0..15, in a byte) to the int8
 // value c - 8 with no carry between bytes.
@@ -544,86 +550,172 @@ __device__ __forceinline__ int32_t w4_hi(uint32_t p) {
   return (int32_t)((((p >> 4) & 0x0f0f0f0fu) + 0x78787878u) ^ 0x80808080u);
 }
 
-// Sum over the 64 lanes in a fixed order (DPP inside rows of 16, then two
-// cross-row shuffles); valid in every lane.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, v), 0xb1, 0xf, 0xf, false));
-  v += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, v), 0x4e, 0xf, 0xf, false));
-  v += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, v), 0x141, 0xf, 0xf, false));
-  v += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, v), 0x140, 0xf, 0xf, false));
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+// Reduces eight per-lane partial sums v[0..7] (one per column) over the 64
+// lanes in a fixed order.  Three exchange steps halve the columns each lane
+// carries (lanes l and l ^ 32 split columns 0..3 / 4..7, then l ^ 16 and l ^ 8
+// split again), so that lane l ends with column (l >> 3) summed over 8 lanes;
+// three DPP steps then sum the lanes that differ in bits 0..2.  The result is
+// valid in the lanes with (l & 7) == 0.
+__device__ __forceinline__ float reduce_columns8(const float (&v)[8], int lane) {
+  const bool u32 = (lane & 32) != 0, u16 = (lane & 16) != 0, u8 = (lane & 8) != 0;
+  float v4[4], v2[2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float keep = u32 ? v[q + 4] : v[q];
+    const float send = u32 ? v[q] : v[q + 4];
+    v4[q] = keep + __shfl_xor(send, 32);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const float keep = u16 ? v4[q + 2] : v4[q];
+    const float send = u16 ? v4[q] : v4[q + 2];
+    v2[q] = keep + __shfl_xor(send, 16);
+  }
+  float s;
+  {
+    const float keep = u8 ? v2[1] : v2[0];
+    const float send = u8 ? v2[0] : v2[1];
+    s = keep + __shfl_xor(send, 8);
+  }
+  s += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, s), 0xb1, 0xf, 0xf, false));   // lane ^ 1
+  s += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, s), 0x4e, 0xf, 0xf, false));   // lane ^ 2
+  s += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, s), 0x141, 0xf, 0xf, false));  // half-row mirror
+  return s;
 }
 
+// Takes the lowest set row of the 128-row mask (m0: rows 0..63, m1: 64..127)
+// out of it; -1 when the mask is empty.
+__device__ __forceinline__ int pop_row(uint64_t &m0, uint64_t &m1) {
+  if (m0) {
+    const int r = __builtin_ctzll(m0);
+    m0 &= m0 - 1;
+    return r;
+  }
+  if (m1) {
+    const int r = 64 + __builtin_ctzll(m1);
+    m1 &= m1 - 1;
+    return r;
+  }
+  return -1;
+}
+
+// (no __restrict__ on the inputs: with it the compiler may move loads across
+// the memory clobbers that fix their issue order)
 __global__ __launch_bounds__(64 * GV_WAVES) void k_grouped_gemv(
-    const int8_t *__restrict__ aq, const uint16_t *__restrict__ ad,
-    const int32_t *__restrict__ ids, int top_k, const uint8_t *__restrict__ wq4,
-    const uint16_t *__restrict__ wd, int n_experts, int n, int k,
-    float *__restrict__ y) {
+    const int8_t *aq, const uint16_t *ad, const int32_t *ids, int rows_total,
+    int top_k, const uint8_t *wq4, const uint16_t *wd, int n_experts, int n,
+    int k, float *y) {
   const int tiles = (n + GV_COLS - 1) / GV_COLS;
   const int r = blockIdx.x / tiles;           // routed row t * top_k + j
   const int tn = blockIdx.x - r * tiles;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // uniform
   const int c0 = tn * GV_COLS + wave * GV_CPW;
   const int e = ids[r];
+  const int id0 = lane < rows_total ? ids[lane] : -1;
+  const int id1 = lane + 64 < rows_total ? ids[lane + 64] : -1;
   if (e < 0 || e >= n_experts) {
     if (lane < GV_CPW && c0 + lane < n) y[(int64_t)r * n + c0 + lane] = 0.0f;
     return;
   }
-  const int t = r / top_k;
+  uint64_t m0 = __ballot(id0 == e), m1 = __ballot(id1 == e);
+  // rank of row r among the rows routed to expert e; the workgroup of every
+  // GV_ROWS-th of them computes it and the next GV_ROWS - 1, the others exit
+  const uint64_t below0 = r < 64 ? m0 & ((1ull << r) - 1) : m0;
+  const uint64_t below1 = r < 64 ? 0ull : m1 & ((1ull << (r - 64)) - 1);
+  const int rank = __builtin_popcountll(below0) + __builtin_popcountll(below1);
+  if (rank % GV_ROWS != 0) return;
+  m0 &= ~below0;  // row r is now the lowest row left
+  m1 &= ~below1;
   const int nbk = k / QK;
   const int64_t wrow0 = (int64_t)e * n;
-  float acc[GV_CPW];
-#pragma unroll
-  for (int q = 0; q < GV_CPW; ++q) acc[q] = 0.0f;
 
-  for (int g0 = 0; g0 < nbk; g0 += 64) {
-    const int b = g0 + lane;
-    const bool ok = b < nbk;
-    const int bb = ok ? b : 0;  // lanes past k re-read group 0 and add zero
-    // every load first: the weight groups (HBM), then the activation group
-    // and the scales
-    i32x4 w[GV_CPW];
-    uint16_t dwh[GV_CPW];
+  {
+    int rr[GV_ROWS];
 #pragma unroll
-    for (int q = 0; q < GV_CPW; ++q) {
-      const int64_t col = wrow0 + min(c0 + q, n - 1);
-      w[q] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(wq4 + col * (k / 2) + 16 * bb));
-      dwh[q] = wd[col * nbk + bb];
+    for (int j = 0; j < GV_ROWS; ++j) rr[j] = pop_row(m0, m1);
+    float acc[GV_ROWS][GV_CPW];
+#pragma unroll
+    for (int j = 0; j < GV_ROWS; ++j)
+#pragma unroll
+      for (int q = 0; q < GV_CPW; ++q) acc[j][q] = 0.0f;
+
+    for (int g0 = 0; g0 < nbk; g0 += 64) {
+      const int b = g0 + lane;
+      const bool ok = b < nbk;
+      const int bb = ok ? b : 0;  // lanes past k re-read group 0 and add zero
+      // every load is issued before any is waited on: first the activation
+      // groups and all scales (L2), then the weight groups (HBM)
+      const uint32_t gofs = (uint32_t)bb;
+      i32x4 a0[GV_ROWS], a1[GV_ROWS];
+      uint16_t dah[GV_ROWS];
+#pragma unroll
+      for (int j = 0; j < GV_ROWS; ++j) {
+        // an absent second row re-reads the first row's token
+        const int t = (rr[j] >= 0 ? rr[j] : rr[0]) / top_k;
+        const int8_t *arow = aq + (int64_t)t * k;
+        a0[j] = *reinterpret_cast<const i32x4 *>(arow + 32u * gofs);
+        a1[j] = *reinterpret_cast<const i32x4 *>(arow + 32u * gofs + 16u);
+        dah[j] = ad[(int64_t)t * nbk + gofs];
+      }
+      uint16_t dwh[GV_CPW];
+#pragma unroll
+      for (int q = 0; q < GV_CPW; ++q) dwh[q] = wd[(wrow0 + min(c0 + q, n - 1)) * nbk + gofs];
+      __asm__ volatile("" ::: "memory");  // (keeps this issue order)
+      i32x4 w[GV_CPW];
+#pragma unroll
+      for (int q = 0; q < GV_CPW; ++q) {
+        const int64_t col = wrow0 + min(c0 + q, n - 1);
+        w[q] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(wq4 + col * (k / 2) + 16u * gofs));
+      }
+      // all of this pass's loads are in flight before any of them is waited on
+      __asm__ volatile("" ::: "memory");
+      float da[GV_ROWS];
+#pragma unroll
+      for (int j = 0; j < GV_ROWS; ++j) da[j] = ok ? half_bits_to_float(dah[j]) : 0.0f;
+      const bool more = rr[1] >= 0;  // wave-uniform
+#pragma unroll
+      for (int q = 0; q < GV_CPW; ++q) {
+        // elements 0..15 of the group pair with the low nibbles, 16..31 with
+        // the high nibbles; each column is unpacked once for both rows
+        const int32_t l0 = w4_lo((uint32_t)w[q].x), l1 = w4_lo((uint32_t)w[q].y);
+        const int32_t l2 = w4_lo((uint32_t)w[q].z), l3 = w4_lo((uint32_t)w[q].w);
+        const int32_t h0 = w4_hi((uint32_t)w[q].x), h1 = w4_hi((uint32_t)w[q].y);
+        const int32_t h2 = w4_hi((uint32_t)w[q].z), h3 = w4_hi((uint32_t)w[q].w);
+        const float dw = half_bits_to_float(dwh[q]);
+#pragma unroll
+        for (int j = 0; j < GV_ROWS; ++j) {
+          if (j == 0 || more) {
+            int32_t p = 0;
+            p = dot4_i8(a0[j].x, l0, p);
+            p = dot4_i8(a0[j].y, l1, p);
+            p = dot4_i8(a0[j].z, l2, p);
+            p = dot4_i8(a0[j].w, l3, p);
+            p = dot4_i8(a1[j].x, h0, p);
+            p = dot4_i8(a1[j].y, h1, p);
+            p = dot4_i8(a1[j].z, h2, p);
+            p = dot4_i8(a1[j].w, h3, p);
+            acc[j][q] = fmaf((float)p, da[j] * dw, acc[j][q]);
+          }
+        }
+      }
     }
-    const i32x4 a0 = *reinterpret_cast<const i32x4 *>(aq + (int64_t)t * k + 32 * bb);
-    const i32x4 a1 = *reinterpret_cast<const i32x4 *>(aq + (int64_t)t * k + 32 * bb + 16);
-    const float da = ok ? half_bits_to_float(ad[(int64_t)t * nbk + bb]) : 0.0f;
 #pragma unroll
-    for (int q = 0; q < GV_CPW; ++q) {
-      // elements 0..15 of the group pair with the low nibbles, 16..31 with the
-      // high nibbles
-      int32_t p = 0;
-      p = dot4_i8(a0.x, w4_lo((uint32_t)w[q].x), p);
-      p = dot4_i8(a0.y, w4_lo((uint32_t)w[q].y), p);
-      p = dot4_i8(a0.z, w4_lo((uint32_t)w[q].z), p);
-      p = dot4_i8(a0.w, w4_lo((uint32_t)w[q].w), p);
-      p = dot4_i8(a1.x, w4_hi((uint32_t)w[q].x), p);
-      p = dot4_i8(a1.y, w4_hi((uint32_t)w[q].y), p);
-      p = dot4_i8(a1.z, w4_hi((uint32_t)w[q].z), p);
-      p = dot4_i8(a1.w, w4_hi((uint32_t)w[q].w), p);
-      acc[q] = fmaf((float)p, da * half_bits_to_float(dwh[q]), acc[q]);
+    for (int j = 0; j < GV_ROWS; ++j) {
+      if (rr[j] < 0) break;  // wave-uniform
+      const float v = reduce_columns8(acc[j], lane);
+      const int c = c0 + (lane >> 3);
+      if ((lane & 7) == 0 && c < n) y[(int64_t)rr[j] * n + c] = v;
     }
-  }
-#pragma unroll
-  for (int q = 0; q < GV_CPW; ++q) {
-    const float v = wave_sum(acc[q]);
-    if (lane == q && c0 + q < n) y[(int64_t)r * n + c0 + q] = v;
   }
 }
 
 }  // namespace
 
 bool grouped_gemv_supported(int64_t rows_total, int64_t k) {
-  // a few routed rows (decode)
+  // a few routed rows (decode): each workgroup checks every routed id
   (void)k;
-  return rows_total <= 128;
+  return rows_total <= GV_MAX_ROWS;
 }
 
 hipError_t launch_grouped_gemv(const int8_t *aq, const uint16_t *ad,
@@ -633,8 +725,8 @@ hipError_t launch_grouped_gemv(const int8_t *aq, const uint16_t *ad,
                                int64_t k, float *y, hipStream_t stream) {
   const int64_t tiles = (n + GV_COLS - 1) / GV_COLS;
   hipLaunchKernelGGL(k_grouped_gemv, dim3((unsigned)(rows_total * tiles)), dim3(64 * GV_WAVES),
-                     0, stream, aq, ad, ids, (int)top_k, wq4, wd, (int)n_experts, (int)n,
-                     (int)k, y);
+                     0, stream, aq, ad, ids, (int)rows_total, (int)top_k, wq4, wd,
+                     (int)n_experts, (int)n, (int)k, y);
   return hipGetLastError();
 }
 
