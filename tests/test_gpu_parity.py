@@ -323,6 +323,26 @@ def test_prefill_workloads_sampled(name):
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
 
 
+@pytest.mark.parametrize("k", [256, 288])
+def test_qgemm_ragged_more_tiles_than_slots(k):
+    """536 tiles of 128 x 128 (more than one round of workgroups, a short
+    last one), ragged rows and columns, k = 288 ending in a partial 4-block
+    stage.  The 328 right-most columns are checked in full against the
+    oracle, the rest on samples, and two runs agree bitwise."""
+    m, n = 1000, 8520
+    aq = W.random_int8(0, 500, (m, k), seed=1)
+    wq = W.random_int8(0, 501, (n, k), seed=2)
+    ad = W.random_scales(0, 502, (m, k // 32), seed=3)
+    wd = W.random_scales(0, 503, (n, k // 32), seed=4)
+    y = run_gemm(aq, ad, wq, wd)
+    sampled_check(y, aq, ad, wq, wd, k, 8, "ragged")
+    mi, nj = np.meshgrid(np.arange(m), np.arange(64 * 128, n), indexing="ij")
+    yr, asum = oracle.qgemm_q8_0_at(aq, ad, wq, wd, mi.ravel(), nj.ravel())
+    assert_within_bound(y[mi.ravel(), nj.ravel()], yr, asum, k // 32, "ragged right columns")
+    y2 = run_gemm(aq, ad, wq, wd)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
 # ---------------------------------------------------------------------------
 # routing and grouped W4A8
 # ---------------------------------------------------------------------------
