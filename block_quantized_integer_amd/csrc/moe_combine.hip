@@ -8,8 +8,9 @@
 //
 // An HBM stream: every y element is read once and every output written once.
 // A thread owns 4 consecutive columns of one token (16-byte loads when the
-// rows allow it) and accumulates the slots in order with one fma each, so
-// every product-and-add is rounded once: |out - exact| <=
+// rows allow it), issues the loads of all its slots at once (top_k <= 8) and
+// accumulates the slots in order with one fma each, so every product-and-add
+// is rounded once: |out - exact| <=
 // top_k * 2^-24 * sum_j |p y|, and the result is deterministic.
 #include "bqi_device.h"
 #include "bqi_launch.h"
@@ -19,42 +20,86 @@ namespace bqi {
 namespace {
 
 constexpr int CT = 256;
+constexpr int TK_UNROLL = 8;  // top_k up to this: all slot loads issued at once
 
-template <bool VEC>
+// Idx: 32-bit when every index and offset fits, else 64-bit.  TK > 0: top_k
+// <= TK, every load (probabilities and y slots) issued before the first fma;
+// TK == 0: any top_k, one slot at a time.
+template <bool VEC, int TK, typename Idx>
 __global__ __launch_bounds__(CT) void k_moe_combine(const float *__restrict__ y,
                                                     const float *__restrict__ p,
-                                                    int64_t T, int top_k, int64_t n,
+                                                    Idx T, int top_k, Idx n,
                                                     float *__restrict__ out) {
-  const int64_t cols4 = (n + 3) / 4;
-  const int64_t total = T * cols4;
-  for (int64_t idx = (int64_t)blockIdx.x * CT + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * CT) {
-    const int64_t t = idx / cols4;
-    const int64_t c = 4 * (idx - t * cols4);
+  const Idx cols4 = (n + 3) / 4;
+  const Idx total = T * cols4;
+  for (Idx idx = (Idx)blockIdx.x * CT + threadIdx.x; idx < total;
+       idx += (Idx)gridDim.x * CT) {
+    const Idx t = idx / cols4;
+    const Idx c = 4 * (idx - t * cols4);
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    const float *yt = y + t * top_k * n;
-    for (int j = 0; j < top_k; ++j) {
-      const float pj = p[t * top_k + j];
-      if constexpr (VEC) {
-        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(yt + j * n + c));
-        acc[0] = fmaf(pj, v.x, acc[0]);
-        acc[1] = fmaf(pj, v.y, acc[1]);
-        acc[2] = fmaf(pj, v.z, acc[2]);
-        acc[3] = fmaf(pj, v.w, acc[3]);
-      } else {
+    const float *yt = y + (int64_t)t * top_k * n;
+    const float *pt = p + (int64_t)t * top_k;
+    if constexpr (TK > 0) {
+      // slots past top_k re-read slot 0 and are skipped below (their product
+      // is never formed, so no inf * 0 can enter the sum)
+      float pj[TK];
+      f32x4 v[TK];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (c + u < n) acc[u] = fmaf(pj, yt[j * n + c + u], acc[u]);
+      for (int j = 0; j < TK; ++j) {
+        const int jj = j < top_k ? j : 0;
+        pj[j] = pt[jj];
+        if constexpr (VEC) {
+          v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(yt + (int64_t)jj * n + c));
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[j][u] = yt[(int64_t)jj * n + (c + u < n ? c + u : c)];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < TK; ++j) {
+        if (j < top_k) {  // uniform
+          acc[0] = fmaf(pj[j], v[j].x, acc[0]);
+          acc[1] = fmaf(pj[j], v[j].y, acc[1]);
+          acc[2] = fmaf(pj[j], v[j].z, acc[2]);
+          acc[3] = fmaf(pj[j], v[j].w, acc[3]);
+        }
+      }
+    } else {
+      for (int j = 0; j < top_k; ++j) {
+        const float pj = pt[j];
+        if constexpr (VEC) {
+          const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(yt + (int64_t)j * n + c));
+          acc[0] = fmaf(pj, v.x, acc[0]);
+          acc[1] = fmaf(pj, v.y, acc[1]);
+          acc[2] = fmaf(pj, v.z, acc[2]);
+          acc[3] = fmaf(pj, v.w, acc[3]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (c + u < n) acc[u] = fmaf(pj, yt[(int64_t)j * n + c + u], acc[u]);
+        }
       }
     }
+    float *ot = out + (int64_t)t * n;
     if constexpr (VEC) {
-      *reinterpret_cast<f32x4 *>(out + t * n + c) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      *reinterpret_cast<f32x4 *>(ot + c) = f32x4{acc[0], acc[1], acc[2], acc[3]};
     } else {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        if (c + u < n) out[t * n + c + u] = acc[u];
+        if (c + u < n) ot[c + u] = acc[u];
     }
   }
+}
+
+template <int TK, typename Idx>
+void launch_combine_kernel(bool vec, unsigned wgs, const float *y, const float *p, int64_t T,
+                           int64_t top_k, int64_t n, float *out, hipStream_t stream) {
+  if (vec)
+    hipLaunchKernelGGL((k_moe_combine<true, TK, Idx>), dim3(wgs), dim3(CT), 0, stream,
+                       y, p, (Idx)T, (int)top_k, (Idx)n, out);
+  else
+    hipLaunchKernelGGL((k_moe_combine<false, TK, Idx>), dim3(wgs), dim3(CT), 0, stream,
+                       y, p, (Idx)T, (int)top_k, (Idx)n, out);
 }
 
 }  // namespace
@@ -66,12 +111,16 @@ hipError_t launch_moe_combine(const float *y, const float *p, int64_t T,
   int64_t wgs = (work + CT - 1) / CT;
   if (wgs > 8192) wgs = 8192;
   const bool vec = n % 4 == 0 && ((uintptr_t)y & 15) == 0 && ((uintptr_t)out & 15) == 0;
-  if (vec)
-    hipLaunchKernelGGL(k_moe_combine<true>, dim3((unsigned)wgs), dim3(CT), 0, stream,
-                       y, p, T, (int)top_k, n, out);
-  else
-    hipLaunchKernelGGL(k_moe_combine<false>, dim3((unsigned)wgs), dim3(CT), 0, stream,
-                       y, p, T, (int)top_k, n, out);
+  // 32-bit indices while the grid-stride index (work + one grid) fits
+  const bool small = work + wgs * CT < ((int64_t)1 << 31) && n < ((int64_t)1 << 31);
+  const unsigned g = (unsigned)wgs;
+  if (top_k <= TK_UNROLL) {
+    if (small) launch_combine_kernel<TK_UNROLL, uint32_t>(vec, g, y, p, T, top_k, n, out, stream);
+    else launch_combine_kernel<TK_UNROLL, int64_t>(vec, g, y, p, T, top_k, n, out, stream);
+  } else {
+    if (small) launch_combine_kernel<0, uint32_t>(vec, g, y, p, T, top_k, n, out, stream);
+    else launch_combine_kernel<0, int64_t>(vec, g, y, p, T, top_k, n, out, stream);
+  }
   return hipGetLastError();
 }
 

@@ -442,7 +442,8 @@ def combine_bound_ok(out, ref, asum, top_k, what):
     assert not bad.any(), "%s: %d outputs outside top_k * 2^-24 * sum|p y|" % (what, int(bad.sum()))
 
 
-@pytest.mark.parametrize("T,top_k,n", [(947, 8, 768), (5, 3, 130), (1, 1, 1), (64, 8, 7), (3, 0, 16)])
+@pytest.mark.parametrize("T,top_k,n", [(947, 8, 768), (5, 3, 130), (1, 1, 1), (64, 8, 7), (3, 0, 16),
+                                       (20, 12, 96), (7, 10, 33)])
 def test_moe_combine(T, top_k, n):
     g = np.random.default_rng(T * 7 + n)
     y = g.standard_normal((T, top_k, n)).astype(np.float32)
