@@ -27,7 +27,9 @@ namespace {
 constexpr int GT_ = 256;  // blocks per workgroup (one per thread)
 
 template <int BLOCK_BYTES, int CODE_BYTES>
-__global__ __launch_bounds__(GT_) void k_gguf_split(const uint8_t *__restrict__ src,
+// (no __restrict__ on src: with it the compiler sinks the chunk loads past the
+// barrier into the stores that use them)
+__global__ __launch_bounds__(GT_) void k_gguf_split(const uint8_t *src,
                                                     int64_t n_blocks,
                                                     uint8_t *__restrict__ codes,
                                                     uint16_t *__restrict__ scales) {
@@ -39,10 +41,22 @@ __global__ __launch_bounds__(GT_) void k_gguf_split(const uint8_t *__restrict__ 
     const int nb = (int)min((int64_t)GT_, n_blocks - b0);
     const int bytes = nb * BLOCK_BYTES;
     const uint8_t *g = src + b0 * BLOCK_BYTES;
+    // full 16-byte chunks, all of a thread's loads issued before any LDS
+    // store (chunks past the span re-read chunk 0, which a span of at least
+    // one block always holds), then the tail byte by byte (last span only)
+    constexpr int CHUNKS = (SPAN / 16 + GT_ - 1) / GT_;
+    i32x4 r[CHUNKS];
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) {
+      const int o = 16 * ((int)threadIdx.x + GT_ * i);
+      r[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(g + (o + 16 <= bytes ? o : 0)));
+    }
     __syncthreads();
-    // full 16-byte chunks, then the tail byte by byte (only the last span)
-    for (int o = 16 * threadIdx.x; o + 16 <= bytes; o += 16 * GT_)
-      *reinterpret_cast<i32x4 *>(s + o) = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(g + o));
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) {
+      const int o = 16 * ((int)threadIdx.x + GT_ * i);
+      if (o + 16 <= bytes) *reinterpret_cast<i32x4 *>(s + o) = r[i];
+    }
     for (int o = (bytes & ~15) + threadIdx.x; o < bytes; o += GT_) s[o] = g[o];
     __syncthreads();
     const int t = threadIdx.x;
