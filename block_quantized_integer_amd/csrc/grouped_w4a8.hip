@@ -74,7 +74,7 @@ __device__ __forceinline__ int route_scan(int v, int *s_tmp, int &total) {
 // positions of four table rows (coalesced), instead of scattering 2-byte
 // reads over every matched token per table row.
 __device__ __forceinline__ void route_copy_scales(const int *s_match, int total, int base,
-                                                  int top_k, const uint16_t *__restrict__ ad,
+                                                  int top_k, const uint16_t *ad,
                                                   int nbk, float *__restrict__ ad32t, int rpad,
                                                   float (*s_t)[65]) {
   const int tid = threadIdx.x;
@@ -86,9 +86,15 @@ __device__ __forceinline__ void route_copy_scales(const int *s_match, int total,
         const int i = i0 + r;
         if (i < total) {
           const uint16_t *src = ad + (int64_t)(s_match[i] / top_k) * nbk;
+          // the four loads are unconditional (clamped to the row) so that
+          // they are in flight together; the values are masked afterwards
+          uint16_t h[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) h[u] = src[min(b0 + c + u, nbk - 1)];
+          __asm__ volatile("" ::: "memory");
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            if (b0 + c + u < nbk) s_t[c + u][r] = half_bits_to_float(src[b0 + c + u]);
+            if (b0 + c + u < nbk) s_t[c + u][r] = half_bits_to_float(h[u]);
         }
       }
       __syncthreads();
@@ -110,7 +116,7 @@ __device__ __forceinline__ void route_copy_scales(const int *s_match, int total,
 __global__ __launch_bounds__(RT) void k_route(
     const int32_t *__restrict__ ids, int rows_total, int n_experts, int top_k,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ rows, const uint16_t *__restrict__ ad, int nbk,
+    int32_t *__restrict__ rows, const uint16_t *ad, int nbk,
     float *__restrict__ ad32t, int rpad, float *__restrict__ y, int n) {
   __shared__ int s_tmp[RT / 64];
   __shared__ int s_match[RCHUNK];  // (position - chunk base) -> routed row
