@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--only-headline", action="store_true", help="skip the secondary workloads")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--workloads", default="decode,prefill,long,moe,moe_decode,combine,gguf,host",
+    p.add_argument("--workloads", default="decode,decode_m,prefill,long,moe,moe_decode,combine,gguf,host",
                    help="comma list of workloads to run (profiling); the JSON line "
                         "is printed only when decode is among them.  'copy' (never a "
                         "default) runs a plain device copy of known size, the "
@@ -260,6 +260,50 @@ def bench_headline(bqi, torch, W, args):
     }
     ctx = dict(s=s, wq=wq, wd=wd, x=x, step_bytes=step_bytes)
     return res, ctx
+
+
+def bench_decode_variants(bqi, torch, W, iters):
+    """The decode GEMV at M = 4 and M = 16 (the other decode sizes of the
+    configuration): the whole step through quantize_qgemm_q8_0 (the quantizer
+    and the GEMV: one launch only pays off for M = 1) and the GEMV alone, 8
+    rotated weight copies."""
+    res = []
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    s1 = W.DECODE[0]
+    copies = 8
+    wq, wd = [], []
+    for c in range(copies):
+        _, q, d = device_q8(bqi, torch, s1.n, s1.k, 0.02, gen)
+        wq.append(q)
+        wd.append(d)
+    for s in W.DECODE[1:]:
+        log("decode workload M=%d K=%d N=%d" % (s.m, s.k, s.n))
+        x = torch.randn((s.m, s.k), generator=gen, device="cuda", dtype=torch.float32)
+        aq = torch.empty((s.m, s.k), dtype=torch.int8, device="cuda")
+        ad = torch.empty((s.m, s.k // 32), dtype=torch.int16, device="cuda")
+        y = torch.empty((s.m, s.n), dtype=torch.float32, device="cuda")
+        bqi.quantize_q8_0(x, aq, ad)
+        T = Timer(torch)
+        # the API step (one launch for m = 1 only; here quantize + GEMV)
+        step = lambda i: bqi.quantize_qgemm_q8_0(x, wq[i % copies], wd[i % copies], y, aq, ad)
+        kernel = "k_quantize_q8_0 + k_gemv_reg<%d,4,ACT_Q8>" % s.m
+        ms_step = T.loop(step, iters, check=lambda: y)
+        ms_gemv = T.loop(lambda i: bqi.qgemm_q8_0(aq, ad, wq[i % copies], wd[i % copies], y), iters,
+                         check=lambda: y)
+        w_bytes = s.n * s.k + s.n * (s.k // 32) * 2
+        a_bytes = s.m * s.k + s.m * (s.k // 32) * 2
+        gemv_bytes = w_bytes + a_bytes + s.m * s.n * 4
+        step_bytes = gemv_bytes + s.m * s.k * 4 + a_bytes
+        res.append({"workload": "decode M=%d K=%d N=%d" % (s.m, s.k, s.n), "kernel": kernel,
+                    "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s",
+                    "ms_per_step": round(ms_step, 6),
+                    "frac_hbm_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "bytes_per_step": step_bytes,
+                    "gemv_only": {"mean_launch_us": round(ms_gemv * 1e3, 3),
+                                  "GB/s": round(gemv_bytes / (ms_gemv * 1e-3) / 1e9, 1),
+                                  "frac_hbm_peak": round(gemv_bytes / (ms_gemv * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}})
+    return res
 
 
 def bench_gemm(bqi, torch, W, name, iters):
@@ -523,6 +567,11 @@ def main():
         torch.cuda.empty_cache()
     also = []
     if not args.only_headline:
+        if "decode_m" in wl:
+            for r in bench_decode_variants(bqi, torch, W, 200):
+                also.append(r)
+                log(json.dumps(r))
+            torch.cuda.empty_cache()
         for name in ("prefill", "long"):
             if name in wl:
                 also.append(bench_gemm(bqi, torch, W, name, 20))

@@ -11,9 +11,11 @@
 // of a wave's weight loads are issued before any arithmetic, and nothing
 // waits on LDS or a barrier first.
 //
-// k_gemv_reg (m <= 4, m * k <= 16 K codes): each wave owns two weight rows;
-// the activation rows are staged once per workgroup in LDS while the weight
-// loads are in flight, and read with the weights' lane mapping.  A lane
+// k_gemv_reg (m <= 16, m * k <= 64 K codes, k <= 8 K for m > 1): each wave
+// owns two weight rows; the activation rows are staged once per workgroup in
+// LDS (dynamic, up to 68 KB) while the weight loads are in flight, and read
+// with the weights' lane mapping; each activation row's sums are finished
+// before the next row's, which keeps the register count low for m = 16.  A lane
 // holds half of a 32-element block per chunk; it forms the half-block dot
 // product with four dot4 ops, and one DPP lane swap adds the partner half,
 // so every block's int32 P is exact before it is scaled.  Only even lanes
@@ -21,12 +23,14 @@
 // acc = fma((float)P, da * dw, acc) with the exact fp16 x fp16 product, and
 // each half-wave reduces one of the two rows with DPP steps.
 //
-// k_gemv_lds (larger m or k): the m <= 16 activation rows of the current K
-// chunk sit in LDS; a group of LPR lanes shares one weight row and each lane
+// k_gemv_lds (the rest of m <= 16: longer rows): the m activation rows of the
+// current K chunk sit in LDS; a group of LPR lanes shares one weight row and each lane
 // owns two consecutive blocks (64 bytes) per pass.
 //
 // Lanes reduce their fp32 partials with a fixed butterfly, so results are
 // deterministic.
+#include <algorithm>
+
 #include "bqi_device.h"
 #include "bqi_launch.h"
 
@@ -165,10 +169,10 @@ __global__ __launch_bounds__(256) void k_gemv_lds(
 }
 
 
-// ---- m <= 4: coalesced 1 KB loads, two rows per wave -------------------------
+// ---- m <= 16: coalesced 1 KB loads, two rows per wave ------------------------
 
 constexpr int REG_RPW = 2;             // weight rows per wave
-constexpr int REG_ACT_BYTES = 16384;   // m * k bytes of activation codes staged in LDS
+constexpr int REG_ACT_BYTES = 65536;   // m * k bytes of activation codes staged in LDS
 
 // v + (v from lane ^ 1): the DPP quad permutation [1,0,3,2]
 __device__ __forceinline__ int32_t add_partner_i32(int32_t v) {
@@ -192,25 +196,32 @@ __device__ __forceinline__ float half_wave_sum(float v) {
 // quantize-and-multiply decode path).
 enum ActSrc { ACT_Q8 = 0, ACT_F32 = 1, ACT_F16 = 2 };
 
-// Threads per workgroup: 4 waves for Q8_0 input; 8 waves when every
-// workgroup quantizes the activations itself, which halves the number of
-// workgroups repeating that work.
-constexpr int reg_threads(int src) { return src == ACT_Q8 ? 256 : 512; }
+// Threads per workgroup: 4 waves for Q8_0 input of up to 4 rows; 8 waves when
+// every workgroup quantizes the activations itself, or stages more than 4
+// activation rows, which halves the number of workgroups repeating that work.
+constexpr int reg_threads(int src, int mt) { return src == ACT_Q8 && mt <= 4 ? 256 : 512; }
+
+// Dynamic LDS of the register kernel: the staged codes (MT * CH KB plus a
+// spare 16-byte slot) and their scales (plus a spare slot).
+constexpr int reg_lds_bytes(int mt, int ch) {
+  return (mt * ch * 1024 + 16) + ((mt * ch * 32 + 1) * 2 + 14) / 16 * 16;
+}
 
 // (no __restrict__ on the inputs: with it the compiler may move the scale
 // loads across the memory clobber below, behind the barrier)
 template <int MT, int CH, int SRC>
-__global__ __launch_bounds__(reg_threads(SRC)) void k_gemv_reg(
+__global__ __launch_bounds__(reg_threads(SRC, MT)) void k_gemv_reg(
     const int8_t *aq, const uint16_t *ad, const void *x, int ldx, int m,
     const int8_t *wq, const uint16_t *wd, int n, int k, float *y,
     int8_t *q_out, uint16_t *d_out) {
   static_assert(MT * CH * 1024 <= REG_ACT_BYTES, "activation stage too small");
   // one spare 16-byte slot (and scale slot) takes the stores of lanes with
   // nothing to stage, so the staging stores stay unconditional
-  __shared__ __attribute__((aligned(16))) int8_t sA[MT * CH * 1024 + 16];
-  __shared__ uint16_t sAd[MT * CH * 32 + 1];
+  extern __shared__ __attribute__((aligned(16))) int8_t reg_lds[];
+  int8_t *sA = reg_lds;                                                      // [MT*CH*1024 + 16]
+  uint16_t *sAd = reinterpret_cast<uint16_t *>(reg_lds + MT * CH * 1024 + 16);  // [MT*CH*32 + 1]
   const int lane = threadIdx.x & 63;
-  constexpr int NT = reg_threads(SRC);
+  constexpr int NT = reg_threads(SRC, MT);
   const int row0 = ((int)blockIdx.x * (NT / 64) + (int)(threadIdx.x >> 6)) * REG_RPW;
   const int nbk = k / QK;
   const bool even = (lane & 1) == 0;
@@ -360,6 +371,11 @@ __global__ __launch_bounds__(reg_threads(SRC)) void k_gemv_reg(
         }
       }
     }
+    // finish this row's sums here: otherwise the compiler sinks them into the
+    // `i < m` store branches at the end and keeps every block's int32 dot
+    // product of every row live until then
+#pragma unroll
+    for (int r = 0; r < REG_RPW; ++r) __asm__ volatile("" : "+v"(acc[r][i]));
   }
 
   // lanes 0..31 finish row 0, lanes 32..63 row 1
@@ -380,13 +396,32 @@ template <int MT, int CH, int SRC>
 hipError_t launch_reg(const int8_t *aq, const uint16_t *ad, const void *x, int64_t ldx,
                       int64_t m, const int8_t *wq, const uint16_t *wd, int64_t n, int64_t k,
                       float *y, int8_t *q_out, uint16_t *d_out, hipStream_t stream) {
-  constexpr int NT = reg_threads(SRC);
+  constexpr int NT = reg_threads(SRC, MT);
+  constexpr int LDS = reg_lds_bytes(MT, CH);
+  if constexpr (LDS > 65536) {
+    // above the default dynamic-LDS limit: raise it once for this kernel
+    static bool raised = false;
+    if (!raised) {
+      const hipError_t e = hipFuncSetAttribute((const void *)k_gemv_reg<MT, CH, SRC>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+      if (e != hipSuccess) return e;
+      raised = true;
+    }
+  }
   const int64_t rows_per_wg = (NT / 64) * REG_RPW;
   const int64_t wgs = (n + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL((k_gemv_reg<MT, CH, SRC>), dim3((unsigned)wgs), dim3(NT), 0,
+  hipLaunchKernelGGL((k_gemv_reg<MT, CH, SRC>), dim3((unsigned)wgs), dim3(NT), LDS,
                      stream, aq, ad, x, (int)ldx, (int)m, wq, wd, (int)n, (int)k, y,
                      q_out, d_out);
   return hipGetLastError();
+}
+
+// The register kernel covers MT * CH <= 64 (MT activation rows of CH KB of
+// codes staged in LDS) with CH <= 8 weight chunks per lane (16 for a single
+// row: more would leave no registers for anything else); the fused
+// activation sources only MT * CH <= 16.
+constexpr bool reg_fits(int mt, int ch, int src) {
+  return ch <= (mt == 1 ? 16 : 8) && mt * ch <= (src == ACT_Q8 ? 64 : 16);
 }
 
 template <int MT, int SRC>
@@ -398,13 +433,20 @@ hipError_t launch_reg_ch(const int8_t *aq, const uint16_t *ad, const void *x, in
   if (ch <= 1) return launch_reg<MT, 1, SRC>(aq, ad, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
   if (ch <= 2) return launch_reg<MT, 2, SRC>(aq, ad, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
   if (ch <= 4) return launch_reg<MT, 4, SRC>(aq, ad, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
-  if constexpr (MT <= 2) {
+  if constexpr (reg_fits(MT, 8, SRC)) {
     if (ch <= 8) return launch_reg<MT, 8, SRC>(aq, ad, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
   }
-  if constexpr (MT <= 1) {
+  if constexpr (reg_fits(MT, 16, SRC)) {
     if (ch <= 16) return launch_reg<MT, 16, SRC>(aq, ad, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
   }
   return hipErrorInvalidValue;  // not reached: the dispatcher checks the size
+}
+
+// Smallest power of two >= v (v >= 1).
+int64_t pow2_ceil(int64_t v) {
+  int64_t p = 1;
+  while (p < v) p <<= 1;
+  return p;
 }
 
 template <int MT>
@@ -429,11 +471,18 @@ hipError_t launch_mt(const int8_t *aq, const uint16_t *ad, int64_t m,
 hipError_t launch_gemv_thin(const int8_t *aq, const uint16_t *ad, int64_t m,
                             const int8_t *wq, const uint16_t *wd, int64_t n,
                             int64_t k, float *y, hipStream_t stream) {
-  // register kernel while m * k activation codes fit its LDS stage
-  const int64_t ch = (k + 1023) / 1024;
-  if (m <= 1 && ch <= 16) return launch_reg_ch<1, ACT_Q8>(aq, ad, nullptr, 0, m, wq, wd, n, k, y, nullptr, nullptr, stream);
-  if (m <= 2 && ch <= 8) return launch_reg_ch<2, ACT_Q8>(aq, ad, nullptr, 0, m, wq, wd, n, k, y, nullptr, nullptr, stream);
-  if (m <= 4 && ch <= 4) return launch_reg_ch<4, ACT_Q8>(aq, ad, nullptr, 0, m, wq, wd, n, k, y, nullptr, nullptr, stream);
+  // register kernel while the m rows of codes fit its LDS stage
+  const int64_t ch = pow2_ceil((k + 1023) / 1024);
+  const int64_t mt = pow2_ceil(m);
+  if (mt <= 16 && reg_fits((int)mt, (int)std::min<int64_t>(ch, 1 << 20), ACT_Q8)) {
+    switch (mt) {
+      case 1: return launch_reg_ch<1, ACT_Q8>(aq, ad, nullptr, 0, m, wq, wd, n, k, y, nullptr, nullptr, stream);
+      case 2: return launch_reg_ch<2, ACT_Q8>(aq, ad, nullptr, 0, m, wq, wd, n, k, y, nullptr, nullptr, stream);
+      case 4: return launch_reg_ch<4, ACT_Q8>(aq, ad, nullptr, 0, m, wq, wd, n, k, y, nullptr, nullptr, stream);
+      case 8: return launch_reg_ch<8, ACT_Q8>(aq, ad, nullptr, 0, m, wq, wd, n, k, y, nullptr, nullptr, stream);
+      default: return launch_reg_ch<16, ACT_Q8>(aq, ad, nullptr, 0, m, wq, wd, n, k, y, nullptr, nullptr, stream);
+    }
+  }
   if (m <= 1) return launch_mt<1>(aq, ad, m, wq, wd, n, k, y, stream);
   if (m <= 2) return launch_mt<2>(aq, ad, m, wq, wd, n, k, y, stream);
   if (m <= 4) return launch_mt<4>(aq, ad, m, wq, wd, n, k, y, stream);
@@ -441,24 +490,21 @@ hipError_t launch_gemv_thin(const int8_t *aq, const uint16_t *ad, int64_t m,
   return launch_mt<16>(aq, ad, m, wq, wd, n, k, y, stream);
 }
 
+// The fused launch pays off for one activation row only: every workgroup
+// quantizes all m rows again (m = 4: 19.9 us against 13.4 us for the two
+// calls on the decode shape), so larger m takes the quantizer and then the
+// GEMV.
 bool gemv_fused_supported(int64_t m, int64_t k) {
   const int64_t ch = (k + 1023) / 1024;
-  return (m <= 1 && ch <= 16) || (m <= 2 && ch <= 8) || (m <= 4 && ch <= 4);
+  return m <= 1 && ch <= 16;
 }
 
 hipError_t launch_gemv_fused(const void *x, bool f16, int64_t ldx, int64_t m,
                              const int8_t *wq, const uint16_t *wd, int64_t n,
                              int64_t k, float *y, int8_t *q_out,
                              uint16_t *d_out, hipStream_t stream) {
-  const int64_t ch = (k + 1023) / 1024;
-  if (f16) {
-    if (m <= 1 && ch <= 16) return launch_reg_ch<1, ACT_F16>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
-    if (m <= 2 && ch <= 8) return launch_reg_ch<2, ACT_F16>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
-    return launch_reg_ch<4, ACT_F16>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
-  }
-  if (m <= 1 && ch <= 16) return launch_reg_ch<1, ACT_F32>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
-  if (m <= 2 && ch <= 8) return launch_reg_ch<2, ACT_F32>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
-  return launch_reg_ch<4, ACT_F32>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
+  if (f16) return launch_reg_ch<1, ACT_F16>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
+  return launch_reg_ch<1, ACT_F32>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
 }
 
 }  // namespace bqi

@@ -134,10 +134,11 @@ BQI_API int qgemm_q8_0(const int8_t *aq, const uint16_t *ad, int64_t m,
  *   q  [m][k] int8, d [m][k/32] fp16 bits (output): the Q8_0 activations,
  *      bit-identical to quantize_q8_0(x)
  *
- * For m <= 4 with k <= 16384 / m (rounded up to 1024) it is one launch: every
- * workgroup quantizes the activation rows itself while its weight loads are
- * in flight, which saves the quantizer's launch on the decode path.  Other
- * sizes run quantize_q8_0 and qgemm_q8_0 back to back on `stream`.
+ * For m == 1 with k <= 16384 it is one launch: every workgroup quantizes the
+ * activation row itself while its weight loads are in flight, which saves
+ * the quantizer's launch on the decode path.  Other sizes (including m > 1,
+ * where repeating the quantization in every workgroup costs more than the
+ * launch) run quantize_q8_0 and qgemm_q8_0 back to back on `stream`.
  * n == 0 only quantizes.  Requirements: those of quantize_q8_0 and
  * qgemm_q8_0.
  */

@@ -257,11 +257,13 @@ def test_decode_workload_full(decode_weights, m):
 
 @pytest.mark.parametrize("m,k,n,dtype", [
     (1, 4096, 12288, "f32"),    # the decode workload, fused (one launch)
-    (4, 4096, 12288, "f32"),    # fused, four rows
-    (2, 8192, 300, "f16"),      # fused, fp16 input, ragged N
+    (1, 8192, 300, "f16"),      # fused, fp16 input, ragged N
     (1, 16384, 77, "f32"),      # fused, largest K of the single-row kernel
-    (3, 96, 40, "f32"),         # fused, K shorter than one 1 KB chunk
-    (16, 4096, 512, "f32"),     # not fused: quantize + thin-M GEMM
+    (1, 96, 40, "f32"),         # fused, K shorter than one 1 KB chunk
+    (4, 4096, 12288, "f32"),    # not fused: quantize + thin-M GEMM, four rows
+    (2, 8192, 300, "f16"),      # not fused, fp16 input, ragged N
+    (3, 96, 40, "f32"),         # not fused, K shorter than one 1 KB chunk
+    (16, 4096, 512, "f32"),     # not fused: quantize + thin-M GEMM (m = 16)
     (40, 256, 130, "f16"),      # not fused: quantize + MFMA GEMM
 ])
 def test_fused_quantize_qgemm(decode_weights, m, k, n, dtype):
@@ -285,11 +287,13 @@ def test_fused_quantize_qgemm(decode_weights, m, k, n, dtype):
     assert_within_bound(host(y), yr, asum, k // 32, "fused m=%d k=%d" % (m, k))
 
 
-def test_fused_quantize_qgemm_strided_rows(decode_weights):
-    """Row stride ldx > k (a column slice of a wider fp32 tensor)."""
+@pytest.mark.parametrize("rows", [1, 3])
+def test_fused_quantize_qgemm_strided_rows(decode_weights, rows):
+    """Row stride ldx > k (a column slice of a wider fp32 tensor); one row
+    takes the fused launch, three the two calls."""
     qw_g, dw_g, qw, dw = decode_weights
     k = W.DECODE[0].k
-    wide = W.activations("decode", 3, k + 64, seed=11)
+    wide = W.activations("decode", rows, k + 64, seed=11)
     x = dev_tensor(wide)[:, :k]
     y, q, d = bqi.quantize_qgemm_q8_0(x, qw_g, dw_g)
     qr, dr = oracle.quantize_q8_0(np.ascontiguousarray(wide[:, :k]))
