@@ -23,6 +23,10 @@
 // acc = fma((float)P, da * dw, acc) with the exact fp16 x fp16 product, and
 // each half-wave reduces one of the two rows with DPP steps.
 //
+// k_gemv_mfma16 (4 < m <= 16 with k a multiple of 64 whose stages fit LDS):
+// the same streaming loads, turned into int8 MFMA operands in registers; one
+// MFMA per block replaces the m rows of dot4 work.
+//
 // k_gemv_lds (the rest of m <= 16: longer rows): the m activation rows of the
 // current K chunk sit in LDS; a group of LPR lanes shares one weight row and each lane
 // owns two consecutive blocks (64 bytes) per pass.
@@ -466,12 +470,268 @@ hipError_t launch_mt(const int8_t *aq, const uint16_t *ad, int64_t m,
   return hipGetLastError();
 }
 
+
+// ---- 4 < m <= 16: int8 MFMA on weights transposed in registers --------------
+//
+// One v_mfma_i32_16x16x32_i8 multiplies 16 activation rows by 16 weight rows
+// over exactly one Q8_0 block: lane l supplies 8 codes of row l % 16 (K bytes
+// 8 * (l / 16) .. +7 of the block) of each operand and receives the int32 dot
+// products of activation rows 4 * (l / 16) + (0..3) with weight row l % 16.
+// The accumulator seed and the two-fma scale epilogue are those of the
+// large-M GEMM (one rounding per block term).
+//
+// Loading the weights straight into that fragment layout would make every
+// load instruction touch 16 rows 32 bytes at a time, which streams at well
+// under half the rate of whole cache lines.  A wave owns 16 weight rows and
+// one K part of at most 1 KB (32 blocks, 8 chunks of 128 bytes); load pair p
+// fetches chunk p of rows 0..7 and of rows 8..15, lane l = 16 q + 8 h + i
+// taking bytes 32 q + 16 h .. +15 of row i (resp. 8 + i), so that every
+// instruction reads eight whole 128-byte lines.  The pair is turned into four
+// MFMA operands in registers:
+//   1. two DPP moves per dword (rotation by 8 inside each 16-lane row, the
+//      bank mask limiting each to the lanes that take the other row's half)
+//      leave lane l = (row l % 16, q) holding all 32 bytes of block q of
+//      the chunk;
+//   2. a 4 x 4 transpose of 8-byte pieces between the four 16-lane rows q and
+//      the four pieces of a block: v_permlane32_swap exchanges the upper
+//      lane rows of pieces 0, 1 with the lower lane rows of pieces 2, 3, then
+//      v_permlane16_swap the odd lane rows of pieces 0, 2 with the even lane
+//      rows of pieces 1, 3.  Piece register e then holds, in lane row g,
+//      bytes 8 g .. 8 g + 7 of block e: the MFMA operand of block 4 p + e.
+// A workgroup has g groups of 16 weight rows and splits K over ks waves per
+// group; the activation rows and their scales are staged once per workgroup
+// in LDS (direct loads, then a barrier that does not wait for the weight
+// stream), so each wave multiplies chunk p as soon as its pair has landed
+// while the rest streams in.  The K parts are added in a fixed order through
+// LDS at the end.  Activation rows past m read row m - 1 and are not stored.
+constexpr int MF_WAVES = 12;                          // waves per workgroup at most
+constexpr int MF_DSTRIDE = 32 * 4 + 16;               // scale row stride in a wave's slot
+constexpr int MF_SLOT = 16 * MF_DSTRIDE;              // LDS bytes per wave (weight scales)
+constexpr int64_t MF_LDS_MAX = 160 * 1024;
+
+// Activation stage row stride: whole 1 KB direct-load pieces plus 16 bytes,
+// so that a fragment read of 16 rows touches every LDS bank once per half-wave.
+constexpr int64_t mf_lda(int64_t k) { return (k + 1023) / 1024 * 1024 + 16; }
+// The activation scale stage has 32 spare blocks (zeros) after the last, so
+// that the last K part reads whole chunks without a bound check.
+constexpr int64_t mf_lds_bytes(int64_t k, int64_t waves) {
+  return 16 * mf_lda(k) + (k / QK + 32) * 16 * 4 + waves * MF_SLOT;
+}
+
+// 8-byte MFMA operand from two dwords (low dword first in K)
+__device__ __forceinline__ long mf_pair(uint32_t lo, uint32_t hi) {
+  return (long)(((uint64_t)hi << 32) | lo);
+}
+
+// (no __restrict__ on the inputs: with it the compiler may move loads across
+// the compiler barriers that fix their issue order)
+__global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
+    const int8_t *aq, const uint16_t *ad, int m, const int8_t *wq,
+    const uint16_t *wd, int n, int k, int ks, float *y) {
+  extern __shared__ __attribute__((aligned(16))) int8_t mf_lds[];
+  const int nbk = k / QK;
+  const int lda = (int)mf_lda(k);
+  int8_t *sA = mf_lds;                                        // [16][lda], rows < m
+  float *sD = reinterpret_cast<float *>(mf_lds + 16 * lda);   // [nbk + 32][16], rows < m
+  const int nthreads = (int)blockDim.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
+  const int nwaves = nthreads >> 6, groups = nwaves / ks;
+  // the weight scales of the part as fp32, zero past the part
+  int8_t *slotD = mf_lds + 16 * lda + (nbk + 32) * 64 + wave * MF_SLOT;  // [16][MF_DSTRIDE]
+  const int grp = wave / ks, part = wave - grp * ks;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int n0 = ((int)blockIdx.x * groups + grp) * 16;
+  const int pb0 = 32 * part;              // first block of this K part
+  const int pb = min(32, nbk - pb0);      // blocks in it (even: k % 64 == 0)
+
+  // Issue order matters (loads retire in order): the activation codes (L2,
+  // straight to LDS, invisible to the compiler), their scales, the weight
+  // scales, then the weight chunks in the order they are multiplied.
+  // 1. activation codes: wave instruction q covers 1 KB of row q / ks, piece
+  //    q % ks; lanes past k re-read the row's last 16 bytes (never used)
+  for (int q = wave; q < m * ks; q += nwaves) {
+    const int r = q / ks, c = q - r * ks;
+    const int off = min(1024 * c + 16 * lane, k - 16);
+    dma_lds16(aq + (int64_t)r * k + off, sA + r * lda + 1024 * c);
+  }
+  // 2. activation scales, four per thread (a loop after the barrier's wait
+  //    takes any beyond that)
+  const int scales = m * nbk;
+  uint16_t h[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) h[u] = ad[min(tid + u * nthreads, scales - 1)];
+  __asm__ volatile("" ::: "memory");
+  // 3. weight scales of the part as dwords: instruction i, lane l -> row
+  //    4 i + l / 16, blocks 2 (l % 16), 2 (l % 16) + 1 (past the part: its
+  //    last pair; rows past n: row n - 1)
+  uint32_t dw2[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = min(n0 + 4 * i + g, n - 1);
+    const int b = pb0 + min(2 * l16, pb - 2);
+    dw2[i] = *reinterpret_cast<const uint32_t *>(wd + (int64_t)row * nbk + b);
+  }
+  // 4. the weight chunks (HBM): pair p = rows n0 + (l & 7) and n0 + 8 + (l & 7),
+  //    bytes 128 p + 16 (l >> 3) of the part (lanes past k: the row's last 16)
+  const int woff = QK * pb0 + 16 * (lane >> 3);
+  const int8_t *wr0 = wq + (int64_t)min(n0 + (lane & 7), n - 1) * k;
+  const int8_t *wr1 = wq + (int64_t)min(n0 + 8 + (lane & 7), n - 1) * k;
+  i32x4 w[16];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int off = min(woff + 128 * p, k - 16);
+    w[2 * p] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(wr0 + off));
+    w[2 * p + 1] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(wr1 + off));
+  }
+  __asm__ volatile("" ::: "memory");
+  // the 20 loads above are the only ones issued after the scales (2.), so
+  // this waits for the scales and the activation codes but not the weights
+  wait_vmcnt<20>();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int c = tid + u * nthreads;
+    const int i = c / nbk, b = c - i * nbk;
+    if (c < scales) sD[b * 16 + i] = half_bits_to_float(h[u]);
+  }
+  for (int c = tid + 4 * nthreads; c < scales; c += nthreads) {
+    const int i = c / nbk, b = c - i * nbk;
+    sD[b * 16 + i] = half_bits_to_float(ad[c]);
+  }
+  for (int c = tid; c < 32 * 16; c += nthreads) sD[nbk * 16 + c] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool in_part = 2 * l16 < pb;
+    float2 v;
+    v.x = in_part ? half_bits_to_float((uint16_t)(dw2[i] & 0xffffu)) : 0.0f;
+    v.y = in_part ? half_bits_to_float((uint16_t)(dw2[i] >> 16)) : 0.0f;
+    *reinterpret_cast<float2 *>(slotD + (4 * i + g) * MF_DSTRIDE + 8 * l16) = v;
+  }
+  lds_barrier();  // the stages are complete; the weight loads stay in flight
+
+  const i32x4 seed = {MAGIC_BITS, MAGIC_BITS, MAGIC_BITS, MAGIC_BITS};
+  const int8_t *arow = sA + min(l16, m - 1) * lda + QK * pb0 + 8 * g;
+  const float *sDrow = sD + pb0 * 16 + 4 * g;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    if (4 * p < pb) {  // uniform
+      // 1. lane (row l % 16, q): block q of chunk p, bytes 0..15 and 16..31.
+      //    Lanes 8..15 of a row (DPP banks 2, 3) take bytes 0..15 of their
+      //    row from the second load of lane l ^ 8; lanes 0..7 (banks 0, 1)
+      //    take bytes 16..31 from the first load of lane l ^ 8.
+      uint32_t lo[4], hi[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int a = w[2 * p][d], b = w[2 * p + 1][d];
+        lo[d] = (uint32_t)__builtin_amdgcn_update_dpp(a, b, 0x128, 0xf, 0xc, false);
+        hi[d] = (uint32_t)__builtin_amdgcn_update_dpp(b, a, 0x128, 0xf, 0x3, false);
+      }
+      // 2. the 4 x 4 transpose of 8-byte pieces: pieces 0..3 are
+      //    (lo0, lo1), (lo2, lo3), (hi0, hi1), (hi2, hi3)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const auto r = __builtin_amdgcn_permlane32_swap(lo[d], hi[d], false, false);
+        lo[d] = r[0];
+        hi[d] = r[1];
+      }
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const auto r = __builtin_amdgcn_permlane16_swap(lo[d], lo[d + 2], false, false);
+        lo[d] = r[0];
+        lo[d + 2] = r[1];
+        const auto s = __builtin_amdgcn_permlane16_swap(hi[d], hi[d + 2], false, false);
+        hi[d] = s[0];
+        hi[d + 2] = s[1];
+      }
+      const long wf[4] = {mf_pair(lo[0], lo[1]), mf_pair(lo[2], lo[3]),
+                          mf_pair(hi[0], hi[1]), mf_pair(hi[2], hi[3])};
+      // the four blocks' weight scales of row l % 16; blocks past the part
+      // (its last chunk only) have a zero scale, which adds exactly nothing,
+      // and their reads stay inside the stages
+      const f32x4 dsc = *reinterpret_cast<const f32x4 *>(slotD + l16 * MF_DSTRIDE + 16 * p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int b = 4 * p + e;  // block within the part
+        const long a = *reinterpret_cast<const long *>(arow + QK * b);
+        const f32x4 da = *reinterpret_cast<const f32x4 *>(sDrow + b * 16);
+        const i32x4 dd = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, wf[e], seed, 0, 0, 0);
+        const float dw = dsc[e];
+        const float ncd = -MAGIC_F * dw;  // exact
+        acc[0] = fmaf(fmaf(bits_to_float(dd[0]), dw, ncd), da.x, acc[0]);
+        acc[1] = fmaf(fmaf(bits_to_float(dd[1]), dw, ncd), da.y, acc[1]);
+        acc[2] = fmaf(fmaf(bits_to_float(dd[2]), dw, ncd), da.z, acc[2]);
+        acc[3] = fmaf(fmaf(bits_to_float(dd[3]), dw, ncd), da.w, acc[3]);
+      }
+    }
+  }
+
+  // 5. the K parts of each group, added in order through LDS, then stored
+  lds_barrier();  // every wave is done reading the stage
+  float *red = reinterpret_cast<float *>(mf_lds);  // [group][part 1..][4][64]
+  if (part > 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[((grp * (ks - 1) + part - 1) * 4 + r) * 64 + lane] = acc[r];
+  }
+  lds_barrier();
+  if (part > 0) return;
+  for (int p = 1; p < ks; ++p)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] += red[((grp * (ks - 1) + p - 1) * 4 + r) * 64 + lane];
+  const int col = n0 + l16;
+  if (col < n) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * g + r;
+      if (row < m) y[(int64_t)row * n + col] = acc[r];
+    }
+  }
+}
+
+// Workgroup shape of the MFMA kernel: ks = ceil(k / 1 KB) waves per group and
+// as many groups as fit MF_WAVES waves and the LDS, but no more than keep one
+// workgroup per CU for the row groups there are.  Returns false when even one
+// group does not fit (the caller then takes the register kernel).
+bool mf_shape(int64_t n, int64_t k, int *ks_out, int *groups_out) {
+  const int64_t ks = (k + 1023) / 1024;
+  if (k % 64 != 0 || ks > MF_WAVES) return false;
+  const int64_t row_groups = (n + 15) / 16;
+  int64_t groups = std::max<int64_t>(1, std::min<int64_t>(MF_WAVES / ks, row_groups / 256));
+  while (groups > 1 && mf_lds_bytes(k, groups * ks) > MF_LDS_MAX) --groups;
+  if (mf_lds_bytes(k, groups * ks) > MF_LDS_MAX) return false;
+  *ks_out = (int)ks;
+  *groups_out = (int)groups;
+  return true;
+}
+
+hipError_t launch_mfma16(const int8_t *aq, const uint16_t *ad, int64_t m,
+                         const int8_t *wq, const uint16_t *wd, int64_t n, int64_t k,
+                         int ks, int groups, float *y, hipStream_t stream) {
+  const int64_t lds = mf_lds_bytes(k, (int64_t)ks * groups);
+  static bool raised = false;
+  if (lds > 65536 && !raised) {
+    const hipError_t e = hipFuncSetAttribute((const void *)k_gemv_mfma16,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)MF_LDS_MAX);
+    if (e != hipSuccess) return e;
+    raised = true;
+  }
+  const int64_t wgs = (n + 16 * groups - 1) / (16 * groups);
+  hipLaunchKernelGGL(k_gemv_mfma16, dim3((unsigned)wgs), dim3(64 * ks * groups), (unsigned)lds,
+                     stream, aq, ad, (int)m, wq, wd, (int)n, (int)k, ks, y);
+  return hipGetLastError();
+}
 }  // namespace
 
 hipError_t launch_gemv_thin(const int8_t *aq, const uint16_t *ad, int64_t m,
                             const int8_t *wq, const uint16_t *wd, int64_t n,
                             int64_t k, float *y, hipStream_t stream) {
-  // register kernel while the m rows of codes fit its LDS stage
+  // more than 4 rows: int8 MFMA while its stages fit (k a multiple of 64 and
+  // wd 4-byte aligned: the weight scales load in aligned pairs)
+  int ks = 0, groups = 0;
+  if (m > 4 && ((uintptr_t)wd & 3) == 0 && mf_shape(n, k, &ks, &groups))
+    return launch_mfma16(aq, ad, m, wq, wd, n, k, ks, groups, y, stream);
+  // otherwise the register kernel while the m rows of codes fit its LDS stage
   const int64_t ch = pow2_ceil((k + 1023) / 1024);
   const int64_t mt = pow2_ceil(m);
   if (mt <= 16 && reg_fits((int)mt, (int)std::min<int64_t>(ch, 1 << 20), ACT_Q8)) {

@@ -145,7 +145,11 @@ def run_gemm(aq, ad, wq, wd):
 
 SHAPES = [(1, 32, 1), (1, 96, 33), (2, 64, 100), (3, 160, 77), (4, 256, 512), (5, 4096, 40),
           (8, 480, 129), (13, 8192, 17), (16, 256, 512), (17, 64, 31), (32, 32, 64),
-          (33, 96, 130), (100, 320, 257), (129, 160, 128), (256, 1024, 384), (300, 4160, 200)]
+          (33, 96, 130), (100, 320, 257), (129, 160, 128), (256, 1024, 384), (300, 4160, 200),
+          # thin-M MFMA kernel: a last K part of two blocks, one part of two
+          # blocks, five and six parts, two row groups per workgroup with a
+          # ragged last workgroup
+          (6, 1088, 70), (9, 64, 3000), (7, 5120, 50), (16, 6144, 33), (12, 2048, 8200)]
 
 
 @pytest.mark.parametrize("m,k,n", SHAPES)
