@@ -505,6 +505,7 @@ hipError_t launch_mt(const int8_t *aq, const uint16_t *ad, int64_t m,
 // while the rest streams in.  The K parts are added in a fixed order through
 // LDS at the end.  Activation rows past m read row m - 1 and are not stored.
 constexpr int MF_WAVES = 12;                          // waves per workgroup at most
+constexpr int MF_DEPTH = 3;                           // weight load pairs in flight per wave
 constexpr int MF_DSTRIDE = 32 * 4 + 16;               // scale row stride in a wave's slot
 constexpr int MF_SLOT = 16 * MF_DSTRIDE;              // LDS bytes per wave (weight scales)
 constexpr int64_t MF_LDS_MAX = 160 * 1024;
@@ -534,8 +535,8 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
   int8_t *sA = mf_lds;                                        // [16][lda], rows < m
   float *sD = reinterpret_cast<float *>(mf_lds + 16 * lda);   // [nbk + 32][16], rows < m
   const int nthreads = (int)blockDim.x;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int nwaves = nthreads >> 6, groups = nwaves / ks;
   // the weight scales of the part as fp32, zero past the part
   int8_t *slotD = mf_lds + 16 * lda + (nbk + 32) * 64 + wave * MF_SLOT;  // [16][MF_DSTRIDE]
@@ -545,22 +546,24 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
   const int pb0 = 32 * part;              // first block of this K part
   const int pb = min(32, nbk - pb0);      // blocks in it (even: k % 64 == 0)
 
-  // Issue order matters (loads retire in order): the activation codes (L2,
-  // straight to LDS, invisible to the compiler), their scales, the weight
-  // scales, then the weight chunks in the order they are multiplied.
-  // 1. activation codes: wave instruction q covers 1 KB of row q / ks, piece
-  //    q % ks; lanes past k re-read the row's last 16 bytes (never used)
-  for (int q = wave; q < m * ks; q += nwaves) {
-    const int r = q / ks, c = q - r * ks;
-    const int off = min(1024 * c + 16 * lane, k - 16);
-    dma_lds16(aq + (int64_t)r * k + off, sA + r * lda + 1024 * c);
-  }
-  // 2. activation scales, four per thread (a loop after the barrier's wait
-  //    takes any beyond that)
-  const int scales = m * nbk;
-  uint16_t h[4];
+  // Each wave stages the activation rows and scales of its own K part; the
+  // waves of the other groups with the same part write the same bytes to the
+  // same places, so no wave waits for another before it multiplies.  Issue
+  // order matters (loads retire in order): the activation codes (L2, straight
+  // to LDS, invisible to the compiler), their scales, the weight scales, then
+  // the weight chunks in the order they are multiplied.
+  // 1. activation codes: row r, bytes [1024 part + 16 lane, +16) (lanes past
+  //    k re-read the row's last 16 bytes, never used)
+  const int aoff = min(1024 * part + 16 * lane, k - 16);
+  for (int r = 0; r < m; ++r) dma_lds16(aq + (int64_t)r * k + aoff, sA + r * lda + 1024 * part);
+  // 2. activation scales of the part: value c = lane + 64 u is row c / 32,
+  //    block c % 32 (past m or the part: re-read a valid one, not stored)
+  uint16_t h[8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) h[u] = ad[min(tid + u * nthreads, scales - 1)];
+  for (int u = 0; u < 8; ++u) {
+    const int c = lane + 64 * u, i = c >> 5, b = c & 31;
+    h[u] = ad[(int64_t)min(i, m - 1) * nbk + pb0 + min(b, pb - 1)];
+  }
   __asm__ volatile("" ::: "memory");
   // 3. weight scales of the part as dwords: instruction i, lane l -> row
   //    4 i + l / 16, blocks 2 (l % 16), 2 (l % 16) + 1 (past the part: its
@@ -573,32 +576,33 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
     dw2[i] = *reinterpret_cast<const uint32_t *>(wd + (int64_t)row * nbk + b);
   }
   // 4. the weight chunks (HBM): pair p = rows n0 + (l & 7) and n0 + 8 + (l & 7),
-  //    bytes 128 p + 16 (l >> 3) of the part (lanes past k: the row's last 16)
+  //    bytes 128 p + 16 (l >> 3) of the part (lanes past k: the row's last 16).
+  //    The first MF_DEPTH pairs now, each later one once the pair MF_DEPTH
+  //    before it has been multiplied: a wave that issued all of its chunks
+  //    at once would see its last one arrive only at the end of the whole
+  //    stream (its lines sit at every depth of every channel's queue), and
+  //    its multiplications would all fall after the stream.
   const int woff = QK * pb0 + 16 * (lane >> 3);
   const int8_t *wr0 = wq + (int64_t)min(n0 + (lane & 7), n - 1) * k;
   const int8_t *wr1 = wq + (int64_t)min(n0 + 8 + (lane & 7), n - 1) * k;
   i32x4 w[16];
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
+  auto load_pair = [&](int p) {
     const int off = min(woff + 128 * p, k - 16);
     w[2 * p] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(wr0 + off));
     w[2 * p + 1] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(wr1 + off));
-  }
-  __asm__ volatile("" ::: "memory");
-  // the 20 loads above are the only ones issued after the scales (2.), so
-  // this waits for the scales and the activation codes but not the weights
-  wait_vmcnt<20>();
+  };
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int c = tid + u * nthreads;
-    const int i = c / nbk, b = c - i * nbk;
-    if (c < scales) sD[b * 16 + i] = half_bits_to_float(h[u]);
+  for (int p = 0; p < MF_DEPTH; ++p) load_pair(p);
+  __asm__ volatile("" ::: "memory");
+  // the loads above are the only ones issued after the scales (2.), so this
+  // waits for the scales and the activation codes but not the weights
+  wait_vmcnt<4 + 2 * MF_DEPTH>();
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int c = lane + 64 * u, i = c >> 5, b = c & 31;
+    // blocks past the part are zeros (the last part reads whole chunks)
+    if (i < m) sD[(pb0 + b) * 16 + i] = b < pb ? half_bits_to_float(h[u]) : 0.0f;
   }
-  for (int c = tid + 4 * nthreads; c < scales; c += nthreads) {
-    const int i = c / nbk, b = c - i * nbk;
-    sD[b * 16 + i] = half_bits_to_float(ad[c]);
-  }
-  for (int c = tid; c < 32 * 16; c += nthreads) sD[nbk * 16 + c] = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const bool in_part = 2 * l16 < pb;
@@ -607,7 +611,10 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
     v.y = in_part ? half_bits_to_float((uint16_t)(dw2[i] >> 16)) : 0.0f;
     *reinterpret_cast<float2 *>(slotD + (4 * i + g) * MF_DSTRIDE + 8 * l16) = v;
   }
-  lds_barrier();  // the stages are complete; the weight loads stay in flight
+  // the LDS operations of one wave complete in program order: the reads
+  // below see this wave's stores and direct loads (other waves' stores of
+  // the same values may land at any time)
+  __asm__ volatile("" ::: "memory");
 
   const i32x4 seed = {MAGIC_BITS, MAGIC_BITS, MAGIC_BITS, MAGIC_BITS};
   const int8_t *arow = sA + min(l16, m - 1) * lda + QK * pb0 + 8 * g;
@@ -663,6 +670,11 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
         acc[2] = fmaf(fmaf(bits_to_float(dd[2]), dw, ncd), da.z, acc[2]);
         acc[3] = fmaf(fmaf(bits_to_float(dd[3]), dw, ncd), da.w, acc[3]);
       }
+    }
+    if (p + MF_DEPTH < 8) {
+      __asm__ volatile("" ::: "memory");
+      load_pair(p + MF_DEPTH);
+      __asm__ volatile("" ::: "memory");
     }
   }
 
