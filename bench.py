@@ -287,7 +287,8 @@ def bench_decode_variants(bqi, torch, W, iters):
         T = Timer(torch)
         # the API step (one launch for m = 1 only; here quantize + GEMV)
         step = lambda i: bqi.quantize_qgemm_q8_0(x, wq[i % copies], wd[i % copies], y, aq, ad)
-        kernel = "k_quantize_q8_0 + k_gemv_reg<%d,4,ACT_Q8>" % s.m
+        gemv = "k_gemv_mfma16" if s.m > 4 else "k_gemv_reg<%d,4,ACT_Q8>" % s.m
+        kernel = "k_quantize_q8_0 + " + gemv
         ms_step = T.loop(step, iters, check=lambda: y)
         ms_gemv = T.loop(lambda i: bqi.qgemm_q8_0(aq, ad, wq[i % copies], wd[i % copies], y), iters,
                          check=lambda: y)
@@ -300,9 +301,11 @@ def bench_decode_variants(bqi, torch, W, iters):
                     "ms_per_step": round(ms_step, 6),
                     "frac_hbm_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                     "bytes_per_step": step_bytes,
-                    "gemv_only": {"mean_launch_us": round(ms_gemv * 1e3, 3),
+                    "gemv_only": {"kernel": gemv, "mean_launch_us": round(ms_gemv * 1e3, 3),
                                   "GB/s": round(gemv_bytes / (ms_gemv * 1e-3) / 1e9, 1),
-                                  "frac_hbm_peak": round(gemv_bytes / (ms_gemv * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}})
+                                  "frac_hbm_peak": round(gemv_bytes / (ms_gemv * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "algorithmic_bytes": gemv_bytes,
+                                  "hbm_bytes_measured": traffic("%s decode M=%d" % (gemv.split("<")[0], s.m))}})
     return res
 
 
