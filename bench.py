@@ -69,12 +69,16 @@ def log(msg):
     sys.stderr.flush()
 
 
+WARM_S = 0.025  # untimed graph replays before each timed one
+
+
 class Timer:
     """Mean duration per launch from HIP events recorded on the launch stream
     around a timed region of back-to-back launches.  Launch-bound loops are
     captured once in a HIP graph (torch.cuda.CUDAGraph) and replayed, so the
     figure is GPU time, not Python launch overhead; every graph is first
-    replayed against an eager run and its output compared bit for bit."""
+    replayed against an eager run and its output compared bit for bit, then
+    replayed untimed for WARM_S seconds before the one timed replay."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -110,6 +114,12 @@ class Timer:
             torch.cuda.synchronize()
             if check is not None and not torch.equal(check(), ref):
                 raise RuntimeError("graph replay %d differs from the eager result" % rep)
+        # untimed replays until the GPU has been busy for WARM_S (its clocks
+        # ramp over the first ~15 ms of load in a fresh process)
+        t0 = time.time()
+        while time.time() - t0 < WARM_S:
+            g.replay()
+            torch.cuda.synchronize()
         a.record()
         g.replay()
         b.record()
@@ -248,7 +258,9 @@ def bench_headline(bqi, torch, W, args):
                      "bytes_per_launch": step_bytes,
                      "mean_launch_us": round(ms_step * 1e3, 3),
                      "timing": "HIP events around %d back-to-back launches replayed "
-                               "from a HIP graph" % args.steps},
+                               "from a HIP graph, after %d eager warm-up steps and "
+                               "%.0f ms of untimed replays" % (args.steps, args.warmup,
+                                                              WARM_S * 1e3)},
         "eager_ms_per_step": round(ms_step_eager, 6),
         "two_call_step": {"calls": "quantize_q8_0 + qgemm_q8_0", "ms_per_step": round(ms_two, 6),
                           "GB/s": round(step_bytes / (ms_two * 1e-3) / 1e9, 2)},
