@@ -32,31 +32,52 @@ __device__ __forceinline__ int32_t dot4_i8(int32_t a, int32_t b, int32_t c) {
   return __builtin_amdgcn_sdot4(a, b, c, false);
 }
 
+// max(v, v of the lane that the DPP control CTRL selects)
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                      __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false)));
+}
+
 // Q8_0 quantization of one 32-element block by the 8 consecutive lanes that
 // own it (lane sub = lane % 8 holds elements 4*sub .. 4*sub+3 in v): the
 // block's absmax is reduced across the 8 lanes, d = fp16_rne(amax / 127)
 // with a correctly rounded fp32 division, and each code is
-// clamp(round-half-away(x / d), -127, 127) with the correctly rounded fp32
-// quotient by the stored d (d == 0 gives codes 0 and scale bits 0).  Returns
+// clamp(round-half-away(x / d), -127, 127) for the exact quotient by the
+// stored d (d == 0 gives codes 0 and scale bits 0).  Returns
 // this lane's 4 codes packed (element 4*sub + i in byte i) and sets the
 // block's scale bits.  Every quantizer in the library goes through this
 // function, so all of them produce identical codes.  Never compile with
 // fast-math.
 __device__ __forceinline__ uint32_t q8_0_quantize4(const float (&v)[4], uint16_t &d_bits) {
   float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-  // reduce over the 8 lanes of this block (lanes differ in bits 0..2)
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-  amax = fmaxf(amax, __shfl_xor(amax, 2));
-  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  // reduce over the 8 lanes of this block (lanes differ in bits 0..2) with
+  // DPP moves, no LDS round trip: lane ^ 1 and lane ^ 2 (quad permutations),
+  // then the mirror inside each 8-lane half-row, which pairs every lane of
+  // one quad with a lane of the other
+  amax = dpp_max<0xb1>(amax);   // quad_perm [1, 0, 3, 2]
+  amax = dpp_max<0x4e>(amax);   // quad_perm [2, 3, 0, 1]
+  amax = dpp_max<0x141>(amax);  // row_half_mirror
   const _Float16 dh = (_Float16)(amax / 127.0f);  // IEEE div, then RNE
   const float dd = (float)dh;
   uint32_t packed = 0;
   if (dd != 0.0f) {
+    // The code is round-half-away(|x| / d) with the sign of x, taken from the
+    // exact quotient without a division: a candidate k from an approximate
+    // reciprocal (relative error ~2^-22, so k is off by at most one for
+    // |x| / d < 2^20), then corrected with the exact signs of
+    // |x| - (k -/+ 1/2) d: (k +/- 1/2) d has at most 9 + 11 significant bits,
+    // so it is exact in fp32, and the fma rounds the difference once, which
+    // keeps its sign.  |x| = (k + 1/2) d exactly (a tie) rounds up.
+    const float r = __builtin_amdgcn_rcpf(dd);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float t = roundf(v[i] / dd);  // half away from zero
-      t = fminf(fmaxf(t, -127.0f), 127.0f);
-      packed |= ((uint32_t)(int32_t)t & 0xffu) << (8 * i);
+      const float ax = fabsf(v[i]);
+      float k = floorf(fmaf(ax, r, 0.5f));
+      if (fmaf(-(k - 0.5f), dd, ax) < 0.0f) k -= 1.0f;
+      if (fmaf(-(k + 0.5f), dd, ax) >= 0.0f) k += 1.0f;
+      const int32_t q = (int32_t)fminf(k, 127.0f);
+      packed |= ((uint32_t)(v[i] < 0.0f ? -q : q) & 0xffu) << (8 * i);
     }
   }
   d_bits = dd != 0.0f ? __builtin_bit_cast(uint16_t, dh) : (uint16_t)0;

@@ -12,11 +12,12 @@
 // Exactness: d = fp16_rne(amax / 127) uses HIP's correctly rounded fp32
 // division followed by the RNE conversion (equal to rounding the exact
 // quotient, because a correctly rounded fp32 quotient can never land on an
-// fp16 rounding midpoint it did not start on).  Codes use the correctly
-// rounded fp32 quotient x / d and round-half-away-from-zero; for |x| <= 2^24
-// ulps of d this decides the same integer as the exact rational quotient,
-// because a non-tie quotient is at least one fp32 half-ulp away from every
-// k + 1/2.  This file must not be compiled with fast-math.
+// fp16 rounding midpoint it did not start on).  Codes round the exact
+// quotient |x| / d half away from zero without dividing: a candidate from an
+// approximate reciprocal is corrected by the exact signs of
+// |x| - (k -/+ 1/2) d (the product is exact in fp32 and the fma rounds the
+// difference once).  The 8-lane absmax reduction runs on DPP moves.  This
+// file must not be compiled with fast-math.
 #include "bqi_device.h"
 #include "bqi_launch.h"
 

@@ -125,6 +125,33 @@ def test_quantize_fp16_input_and_ldx():
     assert np.array_equal(host(qg), qr) and np.array_equal(host(dg), dr)
 
 
+def test_quantize_ties_dense_closed_form():
+    """Codes at and next to every rounding midpoint, against the definition
+    itself (no oracle): element 0 of each block is 127 d, which makes the
+    block's scale exactly d; every other element is +-(k + 1/2) d (exact in
+    fp32: at most 8 + 11 significant bits) or its fp32 neighbour on either
+    side.  Round half away from zero gives +-(k + 1) at and above the
+    midpoint and +-k below it."""
+    g = np.random.default_rng(31)
+    dbits = np.arange(0x0400, 0x7800, 7, dtype=np.uint16)        # normal fp16 scales
+    d = dbits.view(np.float16).astype(np.float32)
+    nb = d.size
+    k = g.integers(0, 127, size=(nb, 31))
+    side = g.integers(0, 3, size=(nb, 31))                         # 0 below, 1 tie, 2 above
+    sign = g.choice(np.array([-1.0, 1.0], np.float32), size=(nb, 31))
+    mid = ((k + 0.5) * d[:, None]).astype(np.float32)
+    assert np.array_equal(mid.astype(np.float64), (k + 0.5) * d[:, None].astype(np.float64))
+    x = np.where(side == 0, np.nextafter(mid, np.float32(0)),
+                 np.where(side == 2, np.nextafter(mid, np.float32(np.inf)), mid))
+    want = np.where(side == 0, k, k + 1) * sign
+    blocks = np.concatenate([(np.float32(127) * d)[:, None], (x * sign).astype(np.float32)], 1)
+    qg, dg = bqi.quantize_q8_0(dev_tensor(blocks.astype(np.float32)))
+    qg, dg = host(qg), host(dg)
+    assert np.array_equal(dg.reshape(-1).astype(np.uint16), dbits)
+    assert (qg[:, 0] == 127).all()
+    assert np.array_equal(qg[:, 1:].astype(np.int64), want.astype(np.int64))
+
+
 def test_quantize_special_blocks():
     x = np.zeros((5, 64), np.float32)
     x[1] = -0.0
