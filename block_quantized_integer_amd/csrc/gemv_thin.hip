@@ -524,11 +524,23 @@ __device__ __forceinline__ long mf_pair(uint32_t lo, uint32_t hi) {
   return (long)(((uint64_t)hi << 32) | lo);
 }
 
+// RG groups of 16 weight rows per wave (the activation fragments and scales of
+// a block serve RG MFMAs, and each wave's staging serves 16 RG rows); a
+// workgroup has up to MF_WAVES waves (RG = 1: several row sets of ks waves;
+// RG = 3: one row set, ks waves).
+
 // (no __restrict__ on the inputs: with it the compiler may move loads across
 // the compiler barriers that fix their issue order)
+template <int RG>
 __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
     const int8_t *aq, const uint16_t *ad, int m, const int8_t *wq,
     const uint16_t *wd, int n, int k, int ks, float *y) {
+  // weight load pairs in flight per wave: MF_DEPTH for RG = 1 (12 waves per
+  // CU); two whole chunks (six pairs) for RG = 3, one wave per SIMD
+  // (measured: four pairs, which split a chunk, 14.1 us at m = 16; six 11.9;
+  // nine 12.1; twelve 12.4)
+  constexpr int DEPTH = RG == 1 ? MF_DEPTH : 2 * RG;
+  constexpr int NPAIR = 8 * RG;  // pair q = chunk q / RG, row group q % RG
   extern __shared__ __attribute__((aligned(16))) int8_t mf_lds[];
   const int nbk = k / QK;
   const int lda = (int)mf_lda(k);
@@ -539,10 +551,10 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int nwaves = nthreads >> 6, groups = nwaves / ks;
   // the weight scales of the part as fp32, zero past the part
-  int8_t *slotD = mf_lds + 16 * lda + (nbk + 32) * 64 + wave * MF_SLOT;  // [16][MF_DSTRIDE]
+  int8_t *slotD = mf_lds + 16 * lda + (nbk + 32) * 64 + wave * (RG * MF_SLOT);  // [16 RG][MF_DSTRIDE]
   const int grp = wave / ks, part = wave - grp * ks;
   const int l16 = lane & 15, g = lane >> 4;
-  const int n0 = ((int)blockIdx.x * groups + grp) * 16;
+  const int n0 = ((int)blockIdx.x * groups + grp) * 16 * RG;
   const int pb0 = 32 * part;              // first block of this K part
   const int pb = min(32, nbk - pb0);      // blocks in it (even: k % 64 == 0)
 
@@ -565,38 +577,46 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
     h[u] = ad[(int64_t)min(i, m - 1) * nbk + pb0 + min(b, pb - 1)];
   }
   __asm__ volatile("" ::: "memory");
-  // 3. weight scales of the part as dwords: instruction i, lane l -> row
-  //    4 i + l / 16, blocks 2 (l % 16), 2 (l % 16) + 1 (past the part: its
-  //    last pair; rows past n: row n - 1)
-  uint32_t dw2[4];
+  // 3. weight scales of the part as dwords: instruction (j, i), lane l -> row
+  //    16 j + 4 i + l / 16, blocks 2 (l % 16), 2 (l % 16) + 1 (past the part:
+  //    its last pair; rows past n: row n - 1)
+  uint32_t dw2[RG][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = min(n0 + 4 * i + g, n - 1);
-    const int b = pb0 + min(2 * l16, pb - 2);
-    dw2[i] = *reinterpret_cast<const uint32_t *>(wd + (int64_t)row * nbk + b);
-  }
-  // 4. the weight chunks (HBM): pair p = rows n0 + (l & 7) and n0 + 8 + (l & 7),
-  //    bytes 128 p + 16 (l >> 3) of the part (lanes past k: the row's last 16).
-  //    The first MF_DEPTH pairs now, each later one once the pair MF_DEPTH
-  //    before it has been multiplied: a wave that issued all of its chunks
-  //    at once would see its last one arrive only at the end of the whole
-  //    stream (its lines sit at every depth of every channel's queue), and
-  //    its multiplications would all fall after the stream.
+  for (int j = 0; j < RG; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = min(n0 + 16 * j + 4 * i + g, n - 1);
+      const int b = pb0 + min(2 * l16, pb - 2);
+      dw2[j][i] = *reinterpret_cast<const uint32_t *>(wd + (int64_t)row * nbk + b);
+    }
+  // 4. the weight chunks (HBM): pair q = (chunk p, group j) is rows
+  //    n0 + 16 j + (l & 7) and n0 + 16 j + 8 + (l & 7), bytes 128 p + 16 (l >> 3)
+  //    of the part (lanes past k: the row's last 16).  The first DEPTH pairs
+  //    now, each later one once the pair DEPTH before it has been multiplied:
+  //    a wave that issued all of its chunks at once would see its last one
+  //    arrive only at the end of the whole stream (its lines sit at every
+  //    depth of every channel's queue), and its multiplications would all
+  //    fall after the stream.
   const int woff = QK * pb0 + 16 * (lane >> 3);
-  const int8_t *wr0 = wq + (int64_t)min(n0 + (lane & 7), n - 1) * k;
-  const int8_t *wr1 = wq + (int64_t)min(n0 + 8 + (lane & 7), n - 1) * k;
-  i32x4 w[16];
-  auto load_pair = [&](int p) {
+  const int8_t *wr[RG][2];
+#pragma unroll
+  for (int j = 0; j < RG; ++j) {
+    wr[j][0] = wq + (int64_t)min(n0 + 16 * j + (lane & 7), n - 1) * k;
+    wr[j][1] = wq + (int64_t)min(n0 + 16 * j + 8 + (lane & 7), n - 1) * k;
+  }
+  i32x4 w[NPAIR][2];
+  auto load_pair = [&](int q) {
+    const int p = q / RG, j = q % RG;
     const int off = min(woff + 128 * p, k - 16);
-    w[2 * p] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(wr0 + off));
-    w[2 * p + 1] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(wr1 + off));
+    w[q][0] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(wr[j][0] + off));
+    w[q][1] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(wr[j][1] + off));
   };
 #pragma unroll
-  for (int p = 0; p < MF_DEPTH; ++p) load_pair(p);
+  for (int q = 0; q < DEPTH; ++q) load_pair(q);
   __asm__ volatile("" ::: "memory");
   // the loads above are the only ones issued after the scales (2.), so this
   // waits for the scales and the activation codes but not the weights
-  wait_vmcnt<4 + 2 * MF_DEPTH>();
+  wait_vmcnt<4 * RG + 2 * DEPTH>();
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int c = lane + 64 * u, i = c >> 5, b = c & 31;
@@ -604,13 +624,15 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
     if (i < m) sD[(pb0 + b) * 16 + i] = b < pb ? half_bits_to_float(h[u]) : 0.0f;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bool in_part = 2 * l16 < pb;
-    float2 v;
-    v.x = in_part ? half_bits_to_float((uint16_t)(dw2[i] & 0xffffu)) : 0.0f;
-    v.y = in_part ? half_bits_to_float((uint16_t)(dw2[i] >> 16)) : 0.0f;
-    *reinterpret_cast<float2 *>(slotD + (4 * i + g) * MF_DSTRIDE + 8 * l16) = v;
-  }
+  for (int j = 0; j < RG; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool in_part = 2 * l16 < pb;
+      float2 v;
+      v.x = in_part ? half_bits_to_float((uint16_t)(dw2[j][i] & 0xffffu)) : 0.0f;
+      v.y = in_part ? half_bits_to_float((uint16_t)(dw2[j][i] >> 16)) : 0.0f;
+      *reinterpret_cast<float2 *>(slotD + (16 * j + 4 * i + g) * MF_DSTRIDE + 8 * l16) = v;
+    }
   // the LDS operations of one wave complete in program order: the reads
   // below see this wave's stores and direct loads (other waves' stores of
   // the same values may land at any time)
@@ -619,119 +641,167 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
   const i32x4 seed = {MAGIC_BITS, MAGIC_BITS, MAGIC_BITS, MAGIC_BITS};
   const int8_t *arow = sA + min(l16, m - 1) * lda + QK * pb0 + 8 * g;
   const float *sDrow = sD + pb0 * 16 + 4 * g;
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acc[RG][4];
+#pragma unroll
+  for (int j = 0; j < RG; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[j][r] = 0.0f;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     if (4 * p < pb) {  // uniform
-      // 1. lane (row l % 16, q): block q of chunk p, bytes 0..15 and 16..31.
-      //    Lanes 8..15 of a row (DPP banks 2, 3) take bytes 0..15 of their
-      //    row from the second load of lane l ^ 8; lanes 0..7 (banks 0, 1)
-      //    take bytes 16..31 from the first load of lane l ^ 8.
-      uint32_t lo[4], hi[4];
+      long wf[RG][4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int a = w[2 * p][d], b = w[2 * p + 1][d];
-        lo[d] = (uint32_t)__builtin_amdgcn_update_dpp(a, b, 0x128, 0xf, 0xc, false);
-        hi[d] = (uint32_t)__builtin_amdgcn_update_dpp(b, a, 0x128, 0xf, 0x3, false);
-      }
-      // 2. the 4 x 4 transpose of 8-byte pieces: pieces 0..3 are
-      //    (lo0, lo1), (lo2, lo3), (hi0, hi1), (hi2, hi3)
+      for (int j = 0; j < RG; ++j) {
+        const int q = p * RG + j;
+        // 1. lane (row l % 16, q'): block q' of chunk p, bytes 0..15 and
+        //    16..31.  Lanes 8..15 of a row (DPP banks 2, 3) take bytes 0..15
+        //    of their row from the second load of lane l ^ 8; lanes 0..7
+        //    (banks 0, 1) take bytes 16..31 from the first load of lane l ^ 8.
+        uint32_t lo[4], hi[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const auto r = __builtin_amdgcn_permlane32_swap(lo[d], hi[d], false, false);
-        lo[d] = r[0];
-        hi[d] = r[1];
-      }
+        for (int d = 0; d < 4; ++d) {
+          const int a = w[q][0][d], b = w[q][1][d];
+          lo[d] = (uint32_t)__builtin_amdgcn_update_dpp(a, b, 0x128, 0xf, 0xc, false);
+          hi[d] = (uint32_t)__builtin_amdgcn_update_dpp(b, a, 0x128, 0xf, 0x3, false);
+        }
+        // 2. the 4 x 4 transpose of 8-byte pieces: pieces 0..3 are
+        //    (lo0, lo1), (lo2, lo3), (hi0, hi1), (hi2, hi3)
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const auto r = __builtin_amdgcn_permlane16_swap(lo[d], lo[d + 2], false, false);
-        lo[d] = r[0];
-        lo[d + 2] = r[1];
-        const auto s = __builtin_amdgcn_permlane16_swap(hi[d], hi[d + 2], false, false);
-        hi[d] = s[0];
-        hi[d + 2] = s[1];
+        for (int d = 0; d < 4; ++d) {
+          const auto r = __builtin_amdgcn_permlane32_swap(lo[d], hi[d], false, false);
+          lo[d] = r[0];
+          hi[d] = r[1];
+        }
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const auto r = __builtin_amdgcn_permlane16_swap(lo[d], lo[d + 2], false, false);
+          lo[d] = r[0];
+          lo[d + 2] = r[1];
+          const auto s = __builtin_amdgcn_permlane16_swap(hi[d], hi[d + 2], false, false);
+          hi[d] = s[0];
+          hi[d + 2] = s[1];
+        }
+        wf[j][0] = mf_pair(lo[0], lo[1]);
+        wf[j][1] = mf_pair(lo[2], lo[3]);
+        wf[j][2] = mf_pair(hi[0], hi[1]);
+        wf[j][3] = mf_pair(hi[2], hi[3]);
       }
-      const long wf[4] = {mf_pair(lo[0], lo[1]), mf_pair(lo[2], lo[3]),
-                          mf_pair(hi[0], hi[1]), mf_pair(hi[2], hi[3])};
-      // the four blocks' weight scales of row l % 16; blocks past the part
-      // (its last chunk only) have a zero scale, which adds exactly nothing,
-      // and their reads stay inside the stages
-      const f32x4 dsc = *reinterpret_cast<const f32x4 *>(slotD + l16 * MF_DSTRIDE + 16 * p);
+      // the four blocks' weight scales of row 16 j + l % 16; blocks past the
+      // part (its last chunk only) have a zero scale, which adds exactly
+      // nothing, and their reads stay inside the stages
+      f32x4 dsc[RG];
+#pragma unroll
+      for (int j = 0; j < RG; ++j)
+        dsc[j] = *reinterpret_cast<const f32x4 *>(slotD + (16 * j + l16) * MF_DSTRIDE + 16 * p);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int b = 4 * p + e;  // block within the part
         const long a = *reinterpret_cast<const long *>(arow + QK * b);
         const f32x4 da = *reinterpret_cast<const f32x4 *>(sDrow + b * 16);
-        const i32x4 dd = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, wf[e], seed, 0, 0, 0);
-        const float dw = dsc[e];
-        const float ncd = -MAGIC_F * dw;  // exact
-        acc[0] = fmaf(fmaf(bits_to_float(dd[0]), dw, ncd), da.x, acc[0]);
-        acc[1] = fmaf(fmaf(bits_to_float(dd[1]), dw, ncd), da.y, acc[1]);
-        acc[2] = fmaf(fmaf(bits_to_float(dd[2]), dw, ncd), da.z, acc[2]);
-        acc[3] = fmaf(fmaf(bits_to_float(dd[3]), dw, ncd), da.w, acc[3]);
+#pragma unroll
+        for (int j = 0; j < RG; ++j) {
+          const i32x4 dd = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, wf[j][e], seed, 0, 0, 0);
+          const float dw = dsc[j][e];
+          const float ncd = -MAGIC_F * dw;  // exact
+          acc[j][0] = fmaf(fmaf(bits_to_float(dd[0]), dw, ncd), da.x, acc[j][0]);
+          acc[j][1] = fmaf(fmaf(bits_to_float(dd[1]), dw, ncd), da.y, acc[j][1]);
+          acc[j][2] = fmaf(fmaf(bits_to_float(dd[2]), dw, ncd), da.z, acc[j][2]);
+          acc[j][3] = fmaf(fmaf(bits_to_float(dd[3]), dw, ncd), da.w, acc[j][3]);
+        }
       }
     }
-    if (p + MF_DEPTH < 8) {
-      __asm__ volatile("" ::: "memory");
-      load_pair(p + MF_DEPTH);
-      __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+      const int q = p * RG + j + DEPTH;
+      if (q < NPAIR) {
+        __asm__ volatile("" ::: "memory");
+        load_pair(q);
+        __asm__ volatile("" ::: "memory");
+      }
     }
   }
 
   // 5. the K parts of each group, added in order through LDS, then stored
   lds_barrier();  // every wave is done reading the stage
-  float *red = reinterpret_cast<float *>(mf_lds);  // [group][part 1..][4][64]
+  float *red = reinterpret_cast<float *>(mf_lds);  // [group][part 1..][RG][4][64]
   if (part > 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[((grp * (ks - 1) + part - 1) * 4 + r) * 64 + lane] = acc[r];
+    for (int j = 0; j < RG; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        red[(((grp * (ks - 1) + part - 1) * RG + j) * 4 + r) * 64 + lane] = acc[j][r];
   }
   lds_barrier();
   if (part > 0) return;
-  for (int p = 1; p < ks; ++p)
+  for (int pp = 1; pp < ks; ++pp)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] += red[((grp * (ks - 1) + p - 1) * 4 + r) * 64 + lane];
-  const int col = n0 + l16;
-  if (col < n) {
+    for (int j = 0; j < RG; ++j)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * g + r;
-      if (row < m) y[(int64_t)row * n + col] = acc[r];
+      for (int r = 0; r < 4; ++r)
+        acc[j][r] += red[(((grp * (ks - 1) + pp - 1) * RG + j) * 4 + r) * 64 + lane];
+#pragma unroll
+  for (int j = 0; j < RG; ++j) {
+    const int col = n0 + 16 * j + l16;
+    if (col < n) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * g + r;
+        if (row < m) y[(int64_t)row * n + col] = acc[j][r];
+      }
     }
   }
 }
 
-// Workgroup shape of the MFMA kernel: ks = ceil(k / 1 KB) waves per group and
-// as many groups as fit MF_WAVES waves and the LDS, but no more than keep one
-// workgroup per CU for the row groups there are.  Returns false when even one
-// group does not fit (the caller then takes the register kernel).
-bool mf_shape(int64_t n, int64_t k, int *ks_out, int *groups_out) {
+// Workgroup shape of the MFMA kernel: ks = ceil(k / 1 KB) waves per row set.
+// When the 16-row groups fill at least 256 workgroups of three groups per
+// wave (RG = 3, ks waves), that shape; otherwise RG = 1 with as many groups
+// per workgroup as fit MF_WAVES waves and the LDS, but no more than keep one
+// workgroup per CU.  Returns false when even one group does not fit (the
+// caller then takes the register kernel).
+struct MfShape {
+  int ks, groups, rg;
+};
+bool mf_shape(int64_t n, int64_t k, MfShape *out) {
   const int64_t ks = (k + 1023) / 1024;
   if (k % 64 != 0 || ks > MF_WAVES) return false;
   const int64_t row_groups = (n + 15) / 16;
+  if (row_groups >= 3 * 256 && mf_lds_bytes(k, ks * 3) <= MF_LDS_MAX) {
+    *out = MfShape{(int)ks, 1, 3};
+    return true;
+  }
   int64_t groups = std::max<int64_t>(1, std::min<int64_t>(MF_WAVES / ks, row_groups / 256));
   while (groups > 1 && mf_lds_bytes(k, groups * ks) > MF_LDS_MAX) --groups;
   if (mf_lds_bytes(k, groups * ks) > MF_LDS_MAX) return false;
-  *ks_out = (int)ks;
-  *groups_out = (int)groups;
+  *out = MfShape{(int)ks, (int)groups, 1};
   return true;
 }
 
-hipError_t launch_mfma16(const int8_t *aq, const uint16_t *ad, int64_t m,
-                         const int8_t *wq, const uint16_t *wd, int64_t n, int64_t k,
-                         int ks, int groups, float *y, hipStream_t stream) {
-  const int64_t lds = mf_lds_bytes(k, (int64_t)ks * groups);
+template <int RG>
+hipError_t launch_mfma16_rg(const int8_t *aq, const uint16_t *ad, int64_t m,
+                            const int8_t *wq, const uint16_t *wd, int64_t n, int64_t k,
+                            const MfShape &sh, float *y, hipStream_t stream) {
+  // LDS: the stages plus one weight-scale slot per row group of every wave
+  const int64_t lds = mf_lds_bytes(k, (int64_t)sh.ks * sh.groups * RG);
   static bool raised = false;
   if (lds > 65536 && !raised) {
-    const hipError_t e = hipFuncSetAttribute((const void *)k_gemv_mfma16,
+    const hipError_t e = hipFuncSetAttribute((const void *)k_gemv_mfma16<RG>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)MF_LDS_MAX);
     if (e != hipSuccess) return e;
     raised = true;
   }
-  const int64_t wgs = (n + 16 * groups - 1) / (16 * groups);
-  hipLaunchKernelGGL(k_gemv_mfma16, dim3((unsigned)wgs), dim3(64 * ks * groups), (unsigned)lds,
-                     stream, aq, ad, (int)m, wq, wd, (int)n, (int)k, ks, y);
+  const int64_t rows_per_wg = 16 * RG * sh.groups;
+  const int64_t wgs = (n + rows_per_wg - 1) / rows_per_wg;
+  hipLaunchKernelGGL(k_gemv_mfma16<RG>, dim3((unsigned)wgs), dim3(64 * sh.ks * sh.groups),
+                     (unsigned)lds, stream, aq, ad, (int)m, wq, wd, (int)n, (int)k, sh.ks, y);
   return hipGetLastError();
+}
+
+hipError_t launch_mfma16(const int8_t *aq, const uint16_t *ad, int64_t m,
+                         const int8_t *wq, const uint16_t *wd, int64_t n, int64_t k,
+                         const MfShape &sh, float *y, hipStream_t stream) {
+  if (sh.rg == 3) return launch_mfma16_rg<3>(aq, ad, m, wq, wd, n, k, sh, y, stream);
+  return launch_mfma16_rg<1>(aq, ad, m, wq, wd, n, k, sh, y, stream);
 }
 }  // namespace
 
@@ -740,9 +810,9 @@ hipError_t launch_gemv_thin(const int8_t *aq, const uint16_t *ad, int64_t m,
                             int64_t k, float *y, hipStream_t stream) {
   // more than 4 rows: int8 MFMA while its stages fit (k a multiple of 64 and
   // wd 4-byte aligned: the weight scales load in aligned pairs)
-  int ks = 0, groups = 0;
-  if (m > 4 && ((uintptr_t)wd & 3) == 0 && mf_shape(n, k, &ks, &groups))
-    return launch_mfma16(aq, ad, m, wq, wd, n, k, ks, groups, y, stream);
+  MfShape sh;
+  if (m > 4 && ((uintptr_t)wd & 3) == 0 && mf_shape(n, k, &sh))
+    return launch_mfma16(aq, ad, m, wq, wd, n, k, sh, y, stream);
   // otherwise the register kernel while the m rows of codes fit its LDS stage
   const int64_t ch = pow2_ceil((k + 1023) / 1024);
   const int64_t mt = pow2_ceil(m);

@@ -176,7 +176,10 @@ SHAPES = [(1, 32, 1), (1, 96, 33), (2, 64, 100), (3, 160, 77), (4, 256, 512), (5
           # thin-M MFMA kernel: a last K part of two blocks, one part of two
           # blocks, five and six parts, two row groups per workgroup with a
           # ragged last workgroup
-          (6, 1088, 70), (9, 64, 3000), (7, 5120, 50), (16, 6144, 33), (12, 2048, 8200)]
+          (6, 1088, 70), (9, 64, 3000), (7, 5120, 50), (16, 6144, 33), (12, 2048, 8200),
+          # three row groups per wave (12288 rows and more), ragged last
+          # workgroup, one, two and five K parts
+          (16, 64, 12290), (7, 1088, 12300), (5, 5120, 12320)]
 
 
 @pytest.mark.parametrize("m,k,n", SHAPES)
