@@ -179,7 +179,9 @@ SHAPES = [(1, 32, 1), (1, 96, 33), (2, 64, 100), (3, 160, 77), (4, 256, 512), (5
           (6, 1088, 70), (9, 64, 3000), (7, 5120, 50), (16, 6144, 33), (12, 2048, 8200),
           # three row groups per wave (12288 rows and more), ragged last
           # workgroup, one, two and five K parts
-          (16, 64, 12290), (7, 1088, 12300), (5, 5120, 12320)]
+          (16, 64, 12290), (7, 1088, 12300), (5, 5120, 12320),
+          # a single weight row and a partial 16-row group
+          (8, 2048, 1), (16, 4096, 7)]
 
 
 @pytest.mark.parametrize("m,k,n", SHAPES)
@@ -196,13 +198,13 @@ def test_qgemm_random_codes_full_range(m, k, n):
     assert_within_bound(y, yr, asum, k // 32, "m=%d k=%d n=%d" % (m, k, n))
 
 
-@pytest.mark.parametrize("m", [1, 5, 16, 40, 128])
-def test_block_dots_bitexact_probe(m):
+@pytest.mark.parametrize("m,n", [(1, 96), (5, 96), (16, 96), (40, 96), (128, 96), (16, 12288)])
+def test_block_dots_bitexact_probe(m, n):
     """One-hot-block probe: each activation row has codes only in block
     b = row % nb and all scales are powers of two, so y = 2^(ea+ew) * P_b is
     exact in fp32 and P_b can be read back and compared bit-exactly with the
     oracle's int32 block dot products."""
-    k, n = 256, 96
+    k = 256
     nb = k // 32
     aq = W.random_int8(0, 500 + m, (m, k), seed=1)
     mask = np.zeros((m, k), bool)
