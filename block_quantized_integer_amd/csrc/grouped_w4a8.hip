@@ -69,18 +69,38 @@ __device__ __forceinline__ int route_scan(int v, int *s_tmp, int &total) {
 
 // Copy the activation scales of this expert's `total` matched rows (routed
 // rows s_match[0 .. total)) into the block-major fp32 table at positions
-// base .. base+total-1.  Tiles of 64 rows x 64 groups go through LDS: each
-// wave reads whole 128-byte scale rows (coalesced), and writes 16 consecutive
-// positions of four table rows (coalesced), instead of scattering 2-byte
-// reads over every matched token per table row.
+// base .. base+total-1.  Tiles of up to 96 rows x 64 groups go through LDS:
+// each thread reads 8 consecutive scales of one row with one 16-byte load
+// (4 two-byte loads for 64-row tiles where the scale rows are not 16-byte
+// aligned), and each 16 threads write 16 consecutive positions of one table
+// row, instead of scattering 2-byte reads over every matched token per table
+// row.  An expert's rows rarely exceed 96, so its gather is one round trip.
+constexpr int RC_ROWS = 96;            // routed rows per tile (16-byte path)
+constexpr int RC_PITCH = RC_ROWS + 1;  // floats per group row of the tile
+
 __device__ __forceinline__ void route_copy_scales(const int *s_match, int total, int base,
                                                   int top_k, const uint16_t *ad,
                                                   int nbk, float *__restrict__ ad32t, int rpad,
-                                                  float (*s_t)[65]) {
+                                                  float *s_t) {
   const int tid = threadIdx.x;
-  for (int i0 = 0; i0 < total; i0 += 64) {
+  const bool vec = nbk % 8 == 0 && ((uintptr_t)ad & 15) == 0;
+  const int tile_rows = vec ? RC_ROWS : 64;
+  for (int i0 = 0; i0 < total; i0 += tile_rows) {
     for (int b0 = 0; b0 < nbk; b0 += 64) {
-      {
+      if (vec) {
+        // thread -> row i0 + tid/8, groups b0 + 8*(tid%8) .. +7
+        const int r = tid >> 3, c = 8 * (tid & 7);
+        const int i = i0 + r;
+        if (r < RC_ROWS && i < total && b0 + c < nbk) {
+          const uint4 v = *reinterpret_cast<const uint4 *>(ad + (int64_t)(s_match[i] / top_k) * nbk + b0 + c);
+          const uint32_t h2[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            s_t[(c + 2 * u) * RC_PITCH + r] = half_bits_to_float((uint16_t)(h2[u] & 0xffffu));
+            s_t[(c + 2 * u + 1) * RC_PITCH + r] = half_bits_to_float((uint16_t)(h2[u] >> 16));
+          }
+        }
+      } else {
         // thread -> row i0 + tid/16, groups b0 + 4*(tid%16) .. +3
         const int r = tid >> 4, c = 4 * (tid & 15);
         const int i = i0 + r;
@@ -94,7 +114,7 @@ __device__ __forceinline__ void route_copy_scales(const int *s_match, int total,
           __asm__ volatile("" ::: "memory");
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            if (b0 + c + u < nbk) s_t[c + u][r] = half_bits_to_float(h[u]);
+            if (b0 + c + u < nbk) s_t[(c + u) * RC_PITCH + r] = half_bits_to_float(h[u]);
         }
       }
       __syncthreads();
@@ -104,8 +124,9 @@ __device__ __forceinline__ void route_copy_scales(const int *s_match, int total,
         if (b0 + c < nbk) {
           float *dst = ad32t + (int64_t)(b0 + c) * rpad + base + i0;
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (i0 + r + 16 * u < total) dst[r + 16 * u] = s_t[c][r + 16 * u];
+          for (int u = 0; u < RC_ROWS / 16; ++u)
+            if (16 * u < tile_rows && i0 + r + 16 * u < total)
+              dst[r + 16 * u] = s_t[c * RC_PITCH + r + 16 * u];
         }
       }
       __syncthreads();
@@ -120,7 +141,7 @@ __global__ __launch_bounds__(RT) void k_route(
     float *__restrict__ ad32t, int rpad, float *__restrict__ y, int n) {
   __shared__ int s_tmp[RT / 64];
   __shared__ int s_match[RCHUNK];  // (position - chunk base) -> routed row
-  __shared__ float s_t[64][65];    // transpose tile of the scale copy
+  __shared__ float s_t[64 * RC_PITCH];  // transpose tile of the scale copy
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
 

@@ -415,7 +415,7 @@ def run_grouped(qa, da, ids, packed, wsc):
 
 
 @pytest.mark.parametrize("case", ["small", "invalid_and_dups", "one_hot_expert", "big_expert",
-                                  "single"])
+                                  "big_expert_wide", "single"])
 def test_grouped_w4a8_cases(case):
     g = np.random.default_rng(zlib.crc32(case.encode()))
     if case == "small":
@@ -434,6 +434,12 @@ def test_grouped_w4a8_cases(case):
         T, tk, E, K, N = 300, 1, 2, 160, 200  # 300 rows on one expert: several token chunks
         ids = np.zeros((T, tk), np.int32)
         ids[::4] = 1
+    elif case == "big_expert_wide":
+        # 16-byte scale gathers in the routing pass: 225 rows of expert 0 in
+        # three row tiles (96, 96, 33) and 72 groups per row in two passes
+        T, tk, E, K, N = 300, 1, 2, 2304, 64
+        ids = np.zeros((T, tk), np.int32)
+        ids[::4] = 1
     else:
         T, tk, E, K, N = 19, 1, 1, 64, 40
         ids = np.zeros((T, tk), np.int32)
@@ -446,6 +452,26 @@ def test_grouped_w4a8_cases(case):
     assert_within_bound(y, yr, asum, K // 32, case)
     bad = (ids < 0) | (ids >= E)
     assert (y[bad] == 0).all()
+
+
+def test_grouped_w4a8_unaligned_scales():
+    """Activation scales that start 2 bytes past a 16-byte boundary: the
+    routing pass gathers them with 2-byte loads instead of 16-byte ones."""
+    T, tk, E, K, N = 150, 2, 3, 512, 48
+    ids = W.topk_ids(T, tk, E, seed=9)
+    qa = W.random_int8("moe", 703, (T, K), seed=K)
+    da = W.random_scales("moe", 704, (T, K // 32), seed=K)
+    g = np.random.default_rng(704)
+    packed = g.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    wsc = W.random_scales("moe", 705, (E, N, K // 32), seed=K)
+    buf = dev_tensor(np.zeros(T * (K // 32) + 8, np.uint16).view(np.int16))
+    da_dev = buf[1:1 + T * (K // 32)].view(T, K // 32)
+    da_dev.copy_(dev_tensor(da.view(np.int16)))
+    assert da_dev.data_ptr() % 16 == 2
+    y = host(bqi.qgemm_w4a8_grouped(dev_tensor(qa), da_dev, dev_tensor(ids),
+                                    dev_tensor(packed), dev_tensor(wsc)))
+    yr, asum = oracle.qgemm_w4a8_grouped(qa, da, ids, packed, wsc, nthreads=oracle_threads())
+    assert_within_bound(y, yr, asum, K // 32, "unaligned scales")
 
 
 @pytest.mark.parametrize("weights", ["quantized_normal", "uniform_codes"])
