@@ -30,6 +30,14 @@
 // the ids are first remapped so each XCD walks a contiguous range of tiles,
 // and tiles are ordered in groups of 8 row-tiles so that workgroups running
 // together on an XCD share A and W tiles through that XCD's L2.
+//
+// Grids of at most one tile per CU (short prompts: m up to ~128 rows for
+// wide weights) run k_gemm_mfma_w8 instead: the same tile, operand layout and
+// epilogue, with 8 waves per workgroup (a 32x64 part each) and one workgroup
+// per CU, so every SIMD still holds two waves where the 4-wave kernel would
+// leave one.  With the CU to itself it keeps three stage buffers in (dynamic)
+// LDS and issues the loads two stages ahead.  Larger grids stay on the 4-wave
+// kernel, whose two workgroups per CU cover each other's stalls.
 #include "bqi_device.h"
 #include "bqi_launch.h"
 
@@ -62,13 +70,9 @@ struct Tiles {
   float wd[BN][NBS];  // [col][block]
 };
 
-__global__ __launch_bounds__(THREADS, 2) void k_gemm_mfma(
-    const int8_t *__restrict__ aq, const uint16_t *__restrict__ ad, int m,
-    const int8_t *__restrict__ wq, const uint16_t *__restrict__ wd, int n,
-    int k, float *__restrict__ y, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) Tiles T[2];
-
-  // ---- tile selection: XCD-contiguous ranges, grouped along M -------------
+// Origin (m0, n0) of this workgroup's tile: XCD-contiguous ranges of tile
+// ids, grouped by GROUP_M row tiles.
+__device__ __forceinline__ void tile_origin(int tiles_m, int tiles_n, int &m0, int &n0) {
   const int tiles = tiles_m * tiles_n;
   int tile;
   {
@@ -82,9 +86,18 @@ __global__ __launch_bounds__(THREADS, 2) void k_gemm_mfma(
   const int first_m = group * GROUP_M;
   const int gm = min(tiles_m - first_m, GROUP_M);
   const int in_group = tile - group * per_group;
-  const int tm = first_m + in_group % gm;
-  const int tn = in_group / gm;
-  const int m0 = tm * BM, n0 = tn * BN;
+  m0 = (first_m + in_group % gm) * BM;
+  n0 = (in_group / gm) * BN;
+}
+
+__global__ __launch_bounds__(THREADS, 2) void k_gemm_mfma(
+    const int8_t *__restrict__ aq, const uint16_t *__restrict__ ad, int m,
+    const int8_t *__restrict__ wq, const uint16_t *__restrict__ wd, int n,
+    int k, float *__restrict__ y, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) Tiles T[2];
+
+  int m0, n0;
+  tile_origin(tiles_m, tiles_n, m0, n0);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -230,14 +243,202 @@ __global__ __launch_bounds__(THREADS, 2) void k_gemm_mfma(
   }
 }
 
+// ---- small grids: 8 waves per tile, three stage buffers -------------------
+constexpr int W8_WAVES = 8;
+constexpr int W8_THREADS = 64 * W8_WAVES;
+constexpr int W8_NBUF = 3;                                          // stage buffers
+constexpr int W8_LOADS_PER_WAVE = BM / ROWS_PER_LOAD / W8_WAVES;    // per operand tile (2)
+constexpr int W8_LDS = W8_NBUF * (int)sizeof(Tiles);
+static_assert(BM * NBS == W8_THREADS, "one scale of each operand per thread and stage");
+
+// Wave w owns row tile w/2 and column tiles 2(w%2), 2(w%2)+1 of the 128x128
+// tile.  Stage s issues the scales of stage s+1 and the tiles of stage s+2
+// (three buffers), and ends by waiting for those scales: loads complete in
+// issue order, so that wait also covers the tiles of stage s+1, and leaves
+// only the tiles of stage s+2 in flight.  All of these loads go through
+// inline asm (dma_lds16 and the scale loads below), which the compiler
+// neither counts nor waits for, because its own count of direct loads ends in
+// a full drain (vmcnt(0)) at every stage.
+__global__ __launch_bounds__(W8_THREADS, 1) void k_gemm_mfma_w8(
+    const int8_t *__restrict__ aq, const uint16_t *__restrict__ ad, int m,
+    const int8_t *__restrict__ wq, const uint16_t *__restrict__ wd, int n,
+    int k, float *__restrict__ y, int tiles_m, int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) int8_t gemm_lds[];
+  Tiles *T = reinterpret_cast<Tiles *>(gemm_lds);  // [W8_NBUF]
+  int m0, n0;
+  tile_origin(tiles_m, tiles_n, m0, n0);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;  // wave's 32x64 part: row tile wm, column tiles 2wn, 2wn+1
+  const int l32 = lane & 31, g = lane >> 5;
+  const int nbk = k / QK;
+  const int stages = (nbk + NBS - 1) / NBS;
+
+  auto issue_direct = [&](int s, int buf) {
+    const int k0 = s * BK;
+#pragma unroll
+    for (int q = 0; q < W8_LOADS_PER_WAVE; ++q) {
+      const int rt = ROWS_PER_LOAD * (W8_LOADS_PER_WAVE * wave + q);  // wave-uniform
+      const int r = rt + lane / CPR;
+      const int c = (lane % CPR) ^ ((r >> 1) & 7);
+      const int kk = k0 + 16 * c < k ? k0 + 16 * c : 0;
+      dma_lds16(aq + (min(m0 + r, m - 1) * k + kk), &T[buf].a[rt * BK]);
+      dma_lds16(wq + (min(n0 + r, n - 1) * k + kk), &T[buf].w[rt * BK]);
+    }
+  };
+  // The explicit waits take the two scale registers as operands, so that
+  // nothing reads them before their loads have landed.
+  uint32_t sa_reg, sw_reg;
+  auto issue_scales = [&](int s) {
+    const int row = tid / NBS, blk = tid % NBS;
+    const int kb = s * NBS + blk < nbk ? s * NBS + blk : 0;
+    const uint16_t *pa = ad + min(m0 + row, m - 1) * nbk + kb;
+    const uint16_t *pw = wd + min(n0 + row, n - 1) * nbk + kb;
+    asm volatile("global_load_ushort %0, %1, off" : "=v"(sa_reg) : "v"(pa) : "memory");
+    asm volatile("global_load_ushort %0, %1, off" : "=v"(sw_reg) : "v"(pw) : "memory");
+  };
+  auto store_scales = [&](int buf) {
+    const int row = tid / NBS, blk = tid % NBS;
+    T[buf].ad[blk][row] = half_bits_to_float((uint16_t)sa_reg);
+    T[buf].wd[row][blk] = half_bits_to_float((uint16_t)sw_reg);
+  };
+
+  float acc[2][16];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+
+  i32x16 seed;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) seed[r] = MAGIC_BITS;
+
+  // stage 0 landed and its scales stored; stage 1's tiles in flight
+  issue_scales(0);
+  issue_direct(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(sa_reg), "+v"(sw_reg) :: "memory");
+  store_scales(0);
+  if (stages > 1) issue_direct(1, 1);
+  __syncthreads();
+
+  for (int s = 0; s < stages; ++s) {
+    const int buf = s % W8_NBUF;
+    const Tiles &TB = T[buf];
+    // unconditional, so that every stage issues the same loads and the wait
+    // count below is exact: past the last stage they re-read it into the
+    // buffer that no stage reads any more
+    issue_scales(min(s + 1, stages - 1));
+    issue_direct(min(s + 2, stages - 1), (s + 2) % W8_NBUF);
+
+    float dwf[2][NBS];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const f32x4 four = *reinterpret_cast<const f32x4 *>(&TB.wd[wn * 64 + j * 32 + l32][0]);
+      dwf[j][0] = four.x;
+      dwf[j][1] = four.y;
+      dwf[j][2] = four.z;
+      dwf[j][3] = four.w;
+    }
+    const int nb_here = min(NBS, nbk - s * NBS);
+
+    for (int b = 0; b < nb_here; ++b) {
+      const int r = wm * 32 + l32;
+      const i32x4 af = *reinterpret_cast<const i32x4 *>(&TB.a[r * BK + swz(r, 2 * b + g) * 16]);
+      float da[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(&TB.ad[b][wm * 32 + 8 * q + 4 * g]);
+        da[4 * q + 0] = v.x;
+        da[4 * q + 1] = v.y;
+        da[4 * q + 2] = v.z;
+        da[4 * q + 3] = v.w;
+      }
+      i32x4 wf[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = wn * 64 + j * 32 + l32;
+        wf[j] = *reinterpret_cast<const i32x4 *>(&TB.w[c * BK + swz(c, 2 * b + g) * 16]);
+      }
+      float dwb[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        dwb[j] = dwf[j][0];
+#pragma unroll
+        for (int bb = 1; bb < NBS; ++bb)
+          if (b == bb) dwb[j] = dwf[j][bb];
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const i32x16 d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, wf[j], seed, 0, 0, 0);
+        const float dw = dwb[j];
+        const float ncd = -MAGIC_F * dw;  // exact
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const float t = fmaf(bits_to_float(d[rr]), dw, ncd);
+          acc[j][rr] = fmaf(t, da[rr], acc[j][rr]);
+        }
+      }
+    }
+
+    if (s + 1 < stages) {
+      // everything but stage s+2's 2 * W8_LOADS_PER_WAVE tile loads has landed
+      asm volatile("s_waitcnt vmcnt(%2)" : "+v"(sa_reg), "+v"(sw_reg) : "n"(2 * W8_LOADS_PER_WAVE) : "memory");
+      store_scales((s + 1) % W8_NBUF);
+      __syncthreads();
+    }
+  }
+
+  __builtin_amdgcn_s_waitcnt(0);  // no direct load may land after the workgroup ends
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = n0 + wn * 64 + j * 32 + l32;
+    if (col < n) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (row < m) y[(int64_t)row * n + col] = acc[j][r];
+      }
+    }
+  }
+}
+
 }  // namespace
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
 
 hipError_t launch_gemm_mfma(const int8_t *aq, const uint16_t *ad, int64_t m,
                             const int8_t *wq, const uint16_t *wd, int64_t n,
                             int64_t k, float *y, hipStream_t stream) {
   const int tiles_m = (int)((m + BM - 1) / BM);
   const int tiles_n = (int)((n + BN - 1) / BN);
-  hipLaunchKernelGGL(k_gemm_mfma, dim3((unsigned)(tiles_m * tiles_n)), dim3(THREADS),
+  const int tiles = tiles_m * tiles_n;
+  if (tiles <= device_cus()) {
+    // at most one tile per CU: the 8-wave, three-stage kernel
+    static bool raised = false;
+    if (!raised) {
+      const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_mfma_w8,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, W8_LDS);
+      if (e != hipSuccess) return e;
+      raised = true;
+    }
+    hipLaunchKernelGGL(k_gemm_mfma_w8, dim3((unsigned)tiles), dim3(W8_THREADS), W8_LDS, stream,
+                       aq, ad, (int)m, wq, wd, (int)n, (int)k, y, tiles_m, tiles_n);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_gemm_mfma, dim3((unsigned)tiles), dim3(THREADS),
                      0, stream, aq, ad, (int)m, wq, wd, (int)n, (int)k, y,
                      tiles_m, tiles_n);
   return hipGetLastError();

@@ -181,7 +181,11 @@ SHAPES = [(1, 32, 1), (1, 96, 33), (2, 64, 100), (3, 160, 77), (4, 256, 512), (5
           # workgroup, one, two and five K parts
           (16, 64, 12290), (7, 1088, 12300), (5, 5120, 12320),
           # a single weight row and a partial 16-row group
-          (8, 2048, 1), (16, 4096, 7)]
+          (8, 2048, 1), (16, 4096, 7),
+          # large-M: 256 tiles of 128 x 128 (one per CU: the 8-wave kernel,
+          # three stages) and 272 tiles (the 4-wave kernel), each with a
+          # short last stage
+          (2048, 416, 2048), (2049, 416, 2048)]
 
 
 @pytest.mark.parametrize("m,k,n", SHAPES)
