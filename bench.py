@@ -44,8 +44,9 @@ sys.path.insert(0, ROOT)
 METRIC = "int8-equiv TOPS (% MFMA peak) prefill GEMM; GB/s (% HBM peak) M=1 GEMV"
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0      # dense int8 MFMA, MI355X
-# fp32 VALU without packed-fp32 instructions: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
-VALU_LANE_OPS_PEAK = 256 * 4 * 16 * 2.4e9
+# fp32 vector FMA lane-ops per second: MI355X's published 157.3 TFLOP/s fp32
+# vector rate counts each FMA as two flops (256 CU x 128 lanes x 2.4 GHz)
+VALU_LANE_OPS_PEAK = 157.3e12 / 2
 
 
 def parse():
