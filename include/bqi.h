@@ -27,6 +27,9 @@
  *    group (16 bytes), byte j holds element j in its low nibble and element
  *    j+16 in its high nibble.  Element value = (code - 8) * scale.
  *
+ * Below, "mining card" cites the euno.news article and "2011 GPU" the
+ * gist.science summary, each with its section.
+ *
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers, allocated and owned by the caller.
  *  - `stream` is a hipStream_t (NULL = the default stream).
@@ -77,8 +80,8 @@ BQI_API int bqi_abi_version(void);
 
 /*
  * quantize_q8_0 -- activations to Q8_0 (the quantizer of the pages' Q8_0
- * prefill path; page 1 "Features", page 3 Method 2 for the 8-bit activations
- * of W4A8).
+ * prefill path, "mining card", Features; and of the 8-bit activations of
+ * W4A8, "2011 GPU", Method 2).
  *
  *   x      [rows][ldx] fp32 (x_dtype = BQI_F32) or fp16 (BQI_F16), row-major;
  *          only the first k columns of each row are read.
@@ -99,8 +102,8 @@ BQI_API int quantize_q8_0(const void *x, int x_dtype, int64_t rows, int64_t k,
 
 /*
  * qgemm_q8_0 -- y = A * W^T with both operands Q8_0 (the prefill GEMM of
- * page 1 "Features" and the thin-M decode GEMM that page 3 "Results" names
- * as the structural decode bottleneck).
+ * "mining card", Features, and the thin-M decode GEMM that "2011 GPU",
+ * Results, names as the structural decode bottleneck).
  *
  *   aq [m][k] int8, ad [m][k/32] fp16 bits   -- activations A
  *   wq [n][k] int8, wd [n][k/32] fp16 bits   -- weights W (PyTorch Linear
@@ -125,7 +128,7 @@ BQI_API int qgemm_q8_0(const int8_t *aq, const uint16_t *ad, int64_t m,
 /*
  * quantize_qgemm_q8_0 -- quantize_q8_0 followed by qgemm_q8_0, the decode
  * step of the Q8_0 path (activation quantization, then the thin-M GEMM that
- * page 3 "Results" names as the decode bottleneck).
+ * "2011 GPU", Results, names as the decode bottleneck).
  *
  *   x  [m][ldx] fp32 (x_dtype = BQI_F32) or fp16 (BQI_F16) activations
  *   wq [n][k] int8, wd [n][k/32] fp16 bits   -- Q8_0 weights
@@ -149,7 +152,7 @@ BQI_API int quantize_qgemm_q8_0(const void *x, int x_dtype, int64_t m, int64_t k
 
 /*
  * route_topk -- group routed rows by expert (the routing step of the grouped
- * 4-bit GEMM for MoE routing, page 3 Method 1).
+ * 4-bit GEMM for MoE routing, "2011 GPU", Method 1).
  *
  *   topk_ids [n_tokens][top_k] int32 expert ids; routed row r = t*top_k + j.
  *   counts   [n_experts] int32 (output): rows routed to each expert.
@@ -174,7 +177,7 @@ BQI_API size_t qgemm_w4a8_grouped_workspace_size(int64_t n_tokens, int64_t top_k
 
 /*
  * qgemm_w4a8_grouped -- expert-routed 4-bit-weight x Q8_0-activation GEMM
- * (the grouped 4-bit GEMM for MoE routing of page 3 Method 1, with the
+ * (the grouped 4-bit GEMM for MoE routing of "2011 GPU", Method 1, with the
  * W4A8 format of its Method 2).
  *
  *   aq [n_tokens][k] int8, ad [n_tokens][k/32] fp16 bits  -- Q8_0 activations
@@ -208,7 +211,7 @@ BQI_API int qgemm_w4a8_grouped(const int8_t *aq, const uint16_t *ad, int64_t n_t
 /*
  * moe_combine_f32 -- the MoE combine after the grouped GEMM: each token's
  * top-k expert outputs weighted by its router probabilities and summed back
- * in token order (page 3: the grouped 4-bit GEMM serves the MoE routing,
+ * in token order ("2011 GPU": the grouped 4-bit GEMM serves the MoE routing,
  * Method 1; the experts are router-weighted, Method 2).
  *
  *   y   [n_tokens][top_k][n] fp32  -- e.g. the output of qgemm_w4a8_grouped
@@ -226,7 +229,7 @@ BQI_API int moe_combine_f32(const float *y, const float *p, int64_t n_tokens,
 /*
  * gguf_q8_0_to_planar, gguf_q4_0_to_planar -- split a GGUF block array into
  * this library's planar layout, so that weights stored as GGUF (the format of
- * page 1's "Honest benchmark" comparison) can be consumed.
+ * "mining card", Honest benchmark) can be consumed.
  *
  *   blocks: rows * k/32 contiguous blocks, row-major; each block is a
  *           little-endian fp16 scale followed by its codes:
@@ -248,7 +251,7 @@ BQI_API int gguf_q4_0_to_planar(const void *blocks, int64_t rows, int64_t k,
 
 /*
  * qgemm_w4a8_grouped_host -- the grouped W4A8 GEMM on the host CPU, with
- * integer SIMD (page 3: the CPU decode path with a hand-written W4A8 kernel on
+ * integer SIMD ("2011 GPU": the CPU decode path with a hand-written W4A8 kernel on
  * pmaddubsw, Method 1 and Contributions; here AVX2 vpmaddubsw).
  *
  * HOST pointers, same layouts and the same function as qgemm_w4a8_grouped
