@@ -10,6 +10,20 @@
 
 namespace bqi {
 
+// Raises a kernel's dynamic-LDS limit (64 KB by default) to `bytes`, once per
+// device: `done` is the calling launcher's own table, indexed by device.
+// Concurrent first calls may both set the attribute, which is harmless.
+inline hipError_t raise_dynamic_lds(const void *kernel, int bytes, bool (&done)[64]) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < 64;
+  if (cached && done[dev]) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && cached) done[dev] = true;
+  return e;
+}
+
 hipError_t launch_quantize_q8_0(const void *x, bool f16, int64_t rows,
                                 int64_t k, int64_t ldx, int8_t *q, uint16_t *d,
                                 hipStream_t stream);

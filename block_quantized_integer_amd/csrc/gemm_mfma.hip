@@ -427,13 +427,9 @@ hipError_t launch_gemm_mfma(const int8_t *aq, const uint16_t *ad, int64_t m,
   const int tiles = tiles_m * tiles_n;
   if (tiles <= device_cus()) {
     // at most one tile per CU: the 8-wave, three-stage kernel
-    static bool raised = false;
-    if (!raised) {
-      const hipError_t e = hipFuncSetAttribute((const void *)k_gemm_mfma_w8,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, W8_LDS);
-      if (e != hipSuccess) return e;
-      raised = true;
-    }
+    static bool raised[64];
+    const hipError_t e = raise_dynamic_lds((const void *)k_gemm_mfma_w8, W8_LDS, raised);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_gemm_mfma_w8, dim3((unsigned)tiles), dim3(W8_THREADS), W8_LDS, stream,
                        aq, ad, (int)m, wq, wd, (int)n, (int)k, y, tiles_m, tiles_n);
     return hipGetLastError();

@@ -403,14 +403,10 @@ hipError_t launch_reg(const int8_t *aq, const uint16_t *ad, const void *x, int64
   constexpr int NT = reg_threads(SRC, MT);
   constexpr int LDS = reg_lds_bytes(MT, CH);
   if constexpr (LDS > 65536) {
-    // above the default dynamic-LDS limit: raise it once for this kernel
-    static bool raised = false;
-    if (!raised) {
-      const hipError_t e = hipFuncSetAttribute((const void *)k_gemv_reg<MT, CH, SRC>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-      if (e != hipSuccess) return e;
-      raised = true;
-    }
+    // above the default dynamic-LDS limit: raise it for this kernel
+    static bool raised[64];
+    const hipError_t e = raise_dynamic_lds((const void *)k_gemv_reg<MT, CH, SRC>, LDS, raised);
+    if (e != hipSuccess) return e;
   }
   const int64_t rows_per_wg = (NT / 64) * REG_RPW;
   const int64_t wgs = (n + rows_per_wg - 1) / rows_per_wg;
@@ -782,13 +778,10 @@ hipError_t launch_mfma16_rg(const int8_t *aq, const uint16_t *ad, int64_t m,
                             const MfShape &sh, float *y, hipStream_t stream) {
   // LDS: the stages plus one weight-scale slot per row group of every wave
   const int64_t lds = mf_lds_bytes(k, (int64_t)sh.ks * sh.groups * RG);
-  static bool raised = false;
-  if (lds > 65536 && !raised) {
-    const hipError_t e = hipFuncSetAttribute((const void *)k_gemv_mfma16<RG>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)MF_LDS_MAX);
+  static bool raised[64];
+  if (lds > 65536) {
+    const hipError_t e = raise_dynamic_lds((const void *)k_gemv_mfma16<RG>, (int)MF_LDS_MAX, raised);
     if (e != hipSuccess) return e;
-    raised = true;
   }
   const int64_t rows_per_wg = 16 * RG * sh.groups;
   const int64_t wgs = (n + rows_per_wg - 1) / rows_per_wg;
