@@ -367,6 +367,22 @@ def test_prefill_workloads_sampled(name):
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
 
 
+def test_qgemm_small_and_large_grid_kernels_agree():
+    """The same 256 x 2048 output rows computed as a grid of 32 tiles (one
+    per CU: the 8-wave kernel) and inside a grid of 544 tiles (the 4-wave
+    kernel) are bit-identical: both sum each output's blocks in one order."""
+    k, n = 416, 2048
+    aq = W.random_int8(0, 510, (4352, k), seed=1)
+    ad = W.random_scales(0, 511, (4352, k // 32), seed=2)
+    wq = W.random_int8(0, 512, (n, k), seed=3)
+    wd = W.random_scales(0, 513, (n, k // 32), seed=4)
+    y_small = run_gemm(aq[:256], ad[:256], wq, wd)
+    y_large = run_gemm(aq, ad, wq, wd)
+    assert np.array_equal(y_small.view(np.uint32), y_large[:256].view(np.uint32))
+    yr, asum = oracle.qgemm_q8_0(aq[:256], ad[:256], wq, wd, nthreads=oracle_threads())
+    assert_within_bound(y_small, yr, asum, k // 32, "small grid")
+
+
 @pytest.mark.parametrize("k", [256, 288])
 def test_qgemm_ragged_more_tiles_than_slots(k):
     """536 tiles of 128 x 128 (more than one round of workgroups, a short
