@@ -57,7 +57,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--only-headline", action="store_true", help="skip the secondary workloads")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--workloads", default="decode,decode_m,prefill,long,moe,moe_decode,combine,gguf,host",
+    p.add_argument("--workloads", default="decode,decode_m,prefill,prefill_short,long,moe,moe_decode,combine,gguf,host",
                    help="comma list of workloads to run (profiling); the JSON line "
                         "is printed only when decode is among them.  'copy' (never a "
                         "default) runs a plain device copy of known size, the "
@@ -323,9 +323,14 @@ def bench_decode_variants(bqi, torch, W, iters):
 
 
 def bench_gemm(bqi, torch, W, name, iters):
-    s = W.PREFILL if name == "prefill" else W.LONG
+    s = {"prefill": W.PREFILL, "prefill_short": W.PREFILL_SHORT, "long": W.LONG}[name]
     gen = torch.Generator(device="cuda")
-    gen.manual_seed(2 if name == "prefill" else 3)
+    gen.manual_seed({"prefill": 2, "long": 3, "prefill_short": 4}[name])
+    # the library runs grids of at most one 128 x 128 tile per CU on its
+    # 8-wave kernel, larger grids on the 4-wave one
+    tiles = -(-s.m // 128) * -(-s.n // 128)
+    kernel = ("k_gemm_mfma_w8" if tiles <= torch.cuda.get_device_properties(0).multi_processor_count
+              else "k_gemm_mfma")
     log("%s GEMM M=%d K=%d N=%d" % (name, s.m, s.k, s.n))
     if name == "long":
         xa, aq, ad = device_q8(bqi, torch, s.m, s.k, 1.0, gen, t_dist=True,
@@ -336,7 +341,9 @@ def bench_gemm(bqi, torch, W, name, iters):
     y = torch.empty((s.m, s.n), dtype=torch.float32, device="cuda")
     T = Timer(torch)
     mean = T.loop(lambda i: bqi.qgemm_q8_0(aq, ad, wq, wd, y), iters, check=lambda: y)
-    qmean = T.loop(lambda i: bqi.quantize_q8_0(xa, aq, ad), max(3, iters // 2), check=lambda: aq)
+    # 100 launches per graph: with a handful, the graph's own launch cost
+    # would be spread over too few of these short kernels
+    qmean = T.loop(lambda i: bqi.quantize_q8_0(xa, aq, ad), 100, check=lambda: aq)
     ops = 2.0 * s.m * s.n * s.k
     tops = ops / (mean * 1e-3) / 1e12
     out_blocks = s.m * s.n * (s.k // 32)
@@ -346,12 +353,12 @@ def bench_gemm(bqi, torch, W, name, iters):
     del xa
     return {
         "workload": "%s GEMM M=%d K=%d N=%d" % (name, s.m, s.k, s.n),
-        "kernel": "k_gemm_mfma", "value": round(tops, 2), "unit": "int8-equiv TOPS",
+        "kernel": kernel, "value": round(tops, 2), "unit": "int8-equiv TOPS",
         "mean_launch_us": round(mean * 1e3, 2),
         "frac_int8_mfma_peak": round(tops / INT8_PEAK_TOPS, 4),
         "epilogue_valu_frac": round(valu_ops / (mean * 1e-3) / VALU_LANE_OPS_PEAK, 4),
         "hbm_bytes_algorithmic": byt,
-        "hbm_bytes_measured": traffic("k_gemm_mfma %s" % name),
+        "hbm_bytes_measured": traffic("%s %s" % (kernel, name)),
         "quantize": {"kernel": "k_quantize_q8_0", "mean_launch_us": round(qmean * 1e3, 2),
                      "GB/s": round(qbytes / (qmean * 1e-3) / 1e9, 1),
                      "frac_hbm_peak": round(qbytes / (qmean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
@@ -588,7 +595,7 @@ def main():
                 also.append(r)
                 log(json.dumps(r))
             torch.cuda.empty_cache()
-        for name in ("prefill", "long"):
+        for name in ("prefill", "prefill_short", "long"):
             if name in wl:
                 also.append(bench_gemm(bqi, torch, W, name, 20))
                 log(json.dumps(also[-1]))
@@ -598,16 +605,16 @@ def main():
             log(json.dumps(also[-1]))
             torch.cuda.empty_cache()
         if "moe_decode" in wl:
-            for r in bench_moe_decode(bqi, torch, W, 100):
+            for r in bench_moe_decode(bqi, torch, W, 400):
                 also.append(r)
                 log(json.dumps(r))
             torch.cuda.empty_cache()
         if "combine" in wl:
-            also.append(bench_combine(bqi, torch, W, 100))
+            also.append(bench_combine(bqi, torch, W, 400))
             log(json.dumps(also[-1]))
             torch.cuda.empty_cache()
         if "gguf" in wl:
-            for r in bench_gguf(bqi, torch, W, 20):
+            for r in bench_gguf(bqi, torch, W, 60):
                 also.append(r)
                 log(json.dumps(r))
         if "host" in wl:

@@ -42,6 +42,8 @@ class GemmShape:
 SMALL = GemmShape("small", 16, 256, 512)
 DECODE = [GemmShape("decode_m%d" % m, m, 4096, 12288) for m in (1, 4, 16)]
 PREFILL = GemmShape("prefill", 2048, 5120, 17408)
+# a short prompt against the same weights: 136 output tiles, fewer than CUs
+PREFILL_SHORT = GemmShape("prefill_short", 128, 5120, 17408)
 LONG = GemmShape("long", 18432, 5120, 5120)
 
 
