@@ -11,11 +11,13 @@ than the 256 MB Infinity Cache) so every step streams its weights from HBM.
 `value` is algorithmic bytes per step / time per step (GB/s); inputs are
 resident in HBM before timing starts.
 
-Also reported (key "also"): the prefill GEMM (M=2048, K=5120, N=17408), the
-long-prefill GEMM (M=18432, K=5120, N=5120, Student-t activations with outlier
-channels), the grouped W4A8 MoE GEMM (947 tokens, top-8 of 128 experts,
-K=2048, N=768), the activation quantizer, the MoE combine and the GGUF
-import, each with its own roofline.
+Also reported (key "also"): the M=4 and M=16 decode steps, the prefill GEMM
+(M=2048, K=5120, N=17408) and a short-prompt prefill against the same weights
+(M=128), the long-prefill GEMM (M=18432, K=5120, N=5120, Student-t
+activations with outlier channels), the grouped W4A8 MoE GEMM (947 tokens,
+top-8 of 128 experts, K=2048, N=768) and its decode form (1, 4 and 16
+tokens), the activation quantizer, the MoE combine, the GGUF import and the
+host-CPU W4A8 decode kernel, each with its own roofline or baseline.
 
 "roofline" describes the step's kernel (the fused quantize + GEMV): achieved =
 algorithmic bytes per launch / mean launch duration, from HIP events recorded
