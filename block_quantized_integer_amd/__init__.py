@@ -15,6 +15,10 @@ Entry points (same names as the C ABI):
 
 fp16 scale bit patterns travel as torch.int16 tensors (torch has no uint16
 arithmetic on GPU); only their bits matter.
+
+Every wrapper takes an optional `stream` (a torch.cuda.Stream or a raw
+hipStream_t handle); without one it uses the current stream.  Outputs and
+workspaces that a wrapper allocates are allocated on that same stream.
 """
 from __future__ import annotations
 
@@ -94,6 +98,22 @@ def _stream(stream):
     return C.c_void_p(int(stream))
 
 
+def _on(stream, device):
+    """Context in which the wrappers allocate their outputs and workspaces:
+    the caller's stream when one is given, so that torch's caching allocator
+    ties those blocks to the stream the kernels run on (a block freed when a
+    wrapper returns is then reused only by work ordered after the kernels).
+    A raw hipStream_t handle is wrapped as an external stream of `device`."""
+    torch = _torch()
+    if stream is None:
+        import contextlib
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        stream = torch.cuda.ExternalStream(handle, device=device)
+    return torch.cuda.stream(stream)
+
+
 def _check(t, dtype, ndim, name):
     torch = _torch()
     if not isinstance(t, torch.Tensor):
@@ -128,10 +148,11 @@ def quantize_q8_0(x, q=None, d=None, stream=None):
         raise ValueError("x must be a 2-D GPU tensor with unit column stride")
     R, K = x.shape
     ldx = x.stride(0) if R > 1 else K
-    if q is None:
-        q = torch.empty((R, K), dtype=torch.int8, device=x.device)
-    if d is None:
-        d = torch.empty((R, K // 32), dtype=torch.int16, device=x.device)
+    with _on(stream, x.device):
+        if q is None:
+            q = torch.empty((R, K), dtype=torch.int8, device=x.device)
+        if d is None:
+            d = torch.empty((R, K // 32), dtype=torch.int16, device=x.device)
     _check(q, torch.int8, 2, "q")
     _check(d, torch.int16, 2, "d")
     dt = BQI_F32 if x.dtype == torch.float32 else BQI_F16
@@ -153,7 +174,8 @@ def qgemm_q8_0(aq, ad, wq, wd, y=None, stream=None):
         raise ValueError("shape mismatch: aq %s ad %s wq %s wd %s" % (
             tuple(aq.shape), tuple(ad.shape), tuple(wq.shape), tuple(wd.shape)))
     if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=aq.device)
+        with _on(stream, aq.device):
+            y = torch.empty((M, N), dtype=torch.float32, device=aq.device)
     _check(y, torch.float32, 2, "y")
     st = lib().qgemm_q8_0(_ptr(aq), _ptr(ad), M, _ptr(wq), _ptr(wd), N, K, _ptr(y),
                           _stream(stream))
@@ -179,12 +201,13 @@ def quantize_qgemm_q8_0(x, wq, wd, y=None, q=None, d=None, stream=None):
         raise ValueError("shape mismatch: x %s wq %s wd %s" % (
             tuple(x.shape), tuple(wq.shape), tuple(wd.shape)))
     ldx = x.stride(0) if M > 1 else K
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    if q is None:
-        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
-    if d is None:
-        d = torch.empty((M, K // 32), dtype=torch.int16, device=x.device)
+    with _on(stream, x.device):
+        if y is None:
+            y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+        if q is None:
+            q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        if d is None:
+            d = torch.empty((M, K // 32), dtype=torch.int16, device=x.device)
     _check(y, torch.float32, 2, "y")
     _check(q, torch.int8, 2, "q")
     _check(d, torch.int16, 2, "d")
@@ -201,12 +224,13 @@ def route_topk(topk_ids, n_experts, counts=None, offsets=None, rows=None, stream
     _check(topk_ids, torch.int32, 2, "topk_ids")
     T, top_k = topk_ids.shape
     dev = topk_ids.device
-    if counts is None:
-        counts = torch.empty(n_experts, dtype=torch.int32, device=dev)
-    if offsets is None:
-        offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
-    if rows is None:
-        rows = torch.empty(max(1, T * top_k), dtype=torch.int32, device=dev)
+    with _on(stream, dev):
+        if counts is None:
+            counts = torch.empty(n_experts, dtype=torch.int32, device=dev)
+        if offsets is None:
+            offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
+        if rows is None:
+            rows = torch.empty(max(1, T * top_k), dtype=torch.int32, device=dev)
     st = lib().route_topk(_ptr(topk_ids), T, top_k, n_experts, _ptr(counts), _ptr(offsets),
                           _ptr(rows), _stream(stream))
     _raise(st, "route_topk")
@@ -232,12 +256,15 @@ def qgemm_w4a8_grouped(aq, ad, topk_ids, wq4, wd, y=None, workspace=None, stream
     if KH * 2 != K or tuple(ad.shape) != (T, K // 32) or topk_ids.shape[0] != T \
             or tuple(wd.shape) != (E, N, K // 32):
         raise ValueError("shape mismatch")
-    if y is None:
-        y = torch.empty((T, top_k, N), dtype=torch.float32, device=aq.device)
-    _check(y, torch.float32, 3, "y")
     need = workspace_size(T, top_k, E, K)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=aq.device)
+    with _on(stream, aq.device):
+        # the workspace is freed when this function returns: allocated on the
+        # kernels' stream, it is not handed out again before they finish
+        if y is None:
+            y = torch.empty((T, top_k, N), dtype=torch.float32, device=aq.device)
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=aq.device)
+    _check(y, torch.float32, 3, "y")
     if workspace.numel() < need:
         raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel(), need))
     st = lib().qgemm_w4a8_grouped(_ptr(aq), _ptr(ad), T, _ptr(topk_ids), top_k, _ptr(wq4),
@@ -257,7 +284,8 @@ def moe_combine_f32(y, p, out=None, stream=None):
     if tuple(p.shape) != (T, top_k):
         raise ValueError("shape mismatch: y %s p %s" % (tuple(y.shape), tuple(p.shape)))
     if out is None:
-        out = torch.empty((T, N), dtype=torch.float32, device=y.device)
+        with _on(stream, y.device):
+            out = torch.empty((T, N), dtype=torch.float32, device=y.device)
     _check(out, torch.float32, 2, "out")
     st = lib().moe_combine_f32(_ptr(y), _ptr(p), T, top_k, N, _ptr(out), _stream(stream))
     _raise(st, "moe_combine_f32")
@@ -270,12 +298,13 @@ def _gguf(fmt, blocks, rows, k, codes, scales, stream):
     per = 34 if fmt == "q8_0" else 18
     if k % 32 or blocks.numel() != rows * (k // 32) * per:
         raise ValueError("blocks must hold rows * k/32 GGUF %s blocks" % fmt)
-    if codes is None:
-        codes = torch.empty((rows, k) if fmt == "q8_0" else (rows, k // 2),
-                            dtype=torch.int8 if fmt == "q8_0" else torch.uint8,
-                            device=blocks.device)
-    if scales is None:
-        scales = torch.empty((rows, k // 32), dtype=torch.int16, device=blocks.device)
+    with _on(stream, blocks.device):
+        if codes is None:
+            codes = torch.empty((rows, k) if fmt == "q8_0" else (rows, k // 2),
+                                dtype=torch.int8 if fmt == "q8_0" else torch.uint8,
+                                device=blocks.device)
+        if scales is None:
+            scales = torch.empty((rows, k // 32), dtype=torch.int16, device=blocks.device)
     _check(codes, torch.int8 if fmt == "q8_0" else torch.uint8, 2, "codes")
     _check(scales, torch.int16, 2, "scales")
     f = lib().gguf_q8_0_to_planar if fmt == "q8_0" else lib().gguf_q4_0_to_planar

@@ -91,12 +91,6 @@ __device__ __forceinline__ uint32_t q8_0_quantize4(const float (&v)[4], uint16_t
 constexpr int32_t MAGIC_BITS = 0x4B400000;
 constexpr float MAGIC_F = 12582912.0f;
 
-// Index of the LDS 16-byte chunk holding logical chunk c (0..3) of row r in
-// a tile stored as rows of 64 bytes: an XOR swizzle that makes the MFMA
-// fragment reads (32 rows, same logical chunk) hit 8 distinct bank groups
-// per 8 lanes.
-__device__ __forceinline__ int swz64(int r, int c) { return c ^ ((r >> 1) & 3); }
-
 // Direct global -> LDS loads (gfx950 LDS DMA).  Lane L's 16 (or 4) bytes
 // land at lds_wave_base + 16 * L (4 * L); lds_wave_base must be wave-uniform
 // (it travels in M0).  The compiler counts these loads in vmcnt like any other
@@ -108,10 +102,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ void load_lds16(const void *gsrc, void *lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void *)lds_wave_base, 16, 0, 0);
-}
-
-__device__ __forceinline__ void load_lds4(const void *gsrc, void *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void *)lds_wave_base, 4, 0, 0);
 }
 
 // The same loads issued through inline asm, invisible to the compiler: it
@@ -151,23 +141,6 @@ __device__ __forceinline__ void dma_lds_u16(const void *gsrc, void *lds_wave_bas
                :
                : "v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base)))
                : "memory");
-}
-
-// A 16-bit register load through inline asm (zero-extended), likewise
-// invisible to the compiler's wait counting: its value may be used only after
-// wait_vmcnt_for() has named the register.
-__device__ __forceinline__ uint32_t load_u16_async(const uint16_t *p) {
-  uint32_t v;
-  asm volatile("global_load_ushort %0, %1, off" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
-
-// s_waitcnt vmcnt(N) that the compiler treats as producing a and b, so no use
-// of them (loaded by load_u16_async) can be scheduled before it.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_for(uint32_t &a, uint32_t &b) {
-  static_assert(N >= 0 && N < 16, "immediate vmcnt");
-  asm volatile("s_waitcnt vmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N) : "memory");
 }
 
 // s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima), in the

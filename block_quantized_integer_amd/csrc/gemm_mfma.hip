@@ -325,10 +325,13 @@ __global__ __launch_bounds__(W8_THREADS, 1) void k_gemm_mfma_w8(
   for (int s = 0; s < stages; ++s) {
     const int buf = s % W8_NBUF;
     const Tiles &TB = T[buf];
-    // unconditional, so that every stage issues the same loads and the wait
-    // count below is exact: past the last stage they re-read it into the
-    // buffer that no stage reads any more
-    issue_scales(min(s + 1, stages - 1));
+    // The tile loads are unconditional, so that every stage issues the same
+    // loads and the wait count below is exact: past the last stage they
+    // re-read it into the buffer that no stage reads any more.  The scale
+    // register loads are issued only for a stage that follows: the last stage
+    // leaves none in flight, so no register load outlives the waits that name
+    // its destination.
+    if (s + 1 < stages) issue_scales(s + 1);
     issue_direct(min(s + 2, stages - 1), (s + 2) % W8_NBUF);
 
     float dwf[2][NBS];
@@ -389,7 +392,9 @@ __global__ __launch_bounds__(W8_THREADS, 1) void k_gemm_mfma_w8(
     }
   }
 
-  __builtin_amdgcn_s_waitcnt(0);  // no direct load may land after the workgroup ends
+  // no direct load may land after the workgroup ends; the scale registers
+  // are named so that this wait also orders them (none is in flight here)
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(sa_reg), "+v"(sw_reg) :: "memory");
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int col = n0 + wn * 64 + j * 32 + l32;

@@ -31,7 +31,7 @@ def build(force: bool = True) -> str:
         return LIB_PATH
     src = os.path.join(_HERE, "bq_oracle.c")
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-pthread",
+    cmd = ["gcc", "-std=c11", "-O3", "-fPIC", "-shared", "-pthread",
            "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
            src, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)

@@ -2,7 +2,7 @@
  * bq_oracle.c -- plain CPU reference for block-quantized integer GEMM/GEMV.
  *
  * TEST INFRASTRUCTURE ONLY (see bq_oracle.h).  Plain C11 loops, no intrinsics,
- * no fast-math; built with gcc -O2 -ffp-contract=off so every float operation
+ * no fast-math; built with gcc -O3 -ffp-contract=off so every float operation
  * is the IEEE operation written.  Page citations are in bq_oracle.h.
  */
 #include "bq_oracle.h"

@@ -23,13 +23,21 @@ def host(t) -> np.ndarray:
     return a
 
 
+BAR = 1e-5  # the stated fp32 bar: relative error 1e-5 of sum|terms|
+
+
 def assert_within_bound(y_gpu, y_ref, asum, nb, what=""):
-    """|y_gpu - y_ref| <= (nb + 1) * 2^-24 * sum|terms| elementwise: the
-    library's stated worst case (each term rounded once, and each term passes
-    through at most nb accumulation roundings).  For nb <= 166 blocks
-    (K <= 5312) this is also below 1e-5 * sum|terms|."""
+    """|y_gpu - y_ref| <= min((nb + 1) * 2^-24, 1e-5) * sum|terms|, elementwise.
+
+    (nb + 1) * 2^-24 is the library's own worst case (each term rounded once,
+    and each term passes through at most nb accumulation roundings); it is the
+    tighter of the two for nb <= 166 blocks (K <= 5312, every workload).  For
+    longer K the library's worst case exceeds the stated 1e-5 bar, and those
+    shapes are held to the 1e-5 bar itself, which random data meets with a
+    wide margin (the rounding errors of an fp32 sum of nb terms grow like
+    sqrt(nb), not nb)."""
     y_gpu = np.asarray(y_gpu, np.float64)
-    bound = (nb + 1) * U * (1.0 + 1e-3) * asum
+    bound = min((nb + 1) * U * (1.0 + 1e-3), BAR) * asum
     err = np.abs(y_gpu - y_ref)
     bad = err > bound
     if bad.any():

@@ -2,10 +2,13 @@
 same seeded inputs.
 
 Bar: bit-exact for quantized codes, scales, routing tables and per-block int32
-dot products; fp32 GEMM outputs within (nb + 1) * 2^-24 * sum|terms| of the
-oracle's exact fp64 value (below 1e-5 * sum|terms| for K <= 5312, which covers
-every workload; the K = 8192 test shape is held to the same (nb + 1) bound).
+dot products; fp32 GEMM outputs within min((nb + 1) * 2^-24, 1e-5) *
+sum|terms| of the oracle's exact fp64 value.  The first is the library's own
+worst case and the tighter one for K <= 5312 (every workload); the K = 8192 and
+K = 16384 test shapes, where it is looser, are held to the stated 1e-5 bar.
+Every workload is compared in full, every output against the oracle.
 """
+import time
 import zlib
 
 import numpy as np
@@ -202,7 +205,12 @@ def test_qgemm_random_codes_full_range(m, k, n):
     assert_within_bound(y, yr, asum, k // 32, "m=%d k=%d n=%d" % (m, k, n))
 
 
-@pytest.mark.parametrize("m,n", [(1, 96), (5, 96), (16, 96), (40, 96), (128, 96), (16, 12288)])
+@pytest.mark.parametrize("m,n", [
+    (1, 96), (2, 96), (3, 96), (4, 96),   # k_gemv_reg, one to four rows
+    (4, 12288),                           # k_gemv_reg at the decode width
+    (5, 96), (16, 96), (8, 12288), (16, 12288),  # k_gemv_mfma16, one and three row groups per wave
+    (40, 96), (128, 96),                  # k_gemm_mfma_w8 (at most one tile per CU)
+    (2304, 2048)])                        # k_gemm_mfma: 288 tiles, more than one per CU
 def test_block_dots_bitexact_probe(m, n):
     """One-hot-block probe: each activation row has codes only in block
     b = row % nb and all scales are powers of two, so y = 2^(ea+ew) * P_b is
@@ -341,27 +349,25 @@ def test_fused_quantize_qgemm_strided_rows(decode_weights, rows):
     assert torch.equal(y, bqi.qgemm_q8_0(q, d, qw_g, dw_g))
 
 
-def sampled_check(y, qa, da, qw, dw, k, seed, what, n_samples=4096):
-    g = np.random.default_rng(seed)
-    m, n = y.shape
-    mi = np.concatenate([g.integers(0, m, n_samples), np.full(n, m - 1), np.zeros(n, np.int64),
-                         np.arange(m), np.arange(m)])
-    nj = np.concatenate([g.integers(0, n, n_samples), np.arange(n), np.arange(n),
-                         np.zeros(m, np.int64), np.full(m, n - 1)])
-    yr, asum = oracle.qgemm_q8_0_at(qa, da, qw, dw, mi, nj)
-    assert_within_bound(y[mi, nj], yr, asum, k // 32, what)
-    assert np.isfinite(y).all()
-
-
 @pytest.mark.parametrize("name", ["prefill", "long"])
-def test_prefill_workloads_sampled(name):
+def test_prefill_workloads_full(name):
+    """The prefill GEMM (2048 x 5120 x 17408) and the long prefill GEMM with
+    outlier channels (18432 x 5120 x 5120) at full size: every output against
+    the oracle (35.7 M and 94.4 M outputs), then a second run bit-identical."""
     s = W.PREFILL if name == "prefill" else W.LONG
     log("%s M=%d K=%d N=%d: generating" % (name, s.m, s.k, s.n))
     qa_g, da_g, qa, da = check_quantize(W.activations(name, s.m, s.k), name + " A")
     qw_g, dw_g, qw, dw = check_quantize(W.weights(name, s.n, s.k), name + " W")
     log("%s: gemm" % name)
     y = host(bqi.qgemm_q8_0(qa_g, da_g, qw_g, dw_g))
-    sampled_check(y, qa, da, qw, dw, s.k, 7, name)
+    assert np.isfinite(y).all()
+    threads = oracle_threads()
+    log("%s: oracle on %d threads" % (name, threads))
+    t0 = time.time()
+    yr, asum = oracle.qgemm_q8_0(qa, da, qw, dw, nthreads=threads)
+    log("%s: oracle took %.1f s; comparing %d outputs" % (name, time.time() - t0, y.size))
+    assert_within_bound(y, yr, asum, s.k // 32, name)
+    del yr, asum
     # run-to-run determinism at full size
     y2 = host(bqi.qgemm_q8_0(qa_g, da_g, qw_g, dw_g))
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
@@ -387,20 +393,42 @@ def test_qgemm_small_and_large_grid_kernels_agree():
 def test_qgemm_ragged_more_tiles_than_slots(k):
     """536 tiles of 128 x 128 (more than one round of workgroups, a short
     last one), ragged rows and columns, k = 288 ending in a partial 4-block
-    stage.  The 328 right-most columns are checked in full against the
-    oracle, the rest on samples, and two runs agree bitwise."""
+    stage.  Every output against the oracle, and two runs agree bitwise."""
     m, n = 1000, 8520
     aq = W.random_int8(0, 500, (m, k), seed=1)
     wq = W.random_int8(0, 501, (n, k), seed=2)
     ad = W.random_scales(0, 502, (m, k // 32), seed=3)
     wd = W.random_scales(0, 503, (n, k // 32), seed=4)
     y = run_gemm(aq, ad, wq, wd)
-    sampled_check(y, aq, ad, wq, wd, k, 8, "ragged")
-    mi, nj = np.meshgrid(np.arange(m), np.arange(64 * 128, n), indexing="ij")
-    yr, asum = oracle.qgemm_q8_0_at(aq, ad, wq, wd, mi.ravel(), nj.ravel())
-    assert_within_bound(y[mi.ravel(), nj.ravel()], yr, asum, k // 32, "ragged right columns")
+    yr, asum = oracle.qgemm_q8_0(aq, ad, wq, wd, nthreads=oracle_threads())
+    assert_within_bound(y, yr, asum, k // 32, "ragged")
     y2 = run_gemm(aq, ad, wq, wd)
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+SPECIAL_SCALES = np.array([0x0000, 0x8000, 0x0001, 0x0002, 0x0155, 0x03FF, 0x0400, 0x8001,
+                           0x83FF, 0xB400, 0x7BFF >> 3, 0x3C00], np.uint16)
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 256, 300), (3, 1024, 70), (12, 2048, 520),
+                                   (300, 256, 300), (40, 4160, 130)])
+def test_qgemm_zero_and_subnormal_scales(m, k, n):
+    """fp16 scales that the quantizer can emit but the random-scale tests never
+    draw: +0, -0, subnormals (down to 2^-24), the smallest normal, and a few
+    negative and ordinary values, mixed at random over both operands (every
+    kernel: the dot4 and MFMA thin-M GEMVs, the MFMA GEMM).  The fp16 -> fp32
+    conversions keep subnormals and the products stay far above the fp32
+    subnormal range, so the usual bound holds."""
+    g = np.random.default_rng(zlib.crc32(b"special scales") + m)
+    aq = W.random_int8(0, 520 + m, (m, k), seed=k)
+    wq = W.random_int8(0, 521 + n, (n, k), seed=k)
+    ad = g.choice(SPECIAL_SCALES, size=(m, k // 32))
+    wd = g.choice(SPECIAL_SCALES, size=(n, k // 32))
+    y = run_gemm(aq, ad, wq, wd)
+    yr, asum = oracle.qgemm_q8_0(aq, ad, wq, wd, nthreads=oracle_threads())
+    assert_within_bound(y, yr, asum, k // 32, "special scales m=%d k=%d n=%d" % (m, k, n))
+    zero_rows = (ad.view(np.float16) == 0).all(1)
+    assert (y[zero_rows] == 0).all()
 
 
 # ---------------------------------------------------------------------------
@@ -426,6 +454,9 @@ def test_route_topk_bitexact():
     check_route(np.zeros((1000, 1), np.int32), 3)          # one expert takes all
     check_route(np.full((5, 2), 99, np.int32), 4)          # all invalid
     check_route(np.zeros((0, 8), np.int32).reshape(0, 8), 16)
+    # the largest single pass (8192 routed rows) and the first chunked one
+    check_route(W.topk_ids(1024, 8, 128, seed=6), 128)
+    check_route(W.topk_ids(1025, 8, 128, seed=7), 128)
 
 
 def run_grouped(qa, da, ids, packed, wsc):
@@ -515,6 +546,100 @@ def test_grouped_w4a8_moe_workload_full(weights):
     y2 = host(bqi.qgemm_w4a8_grouped(qa_g, da_g, dev_tensor(ids), dev_tensor(packed),
                                      dev_tensor(wsc)))
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+def grouped_one_hot_probe(T, top_k, E, K, N, seed):
+    """One-hot-block probe through the grouped W4A8 path: token t's
+    activation codes are nonzero only in group t % nb and every scale is a
+    power of two, so each output is 2^-6 * P exactly, where P is the int32
+    dot product of that group with the unpacked weight codes (c - 8); P is
+    read back and compared bit-exactly with the oracle's block dots."""
+    nb = K // 32
+    g = np.random.default_rng(seed)
+    ids = W.topk_ids(T, top_k, E, seed=seed)
+    aq = W.random_int8("moe", 740, (T, K), seed=seed)
+    keep = (np.arange(K)[None, :] // 32) == (np.arange(T)[:, None] % nb)
+    aq = np.where(keep, aq, 0).astype(np.int8)
+    packed = g.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    ad = np.full((T, nb), 0x3400, np.uint16)        # 2^-2
+    wsc = np.full((E, N, nb), 0x2C00, np.uint16)    # 2^-4
+    y = run_grouped(aq, ad, ids, packed, wsc)
+    wcodes = (oracle.unpack_w4(packed).astype(np.int16) - 8).astype(np.int8)
+    want = np.zeros((T, top_k, N), np.int64)
+    for e in range(E):
+        t, j = np.nonzero(ids == e)
+        if t.size == 0:
+            continue
+        P = oracle.block_dots(aq[t], wcodes[e])                  # [rows][N][nb]
+        want[t, j] = P[np.arange(t.size), :, t % nb]
+    got = y.astype(np.float64) * 64.0
+    assert np.array_equal(got, want.astype(np.float64))
+
+
+@pytest.mark.parametrize("T,top_k,E,K,N", [
+    (160, 4, 16, 256, 96),     # k_grouped_w4a8: ~40 rows per expert (one 32-row tile or two)
+    (300, 2, 4, 2048, 130),    # k_grouped_w4a8: ~150 rows per expert (two 96-row chunks), ragged N
+    (12, 8, 32, 256, 96),      # k_grouped_gemv: 96 routed rows
+    (16, 8, 128, 2048, 768)])  # k_grouped_gemv at the MoE expert shape (128 routed rows)
+def test_grouped_block_dots_bitexact_probe(T, top_k, E, K, N):
+    log("grouped probe T=%d top_k=%d E=%d K=%d N=%d" % (T, top_k, E, K, N))
+    grouped_one_hot_probe(T, top_k, E, K, N, seed=T + K)
+
+
+def test_grouped_w4a8_beyond_one_routing_chunk():
+    """2048 tokens x top-8 of 128 experts: 16384 routed rows, more than the
+    8192 that the routing pass holds in registers, so it counts and places
+    chunk by chunk (and copies the scale table per chunk).  A few invalid ids
+    exercise the strided zeroing of their output rows.  route_topk is
+    compared bit-exactly, the full K=2048, N=768 output against the oracle."""
+    T, tk, E, K, N = 2048, 8, 128, 2048, 768
+    ids = W.topk_ids(T, tk, E, seed=17)
+    ids[5, 3] = -1
+    ids[1000:1003, 2] = -5
+    ids[1500, 0] = E
+    ids[2047, 7] = 10 ** 6
+    log("grouped, 16384 routed rows: routing")
+    check_route(ids, E)
+    qa, da = oracle.quantize_q8_0(W.activations("moe", T, K, seed=17))
+    packed, wsc = W.random_w4_codes(E, N, K, seed=17)
+    log("grouped, 16384 routed rows: gemm")
+    y = run_grouped(qa, da, ids, packed, wsc)
+    log("grouped, 16384 routed rows: oracle")
+    yr, asum = oracle.qgemm_w4a8_grouped(qa, da, ids, packed, wsc, nthreads=oracle_threads())
+    assert_within_bound(y, yr, asum, K // 32, "16384 routed rows")
+    bad = (ids < 0) | (ids >= E)
+    assert bad.sum() == 6 and (y[bad] == 0).all()
+
+
+def test_wrappers_on_an_explicit_side_stream():
+    """Every wrapper given a stream other than the current one (a
+    torch.cuda.Stream, and a raw hipStream_t handle) allocates its outputs and
+    workspace on that stream and gives the same bits as on the current
+    stream."""
+    T, tk, E, K, N = 200, 4, 8, 256, 96
+    x = dev_tensor(W.activations("moe", T, K, seed=23))
+    ids = dev_tensor(W.topk_ids(T, tk, E, seed=23))
+    packed, wsc = W.random_w4_codes(E, N, K, seed=23)
+    packed, wsc = dev_tensor(packed), dev_tensor(wsc)
+    wq, wd = bqi.quantize_q8_0(dev_tensor(W.weights("moe", 64, K, seed=23)))
+
+    def run(stream):
+        q, d = bqi.quantize_q8_0(x, stream=stream)
+        y1 = bqi.qgemm_q8_0(q, d, wq, wd, stream=stream)
+        y2 = bqi.qgemm_w4a8_grouped(q, d, ids, packed, wsc, stream=stream)
+        c, o, r = bqi.route_topk(ids, E, stream=stream)
+        return [q, d, y1, y2, c, o, r]
+
+    ref = run(None)
+    torch.cuda.synchronize()
+    for make in (lambda s: s, lambda s: s.cuda_stream):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        outs = run(make(side))
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for a, b in zip(ref, outs):
+            assert torch.equal(a, b)
 
 
 # ---------------------------------------------------------------------------
@@ -620,7 +745,7 @@ def test_grouped_decode_workload(T, weights):
 
 @pytest.mark.parametrize("case", ["crowded", "invalid_and_dups", "ragged", "k_large"])
 def test_grouped_decode_cases(case):
-    g = np.random.default_rng(hash(case) % 1000)
+    g = np.random.default_rng(zlib.crc32(case.encode()))
     if case == "crowded":          # 16 tokens on the same 8 experts: 16 rows each
         T, tk, E, K, N = 16, 8, 64, 256, 96
         ids = np.tile(np.arange(8, dtype=np.int32), (T, 1))
@@ -632,8 +757,8 @@ def test_grouped_decode_cases(case):
     elif case == "ragged":         # K shorter than 64 groups, N not a multiple of 16
         T, tk, E, K, N = 3, 4, 9, 96, 130
         ids = g.integers(0, E, (T, tk)).astype(np.int32)
-    else:                          # K past the GEMV stage limit: the MFMA path on few rows
-        T, tk, E, K, N = 2, 8, 32, 4096, 64
+    else:                          # long K, 160 routed rows: the MFMA path, ~5 rows per expert
+        T, tk, E, K, N = 20, 8, 32, 4096, 64
         ids = W.topk_ids(T, tk, E, seed=9)
     qa = W.random_int8("moe", 710, (T, K), seed=K)
     da = W.random_scales("moe", 711, (T, K // 32), seed=K)

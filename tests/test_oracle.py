@@ -386,6 +386,37 @@ def test_w4_quantizer_bounds():
         assert f16_value(d[blk, 0]) == dq
 
 
+def test_w4_quantizer_ties_closed_form():
+    """Round half away from zero in the 4-bit quantizer, from closed forms:
+    element 0 of each group is 7 d, which makes the group's scale exactly d
+    (7 d and d are exact in fp32, and 7 d / 7 = d has no rounding); every
+    other element is +-(k + 1/2) d (k = 0..6, exact: at most 4 + 11
+    significant bits) or its fp32 neighbour toward or away from zero.  The
+    code is 8 +- (k + 1) at and beyond the midpoint, 8 +- k below it.  A
+    round-to-even quantizer differs at k = 0, 2, 4, 6."""
+    g = np.random.default_rng(13)
+    dbits = np.arange(0x0800, 0x7000, 53, dtype=np.uint16)      # normal fp16 scales
+    d = dbits.view(np.float16).astype(np.float32)
+    ng = d.size
+    k = g.integers(0, 7, size=(ng, 31))
+    side = g.integers(0, 3, size=(ng, 31))                       # 0 toward zero, 1 tie, 2 away
+    sign = g.choice(np.array([-1.0, 1.0], np.float32), size=(ng, 31))
+    mid = ((k + 0.5) * d[:, None]).astype(np.float32)
+    assert np.array_equal(mid.astype(np.float64), (k + 0.5) * d[:, None].astype(np.float64))
+    x = np.where(side == 0, np.nextafter(mid, np.float32(0)),
+                 np.where(side == 2, np.nextafter(mid, np.float32(np.inf)), mid))
+    w = np.concatenate([(np.float32(7) * d)[:, None], (x * sign).astype(np.float32)], 1)
+    p, dq = oracle.quantize_w4(w.astype(np.float32))
+    assert np.array_equal(dq.reshape(-1), dbits)
+    c = oracle.unpack_w4(p).astype(np.int64)
+    want = 8 + np.where(side == 0, k, k + 1) * sign.astype(np.int64)
+    assert (c[:, 0] == 15).all()
+    assert np.array_equal(c[:, 1:], want)
+    # the ties alone: 8 +- (k + 1), never the even neighbour
+    tie = side == 1
+    assert np.array_equal(np.abs(c[:, 1:][tie] - 8), (k + 1)[tie])
+
+
 def test_route_topk_properties():
     ids = W.topk_ids(97, 8, 16, seed=3)
     ids[5, 2] = -1
