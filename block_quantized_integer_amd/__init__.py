@@ -34,7 +34,7 @@ BQI_F32, BQI_F16 = 0, 1
 SYMBOLS = ("bqi_status_string", "bqi_abi_version", "quantize_q8_0", "qgemm_q8_0",
            "quantize_qgemm_q8_0", "route_topk", "qgemm_w4a8_grouped_workspace_size",
            "qgemm_w4a8_grouped", "moe_combine_f32", "gguf_q8_0_to_planar",
-           "gguf_q4_0_to_planar", "qgemm_w4a8_grouped_host")
+           "gguf_q4_0_to_planar", "qgemm_w4a8_grouped_host", "qgemm_w4a8_grouped_noalloc")
 
 _lib = None
 
@@ -80,6 +80,8 @@ def lib() -> C.CDLL:
     L.qgemm_w4a8_grouped.restype = I32
     L.qgemm_w4a8_grouped.argtypes = [P, P, I64, P, I64, P, P, I64, I64, I64, P, P,
                                      C.c_size_t, P]
+    L.qgemm_w4a8_grouped_noalloc.restype = I32
+    L.qgemm_w4a8_grouped_noalloc.argtypes = [P, P, I64, P, I64, P, P, I64, I64, I64, P, P]
     _lib = L
     return L
 
@@ -271,6 +273,33 @@ def qgemm_w4a8_grouped(aq, ad, topk_ids, wq4, wd, y=None, workspace=None, stream
                                   _ptr(wd), E, N, K, _ptr(y), _ptr(workspace),
                                   workspace.numel(), _stream(stream))
     _raise(st, "qgemm_w4a8_grouped")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # BQI_NOALLOC_SCRATCH_BYTES
+
+
+def qgemm_w4a8_grouped_noalloc(aq, ad, topk_ids, wq4, wd, y, stream=None):
+    """qgemm_w4a8_grouped with the library's own per-GPU workspace array: the
+    library allocates nothing (y must be given).  Calls that overlap on one GPU
+    race on that array."""
+    torch = _torch()
+    _check(aq, torch.int8, 2, "aq")
+    _check(ad, torch.int16, 2, "ad")
+    _check(topk_ids, torch.int32, 2, "topk_ids")
+    _check(wq4, torch.uint8, 3, "wq4")
+    _check(wd, torch.int16, 3, "wd")
+    _check(y, torch.float32, 3, "y")
+    T, K = aq.shape
+    top_k = topk_ids.shape[1]
+    E, N, KH = wq4.shape
+    if KH * 2 != K or tuple(ad.shape) != (T, K // 32) or topk_ids.shape[0] != T \
+            or tuple(wd.shape) != (E, N, K // 32) or tuple(y.shape) != (T, top_k, N):
+        raise ValueError("shape mismatch")
+    st = lib().qgemm_w4a8_grouped_noalloc(_ptr(aq), _ptr(ad), T, _ptr(topk_ids), top_k,
+                                          _ptr(wq4), _ptr(wd), E, N, K, _ptr(y),
+                                          _stream(stream))
+    _raise(st, "qgemm_w4a8_grouped_noalloc")
     return y
 
 

@@ -5,6 +5,8 @@
 #include "bqi.h"
 #include "bqi_launch.h"
 
+#include <mutex>
+
 namespace {
 
 constexpr int64_t kQK = 32;
@@ -50,6 +52,98 @@ int qgemm_launch(const int8_t *aq, const uint16_t *ad, int64_t m,
   return hip_status(bqi::launch_gemm_mfma(aq, ad, m, wq, wd, n, k, y, s));
 }
 
+// ---- the allocation-free grouped entry point ---------------------------------
+// Its workspace is this file-scope device array: one copy per GPU, created
+// when the library's code is loaded on that GPU and held until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it
+// is only a stand-in for the symbol); it looks up the array's device address
+// once per device with hipGetSymbolAddress, with that device current, and
+// passes that address.  Calls that overlap on one GPU share the array and
+// race; the routing pass rewrites every entry that the GEMM reads (counts,
+// offsets, rows and the scale-table rows of this call), so nothing needs
+// clearing between calls.
+static __device__ __align__(256) unsigned char scratch[BQI_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+int scratch_for_current_device(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BQI_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return BQI_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return BQI_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BQI_OK;
+}
+
+// The grouped GEMM behind both entry points.  With use_scratch, the
+// workspace is the library's own device array (no allocation); the size
+// check against it comes first, before any HIP call.
+int grouped_impl(const int8_t *aq, const uint16_t *ad, int64_t n_tokens,
+                 const int32_t *topk_ids, int64_t top_k, const uint8_t *wq4,
+                 const uint16_t *wd, int64_t n_experts, int64_t n, int64_t k,
+                 float *y, void *workspace, size_t workspace_bytes,
+                 bool use_scratch, void *stream) {
+  if (n_tokens < 0 || top_k < 0 || n_experts < 0 || n < 0 || k < 0 ||
+      k % kQK != 0)
+    return BQI_ESHAPE;
+  if (n_experts > 65536 || n_tokens * top_k > kMaxRouted || n > kI32Max ||
+      k > kI32Max)
+    return BQI_ESHAPE;
+  const int64_t rows_total = n_tokens * top_k;
+  if (rows_total == 0 || n == 0) return BQI_OK;
+  if (!y || !topk_ids) return BQI_EINVAL;
+  if (n_experts > 0 && n_experts * ((n + 127) / 128) > kI32Max) return BQI_ESHAPE;
+  if (k > 0 && (!aq || !ad)) return BQI_EINVAL;
+  if (k > 0 && n_experts > 0 && (!wq4 || !wd)) return BQI_EINVAL;
+  if (!aligned(y, 4) || !aligned(topk_ids, 4)) return BQI_EALIGN;
+  if (k > 0 && (!aligned(aq, 16) || !aligned(ad, 2))) return BQI_EALIGN;
+  if (k > 0 && n_experts > 0 && (!aligned(wq4, 16) || !aligned(wd, 2)))
+    return BQI_EALIGN;
+  hipStream_t s = as_stream(stream);
+  if (k == 0 || n_experts == 0) {
+    // every valid row is an empty sum, or every row is invalid: y = 0
+    return hip_status(bqi::launch_zero_f32(y, rows_total * n, s));
+  }
+  const WsLayout L = ws_layout(rows_total, n_experts, k);
+  if (use_scratch) {
+    if (L.total > (size_t)BQI_NOALLOC_SCRATCH_BYTES) return BQI_ESHAPE;
+    if (!bqi::grouped_gemv_supported(rows_total, k)) {
+      const int st = scratch_for_current_device(&workspace);
+      if (st != BQI_OK) return st;
+      workspace_bytes = (size_t)BQI_NOALLOC_SCRATCH_BYTES;
+    }
+  } else {
+    if (!workspace || workspace_bytes < L.total) return BQI_EINVAL;
+    if (!aligned(workspace, 256)) return BQI_EALIGN;
+  }
+  // a few routed rows (decode): the v_dot4 GEMV per routed row, which needs
+  // no routing pass and no workspace; otherwise route, then the int8-MFMA
+  // kernel
+  if (bqi::grouped_gemv_supported(rows_total, k))
+    return hip_status(bqi::launch_grouped_gemv(aq, ad, topk_ids, rows_total, top_k,
+                                               wq4, wd, n_experts, n, k, y, s));
+  char *ws = static_cast<char *>(workspace);
+  int32_t *counts = reinterpret_cast<int32_t *>(ws + L.counts);
+  int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
+  int32_t *rows = reinterpret_cast<int32_t *>(ws + L.rows);
+  float *ad32t = reinterpret_cast<float *>(ws + L.ad32t);
+  hipError_t e = bqi::launch_route_topk(topk_ids, rows_total, n_experts, top_k,
+                                        counts, offsets, rows, ad, k, ad32t, y,
+                                        n, s);
+  if (e != hipSuccess) return BQI_EHIP;
+  return hip_status(bqi::launch_grouped_w4a8(aq, ad32t, rows_total, top_k, wq4,
+                                             wd, n_experts, n, k, counts,
+                                             offsets, rows, y, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -58,7 +152,7 @@ const char *bqi_status_string(int status) {
   switch (status) {
     case BQI_OK: return "BQI_OK";
     case BQI_EINVAL: return "BQI_EINVAL: null pointer, bad dtype or workspace too small";
-    case BQI_ESHAPE: return "BQI_ESHAPE: bad size (negative, k not a multiple of 32, ldx < k, too large)";
+    case BQI_ESHAPE: return "BQI_ESHAPE: bad size (negative, k not a multiple of 32, ldx < k, too large; for qgemm_w4a8_grouped_noalloc, a workspace beyond BQI_NOALLOC_SCRATCH_BYTES)";
     case BQI_EALIGN: return "BQI_EALIGN: pointer or leading dimension misaligned";
     case BQI_EHIP: return "BQI_EHIP: HIP runtime error at launch";
     case BQI_ENOTSUP: return "BQI_ENOTSUP: the host CPU lacks AVX2/FMA";
@@ -66,7 +160,7 @@ const char *bqi_status_string(int status) {
   }
 }
 
-int bqi_abi_version(void) { return 230; }
+int bqi_abi_version(void) { return 240; }
 
 int quantize_q8_0(const void *x, int x_dtype, int64_t rows, int64_t k,
                   int64_t ldx, int8_t *q, uint16_t *d, void *stream) {
@@ -175,47 +269,17 @@ int qgemm_w4a8_grouped(const int8_t *aq, const uint16_t *ad, int64_t n_tokens,
                        const uint8_t *wq4, const uint16_t *wd,
                        int64_t n_experts, int64_t n, int64_t k, float *y,
                        void *workspace, size_t workspace_bytes, void *stream) {
-  if (n_tokens < 0 || top_k < 0 || n_experts < 0 || n < 0 || k < 0 ||
-      k % kQK != 0)
-    return BQI_ESHAPE;
-  if (n_experts > 65536 || n_tokens * top_k > kMaxRouted || n > kI32Max ||
-      k > kI32Max)
-    return BQI_ESHAPE;
-  const int64_t rows_total = n_tokens * top_k;
-  if (rows_total == 0 || n == 0) return BQI_OK;
-  if (!y || !topk_ids) return BQI_EINVAL;
-  if (n_experts > 0 && n_experts * ((n + 127) / 128) > kI32Max) return BQI_ESHAPE;
-  if (k > 0 && (!aq || !ad)) return BQI_EINVAL;
-  if (k > 0 && n_experts > 0 && (!wq4 || !wd)) return BQI_EINVAL;
-  if (!aligned(y, 4) || !aligned(topk_ids, 4)) return BQI_EALIGN;
-  if (k > 0 && (!aligned(aq, 16) || !aligned(ad, 2))) return BQI_EALIGN;
-  if (k > 0 && n_experts > 0 && (!aligned(wq4, 16) || !aligned(wd, 2)))
-    return BQI_EALIGN;
-  hipStream_t s = as_stream(stream);
-  if (k == 0 || n_experts == 0) {
-    // every valid row is an empty sum, or every row is invalid: y = 0
-    return hip_status(bqi::launch_zero_f32(y, rows_total * n, s));
-  }
-  const WsLayout L = ws_layout(rows_total, n_experts, k);
-  if (!workspace || workspace_bytes < L.total) return BQI_EINVAL;
-  if (!aligned(workspace, 256)) return BQI_EALIGN;
-  char *ws = static_cast<char *>(workspace);
-  int32_t *counts = reinterpret_cast<int32_t *>(ws + L.counts);
-  int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
-  int32_t *rows = reinterpret_cast<int32_t *>(ws + L.rows);
-  float *ad32t = reinterpret_cast<float *>(ws + L.ad32t);
-  // a few routed rows (decode): the v_dot4 GEMV per routed row, which needs
-  // no routing pass; otherwise route, then the int8-MFMA kernel
-  if (bqi::grouped_gemv_supported(rows_total, k))
-    return hip_status(bqi::launch_grouped_gemv(aq, ad, topk_ids, rows_total, top_k,
-                                               wq4, wd, n_experts, n, k, y, s));
-  hipError_t e = bqi::launch_route_topk(topk_ids, rows_total, n_experts, top_k,
-                                        counts, offsets, rows, ad, k, ad32t, y,
-                                        n, s);
-  if (e != hipSuccess) return BQI_EHIP;
-  return hip_status(bqi::launch_grouped_w4a8(aq, ad32t, rows_total, top_k, wq4,
-                                             wd, n_experts, n, k, counts,
-                                             offsets, rows, y, s));
+  return grouped_impl(aq, ad, n_tokens, topk_ids, top_k, wq4, wd, n_experts, n,
+                      k, y, workspace, workspace_bytes, false, stream);
+}
+
+int qgemm_w4a8_grouped_noalloc(const int8_t *aq, const uint16_t *ad,
+                               int64_t n_tokens, const int32_t *topk_ids,
+                               int64_t top_k, const uint8_t *wq4,
+                               const uint16_t *wd, int64_t n_experts,
+                               int64_t n, int64_t k, float *y, void *stream) {
+  return grouped_impl(aq, ad, n_tokens, topk_ids, top_k, wq4, wd, n_experts, n,
+                      k, y, nullptr, 0, true, stream);
 }
 
 int moe_combine_f32(const float *y, const float *p, int64_t n_tokens,

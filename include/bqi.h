@@ -72,10 +72,10 @@ extern "C" {
 /* Human-readable name of a status code (static string, never NULL). */
 BQI_API const char *bqi_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor): 230.  Version 200 added
+/* ABI version of this header (major * 100 + minor): 240.  Version 200 added
  * the k argument of qgemm_w4a8_grouped_workspace_size; 210 added
  * quantize_qgemm_q8_0; 220 added moe_combine_f32 and the GGUF import; 230
- * added qgemm_w4a8_grouped_host. */
+ * added qgemm_w4a8_grouped_host; 240 added qgemm_w4a8_grouped_noalloc. */
 BQI_API int bqi_abi_version(void);
 
 /*
@@ -207,6 +207,33 @@ BQI_API int qgemm_w4a8_grouped(const int8_t *aq, const uint16_t *ad, int64_t n_t
                        const uint8_t *wq4, const uint16_t *wd,
                        int64_t n_experts, int64_t n, int64_t k, float *y,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Size of the device array that qgemm_w4a8_grouped_noalloc uses as its
+ * workspace: 16 MiB per GPU the library runs on. */
+#define BQI_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * qgemm_w4a8_grouped_noalloc -- qgemm_w4a8_grouped for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments (without the workspace),
+ * same kernels, same results.
+ *
+ * The workspace is a device array inside the library, BQI_NOALLOC_SCRATCH_BYTES
+ * per GPU, created when the library is first used on that GPU and held until
+ * the process ends; this call allocates nothing.  The caller still passes the
+ * inputs and y.  Problems whose workspace
+ * (qgemm_w4a8_grouped_workspace_size) exceeds the array return BQI_ESHAPE
+ * before anything is launched (e.g. k = 2048 fits up to about 62,000 routed
+ * rows).  The array belongs to the current device: `stream` must be a stream
+ * of that device.  Calls that overlap on one GPU (several host threads, or
+ * several streams) share the array and race; serialize them.  Up to 128
+ * routed rows need no workspace and never touch the array.
+ */
+BQI_API int qgemm_w4a8_grouped_noalloc(const int8_t *aq, const uint16_t *ad,
+                               int64_t n_tokens, const int32_t *topk_ids,
+                               int64_t top_k, const uint8_t *wq4,
+                               const uint16_t *wd, int64_t n_experts,
+                               int64_t n, int64_t k, float *y, void *stream);
 
 /*
  * moe_combine_f32 -- the MoE combine after the grouped GEMM: each token's

@@ -43,7 +43,7 @@ def test_library_exports_exactly_the_header_symbols():
 
 def test_status_strings():
     L = bqi.lib()
-    assert L.bqi_abi_version() == 230
+    assert L.bqi_abi_version() == 240
     for st in (OK, EINVAL, ESHAPE, EALIGN, bqi.BQI_EHIP):
         assert L.bqi_status_string(st).decode().startswith("BQI_")
     assert L.bqi_status_string(12345)
@@ -186,6 +186,35 @@ def test_grouped_validation_and_workspace():
     assert w(y=FAKE + 1) == EALIGN
     assert w(T=0) == OK
     assert w(n=0) == OK
+
+
+def test_grouped_noalloc_validation():
+    """The allocation-free grouped entry point checks its arguments like the
+    workspace one, and rejects a problem whose workspace exceeds the library's
+    array before any HIP call (so these run without a GPU)."""
+    L = bqi.lib()
+
+    def w(aq=FAKE, ad=FAKE, T=4, ids=FAKE, tk=2, wq=FAKE, wd=FAKE, E=3, n=16, k=64, y=FAKE):
+        return L.qgemm_w4a8_grouped_noalloc(P(aq), P(ad), T, P(ids), tk, P(wq), P(wd), E, n, k,
+                                            P(y), P(0))
+    assert w(k=48) == ESHAPE
+    assert w(T=-1) == ESHAPE
+    assert w(E=65537) == ESHAPE
+    assert w(y=0) == EINVAL
+    assert w(ids=0) == EINVAL
+    assert w(aq=0) == EINVAL
+    assert w(wq=0) == EINVAL
+    assert w(aq=FAKE + 4) == EALIGN
+    assert w(y=FAKE + 1) == EALIGN
+    assert w(T=0) == OK
+    assert w(n=0) == OK
+    limit = bqi.NOALLOC_SCRATCH_BYTES
+    # the largest token count whose workspace fits, and one more, at k = 2048
+    fits = max(t for t in range(60000, 64000, 8)
+               if L.qgemm_w4a8_grouped_workspace_size(t, 1, 128, 2048) <= limit)
+    assert L.qgemm_w4a8_grouped_workspace_size(fits + 1000, 1, 128, 2048) > limit
+    assert w(T=fits + 1000, tk=1, E=128, n=768, k=2048) == ESHAPE
+    assert w(T=1 << 16, tk=8, E=128, n=768, k=2048) == ESHAPE
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
