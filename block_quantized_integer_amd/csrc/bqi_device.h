@@ -12,6 +12,7 @@ namespace bqi {
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int QK = 32;  // elements per Q8_0 block / W4 group along K
 

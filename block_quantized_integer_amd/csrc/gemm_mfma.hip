@@ -109,42 +109,80 @@ __global__ __launch_bounds__(THREADS, 2) void k_gemm_mfma(
   // ---- stage loads -----------------------------------------------------------
   // Wave load q fills tile rows rt .. rt+7 (rt = 8*(4*wave + q)); lane L lands
   // in LDS slot L: row rt + L/8, physical chunk L%8, which holds logical chunk
-  // (L%8) ^ swizzle(row).  Rows past m (n) re-read the last row and chunks
-  // past k re-read chunk 0 (such blocks are never used), so every load stays
-  // in bounds.  Offsets are 32-bit (the ABI layer guarantees m*k, n*k < 2^31)
-  // and recomputed per stage rather than kept in registers.
+  // (L%8) ^ swizzle(row).  Rows past m (n) re-read the last row, so every
+  // load stays in bounds.  The loads take a wave-uniform 64-bit base in
+  // SGPRs (the operand pointer advanced to the stage's first byte) and a
+  // loop-invariant 32-bit lane offset (the ABI layer guarantees m*k, n*k <
+  // 2^31), so a full stage issues its loads with no per-lane address
+  // arithmetic.  In a short last stage, chunks past k re-read the row's last
+  // chunk instead (their blocks get scale 0 below), which keeps every offset
+  // non-negative and inside the row.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy
+  int aoff[LOADS_PER_WAVE], woff[LOADS_PER_WAVE], c16[LOADS_PER_WAVE];
+#pragma unroll
+  for (int q = 0; q < LOADS_PER_WAVE; ++q) {
+    const int r = ROWS_PER_LOAD * (LOADS_PER_WAVE * wave + q) + lane / CPR;
+    c16[q] = 16 * ((lane % CPR) ^ ((r >> 1) & 7));
+    aoff[q] = min(m0 + r, m - 1) * k + c16[q];
+    woff[q] = min(n0 + r, n - 1) * k + c16[q];
+  }
+  // scales: thread -> (row, block) pairs tid + THREADS*h; a short last stage
+  // clamps the block to the row's last one (its scale is replaced by 0)
+  int sa_off[SCALES_PER_THREAD], sw_off[SCALES_PER_THREAD];
+#pragma unroll
+  for (int h = 0; h < SCALES_PER_THREAD; ++h) {
+    const int c = tid + THREADS * h;
+    const int row = c / NBS, blk = c % NBS;
+    sa_off[h] = min(m0 + row, m - 1) * nbk + blk;
+    sw_off[h] = min(n0 + row, n - 1) * nbk + blk;
+  }
   uint16_t sa_reg[SCALES_PER_THREAD], sw_reg[SCALES_PER_THREAD];
   auto issue_stage = [&](int s, int buf) {
     const int k0 = s * BK;
+    const bool full = k0 + BK <= k;  // uniform
+    const int8_t *abase = aq + k0, *wbase = wq + k0;
 #pragma unroll
     for (int q = 0; q < LOADS_PER_WAVE; ++q) {
-      const int rt = ROWS_PER_LOAD * (LOADS_PER_WAVE * wave + q);  // wave-uniform
-      const int r = rt + lane / CPR;
-      const int c = (lane % CPR) ^ ((r >> 1) & 7);
-      const int kk = k0 + 16 * c < k ? k0 + 16 * c : 0;
-      load_lds16(aq + (min(m0 + r, m - 1) * k + kk), &T[buf].a[rt * BK]);
-      load_lds16(wq + (min(n0 + r, n - 1) * k + kk), &T[buf].w[rt * BK]);
+      int ao = aoff[q], wo = woff[q];
+      if (!full) {
+        const int fix = min(c16[q], k - 16 - k0) - c16[q];
+        ao += fix;
+        wo += fix;
+      }
+      const uint32_t lds_a = lds_addr(&T[buf].a[ROWS_PER_LOAD * (LOADS_PER_WAVE * wave_u + q) * BK]);
+      const uint32_t lds_w = lds_addr(&T[buf].w[ROWS_PER_LOAD * (LOADS_PER_WAVE * wave_u + q) * BK]);
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(ao), "s"(abase), "{m0}"(lds_a) : "memory");
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(wo), "s"(wbase), "{m0}"(lds_w) : "memory");
     }
+    const uint16_t *sabase = ad + s * NBS, *swbase = wd + s * NBS;
 #pragma unroll
     for (int h = 0; h < SCALES_PER_THREAD; ++h) {
-      const int c = tid + THREADS * h;
-      const int row = c / NBS, blk = c % NBS;
-      const int kb = s * NBS + blk < nbk ? s * NBS + blk : 0;
-      sa_reg[h] = ad[min(m0 + row, m - 1) * nbk + kb];
-      sw_reg[h] = wd[min(n0 + row, n - 1) * nbk + kb];
+      int ao = sa_off[h], wo = sw_off[h];
+      if (!full) {
+        const int blk = (tid + THREADS * h) % NBS;
+        const int fix = min(blk, nbk - 1 - s * NBS) - blk;
+        ao += fix;
+        wo += fix;
+      }
+      sa_reg[h] = sabase[(uint32_t)ao];
+      sw_reg[h] = swbase[(uint32_t)wo];
     }
   };
-  auto store_scales = [&](int buf) {
+  // Blocks past k (a short last stage) get activation scale 0: the stage
+  // loop always runs all NBS blocks, and such a block's term
+  // fma(t, 0, acc) leaves acc unchanged (t is finite, and acc, which starts
+  // at +0 and only ever gains round-to-nearest sums, is never -0).
+  auto store_scales = [&](int s, int buf) {
 #pragma unroll
     for (int h = 0; h < SCALES_PER_THREAD; ++h) {
       const int c = tid + THREADS * h;
       const int row = c / NBS, blk = c % NBS;
-      T[buf].ad[blk][row] = half_bits_to_float(sa_reg[h]);
+      const bool valid = s * NBS + blk < nbk;
+      T[buf].ad[blk][row] = valid ? half_bits_to_float(sa_reg[h]) : 0.0f;
       T[buf].wd[row][blk] = half_bits_to_float(sw_reg[h]);
     }
   };
-
-  float acc[2][2][16];
+  f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -157,8 +195,8 @@ __global__ __launch_bounds__(THREADS, 2) void k_gemm_mfma(
   for (int r = 0; r < 16; ++r) seed[r] = MAGIC_BITS;
 
   issue_stage(0, 0);
-  store_scales(0);
-  __builtin_amdgcn_s_waitcnt(0);  // direct loads of stage 0 have landed
+  store_scales(0, 0);
+  wait_vmcnt<0>();  // direct loads of stage 0 have landed
   __syncthreads();
 
   for (int s = 0; s < stages; ++s) {
@@ -166,7 +204,12 @@ __global__ __launch_bounds__(THREADS, 2) void k_gemm_mfma(
     const Tiles &TB = T[buf];
     if (s + 1 < stages) issue_stage(s + 1, buf ^ 1);
 
-    float dwf[2][NBS];
+    // The stage's 16 MFMAs (4 blocks x 2x2 tiles) run as a pipeline of depth
+    // one: tile u's MFMA is issued before tile u-1's epilogue, into the other
+    // of two result register sets, so the matrix core works on tile u while
+    // the VALU scales tile u-1.  The block loop is unrolled, so every scale
+    // sits in a register named at compile time.
+    float dwf[2][NBS], ncd[2][NBS];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const f32x4 four = *reinterpret_cast<const f32x4 *>(&TB.wd[wn * 64 + j * 32 + l32][0]);
@@ -174,56 +217,92 @@ __global__ __launch_bounds__(THREADS, 2) void k_gemm_mfma(
       dwf[j][1] = four.y;
       dwf[j][2] = four.z;
       dwf[j][3] = four.w;
-    }
-    const int nb_here = min(NBS, nbk - s * NBS);
-
-    i32x4 af[2], wf[2];
-    float da[2][16];
-    for (int b = 0; b < nb_here; ++b) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + l32;
-        af[i] = *reinterpret_cast<const i32x4 *>(&TB.a[r * BK + swz(r, 2 * b + g) * 16]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = *reinterpret_cast<const f32x4 *>(&TB.ad[b][wm * 64 + i * 32 + 8 * q + 4 * g]);
-          da[i][4 * q + 0] = v.x;
-          da[i][4 * q + 1] = v.y;
-          da[i][4 * q + 2] = v.z;
-          da[i][4 * q + 3] = v.w;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int c = wn * 64 + j * 32 + l32;
-        wf[j] = *reinterpret_cast<const i32x4 *>(&TB.w[c * BK + swz(c, 2 * b + g) * 16]);
-      }
-      // lane-uniform weight scale of this block (b is a runtime value here)
-      float dwb[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        dwb[j] = dwf[j][0];
-#pragma unroll
-        for (int bb = 1; bb < NBS; ++bb)
-          if (b == bb) dwb[j] = dwf[j][bb];
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const i32x16 d = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], wf[j], seed, 0, 0, 0);
-          const float dw = dwb[j];
-          const float ncd = -MAGIC_F * dw;  // exact
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float t = fmaf(bits_to_float(d[r]), dw, ncd);
-            acc[i][j][r] = fmaf(t, da[i][r], acc[i][j][r]);
-          }
-        }
+      for (int b = 0; b < NBS; ++b) ncd[j][b] = -MAGIC_F * dwf[j][b];  // exact
     }
 
-    if (s + 1 < stages) store_scales(buf ^ 1);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
+    // Operands are read from LDS one step ahead of their use: at step u the
+    // wave reads the fragments of tile u+1 that it does not hold yet and the
+    // activation scales that the next epilogues need, so about one tile of
+    // operands is in flight beside the accumulators.
+    //
+    // Each step is pinned in place with empty asm statements (the compiler
+    // otherwise places the pure MFMA and FMA operations anywhere in the
+    // unrolled stage: it issued a dozen MFMAs into separate registers and
+    // spilled).  A step starts with a statement that takes the MFMA's
+    // fragments (so the MFMA cannot move above it) and ends with one that
+    // takes the epilogue's accumulators and the new MFMA result (so neither
+    // can move below it); by then 32 VALU instructions separate the MFMA from
+    // that statement, so reading its result costs no wait.
+    i32x4 af[2], wf[2];        // [row tile], [column tile] of the current block
+    i32x4 af_n, wf_n[2];       // the next block's first row fragment and column fragments
+    float da[2][16];           // activation scales of the block's two row tiles
+    auto read_a = [&](int b, int i) {
+      const int r = wm * 64 + i * 32 + l32;
+      return *reinterpret_cast<const i32x4 *>(&TB.a[r * BK + swz(r, 2 * b + g) * 16]);
+    };
+    auto read_w = [&](int b, int j) {
+      const int c = wn * 64 + j * 32 + l32;
+      return *reinterpret_cast<const i32x4 *>(&TB.w[c * BK + swz(c, 2 * b + g) * 16]);
+    };
+    auto read_da = [&](int b, int i, float (&dst)[16]) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(&TB.ad[b][wm * 64 + i * 32 + 8 * q + 4 * g]);
+        dst[4 * q + 0] = v.x;
+        dst[4 * q + 1] = v.y;
+        dst[4 * q + 2] = v.z;
+        dst[4 * q + 3] = v.w;
+      }
+    };
+    auto epilogue = [&](const i32x16 &d, int u) {
+      const int b = u >> 2, i = (u >> 1) & 1, j = u & 1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float t = fmaf(bits_to_float(d[r]), dwf[j][b], ncd[j][b]);
+        acc[i][j][r] = fmaf(t, da[i][r], acc[i][j][r]);
+      }
+    };
+
+    // tiles of a block in the order (0,0) (0,1) (1,0) (1,1)
+    af[0] = read_a(0, 0);
+    wf[0] = read_w(0, 0);
+    wf[1] = read_w(0, 1);
+    read_da(0, 0, da[0]);
+    i32x16 dres[2];
+#pragma unroll
+    for (int u = 0; u < 4 * NBS; ++u) {
+      const int b = u >> 2, t = u & 3, i = t >> 1, j = t & 1;
+      if (t == 0) af[1] = read_a(b, 1);
+      if (t == 1) read_da(b, 1, da[1]);
+      if (t == 2 && b + 1 < NBS) { af_n = read_a(b + 1, 0); wf_n[0] = read_w(b + 1, 0); }
+      if (t == 3 && b + 1 < NBS) wf_n[1] = read_w(b + 1, 1);
+      asm volatile("" : "+v"(af[i]), "+v"(wf[j]));
+      dres[u & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], wf[j], seed, 0, 0, 0);
+      // within the step: the MFMA first, then the previous tile's epilogue
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (u > 0) {
+        epilogue(dres[(u - 1) & 1], u - 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
+        const int pi = ((u - 1) >> 1) & 1, pj = (u - 1) & 1;
+        asm volatile("" : "+v"(acc[pi][pj]), "+v"(dres[u & 1]));
+      } else {
+        asm volatile("" : "+v"(dres[u & 1]));
+      }
+      if (t == 3 && b + 1 < NBS) {
+        // the next block's fragments become current; its row tile 0 scales
+        // replace this block's (their last use was the epilogue above)
+        af[0] = af_n;
+        wf[0] = wf_n[0];
+        wf[1] = wf_n[1];
+        read_da(b + 1, 0, da[0]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    epilogue(dres[(4 * NBS - 1) & 1], 4 * NBS - 1);
+
+    if (s + 1 < stages) store_scales(s + 1, buf ^ 1);
+    wait_vmcnt<0>();  // this wave's direct loads have landed
     __syncthreads();
   }
 
