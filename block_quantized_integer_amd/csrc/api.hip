@@ -22,23 +22,21 @@ int hip_status(hipError_t e) { return e == hipSuccess ? BQI_OK : BQI_EHIP; }
 
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
-// Workspace layout of qgemm_w4a8_grouped: counts[E], offsets[E+1],
-// rows[T*top_k] (int32), then the expert-ordered fp32 activation-scale table
-// [k/32][grouped_ad32_rows(T*top_k)]; each section starts on a 256-byte
-// boundary.
+// Workspace layout of qgemm_w4a8_grouped: counts[E], offsets[E+1] and
+// rows[T*top_k] (int32), each section on a 256-byte boundary.
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t counts, offsets, rows, ad32t, total;
+  size_t counts, offsets, rows, total;
 };
 
 WsLayout ws_layout(int64_t rows_total, int64_t n_experts, int64_t k) {
+  (void)k;
   WsLayout L;
   L.counts = 0;
   L.offsets = round256((size_t)n_experts * 4);
   L.rows = L.offsets + round256((size_t)(n_experts + 1) * 4);
-  L.ad32t = L.rows + round256((size_t)rows_total * 4);
-  L.total = L.ad32t + round256((size_t)(k / kQK) * (size_t)bqi::grouped_ad32_rows(rows_total) * 4);
+  L.total = L.rows + round256((size_t)rows_total * 4);
   return L;
 }
 
@@ -60,8 +58,8 @@ int qgemm_launch(const int8_t *aq, const uint16_t *ad, int64_t m,
 // once per device with hipGetSymbolAddress, with that device current, and
 // passes that address.  Calls that overlap on one GPU share the array and
 // race; the routing pass rewrites every entry that the GEMM reads (counts,
-// offsets, rows and the scale-table rows of this call), so nothing needs
-// clearing between calls.
+// offsets and the rows of this call), so nothing needs clearing between
+// calls.
 static __device__ __align__(256) unsigned char scratch[BQI_NOALLOC_SCRATCH_BYTES];
 
 constexpr int kMaxDevices = 64;
@@ -101,6 +99,9 @@ int grouped_impl(const int8_t *aq, const uint16_t *ad, int64_t n_tokens,
   if (rows_total == 0 || n == 0) return BQI_OK;
   if (!y || !topk_ids) return BQI_EINVAL;
   if (n_experts > 0 && n_experts * ((n + 127) / 128) > kI32Max) return BQI_ESHAPE;
+  // the MFMA path addresses one expert's packed weights and the activations
+  // with 32-bit offsets
+  if (n * (k / 2) > kI32Max || n_tokens * k > kI32Max) return BQI_ESHAPE;
   if (k > 0 && (!aq || !ad)) return BQI_EINVAL;
   if (k > 0 && n_experts > 0 && (!wq4 || !wd)) return BQI_EINVAL;
   if (!aligned(y, 4) || !aligned(topk_ids, 4)) return BQI_EALIGN;
@@ -134,14 +135,11 @@ int grouped_impl(const int8_t *aq, const uint16_t *ad, int64_t n_tokens,
   int32_t *counts = reinterpret_cast<int32_t *>(ws + L.counts);
   int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
   int32_t *rows = reinterpret_cast<int32_t *>(ws + L.rows);
-  float *ad32t = reinterpret_cast<float *>(ws + L.ad32t);
   hipError_t e = bqi::launch_route_topk(topk_ids, rows_total, n_experts, top_k,
-                                        counts, offsets, rows, ad, k, ad32t, y,
-                                        n, s);
+                                        counts, offsets, rows, y, n, s);
   if (e != hipSuccess) return BQI_EHIP;
-  return hip_status(bqi::launch_grouped_w4a8(aq, ad32t, rows_total, top_k, wq4,
-                                             wd, n_experts, n, k, counts,
-                                             offsets, rows, y, s));
+  return hip_status(bqi::launch_grouped_w4a8(aq, ad, top_k, wq4, wd, n_experts,
+                                             n, k, counts, offsets, rows, y, s));
 }
 
 }  // namespace
@@ -251,8 +249,7 @@ int route_topk(const int32_t *topk_ids, int64_t n_tokens, int64_t top_k,
     return BQI_EALIGN;
   return hip_status(bqi::launch_route_topk(topk_ids, n_tokens * top_k,
                                            n_experts, top_k, counts, offsets,
-                                           rows, nullptr, 0, nullptr, nullptr,
-                                           0, as_stream(stream)));
+                                           rows, nullptr, 0, as_stream(stream)));
 }
 
 size_t qgemm_w4a8_grouped_workspace_size(int64_t n_tokens, int64_t top_k,

@@ -11,26 +11,17 @@
 // expert (its offset) and equal to it, and one workgroup scan orders the
 // matches, so rows come out in increasing row order.  Up to 8192 routed rows
 // this is a single pass over ids held in registers; beyond, a counting pass
-// and a placing pass run chunk by chunk.  No atomics, deterministic.  For the grouped GEMM the same kernel also
-// copies the activation scales of the routed rows, converted to fp32, into a
-// block-major table in expert order (one 4-byte entry per routed row and
-// block), which the GEMM then streams into LDS without conversion.
+// and a placing pass run chunk by chunk.  No atomics, deterministic.  The
+// same pass writes zeros to the output rows of invalid ids.
 //
-// GEMM (k_grouped_w4a8): one workgroup of 12 waves per (expert, 384-column
-// tile); each wave owns 32 output columns.  K advances 4 groups (128
-// elements) per stage through three LDS buffers, two stages in flight.  Every
-// operand travels HBM/L2 -> LDS through gfx950's direct loads: the packed
-// weights (64 bytes per column and stage), their fp16 scales, the routed
-// activation rows (gathered by token, 128 bytes per row and stage) and the
-// fp32 activation scales.  The products run on v_mfma_i32_32x32x32_i8 (one
-// instruction = one 32x32 tile for exactly one group); on gfx950 it costs
-// about as many cycles as the 16x16x32 form while doing four times the MACs,
-// and MFMA and VALU time largely add up in this kernel.  Per group a lane
-// unpacks its 16 codes (low or high nibbles by lane half) into the int8
-// values 16*(c - 8) with a shift, a mask and an xor; the factor 16 is folded
-// into the weight scale.  The scale epilogue is the one of the Q8_0
-// MFMA GEMM (one rounding per term).  Routed rows are taken 96 at a time (six
-// 16-row tiles), so an expert's weights are streamed once per 96 rows.
+// GEMM (k_grouped_w4a8): one workgroup of 4 waves per (expert, 128-column
+// tile), three per CU, heaviest expert first; the weights are the MFMA's A
+// operand and the gathered activation rows its B operand (details below).
+// The products run on v_mfma_i32_32x32x32_i8 (one instruction = one 32x32
+// tile for exactly one group).  Per group a lane unpacks its 16 codes (low or
+// high nibbles by lane half) into the int8 values 16*(c - 8) with a shift, a
+// mask and an xor; the factor 16 is folded into the weight scale.  The scale
+// epilogue is the one of the Q8_0 MFMA GEMM (one rounding per term).
 #include "bqi_device.h"
 #include "bqi_launch.h"
 
@@ -67,81 +58,11 @@ __device__ __forceinline__ int route_scan(int v, int *s_tmp, int &total) {
   return wave_base + incl - v;
 }
 
-// Copy the activation scales of this expert's `total` matched rows (routed
-// rows s_match[0 .. total)) into the block-major fp32 table at positions
-// base .. base+total-1.  Tiles of up to 96 rows x 64 groups go through LDS:
-// each thread reads 8 consecutive scales of one row with one 16-byte load
-// (4 two-byte loads for 64-row tiles where the scale rows are not 16-byte
-// aligned), and each 16 threads write 16 consecutive positions of one table
-// row, instead of scattering 2-byte reads over every matched token per table
-// row.  An expert's rows rarely exceed 96, so its gather is one round trip.
-constexpr int RC_ROWS = 96;            // routed rows per tile (16-byte path)
-constexpr int RC_PITCH = RC_ROWS + 1;  // floats per group row of the tile
-
-__device__ __forceinline__ void route_copy_scales(const int *s_match, int total, int base,
-                                                  int top_k, const uint16_t *ad,
-                                                  int nbk, float *__restrict__ ad32t, int rpad,
-                                                  float *s_t) {
-  const int tid = threadIdx.x;
-  const bool vec = nbk % 8 == 0 && ((uintptr_t)ad & 15) == 0;
-  const int tile_rows = vec ? RC_ROWS : 64;
-  for (int i0 = 0; i0 < total; i0 += tile_rows) {
-    for (int b0 = 0; b0 < nbk; b0 += 64) {
-      if (vec) {
-        // thread -> row i0 + tid/8, groups b0 + 8*(tid%8) .. +7
-        const int r = tid >> 3, c = 8 * (tid & 7);
-        const int i = i0 + r;
-        if (r < RC_ROWS && i < total && b0 + c < nbk) {
-          const uint4 v = *reinterpret_cast<const uint4 *>(ad + (int64_t)(s_match[i] / top_k) * nbk + b0 + c);
-          const uint32_t h2[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            s_t[(c + 2 * u) * RC_PITCH + r] = half_bits_to_float((uint16_t)(h2[u] & 0xffffu));
-            s_t[(c + 2 * u + 1) * RC_PITCH + r] = half_bits_to_float((uint16_t)(h2[u] >> 16));
-          }
-        }
-      } else {
-        // thread -> row i0 + tid/16, groups b0 + 4*(tid%16) .. +3
-        const int r = tid >> 4, c = 4 * (tid & 15);
-        const int i = i0 + r;
-        if (i < total) {
-          const uint16_t *src = ad + (int64_t)(s_match[i] / top_k) * nbk;
-          // the four loads are unconditional (clamped to the row) so that
-          // they are in flight together; the values are masked afterwards
-          uint16_t h[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) h[u] = src[min(b0 + c + u, nbk - 1)];
-          __asm__ volatile("" ::: "memory");
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (b0 + c + u < nbk) s_t[(c + u) * RC_PITCH + r] = half_bits_to_float(h[u]);
-        }
-      }
-      __syncthreads();
-      {
-        // thread -> table row b0 + tid/16, positions i0 + (tid%16) + 16*u
-        const int c = tid >> 4, r = tid & 15;
-        if (b0 + c < nbk) {
-          float *dst = ad32t + (int64_t)(b0 + c) * rpad + base + i0;
-#pragma unroll
-          for (int u = 0; u < RC_ROWS / 16; ++u)
-            if (16 * u < tile_rows && i0 + r + 16 * u < total)
-              dst[r + 16 * u] = s_t[c * RC_PITCH + r + 16 * u];
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
 __global__ __launch_bounds__(RT) void k_route(
     const int32_t *__restrict__ ids, int rows_total, int n_experts, int top_k,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ rows, const uint16_t *ad, int nbk,
-    float *__restrict__ ad32t, int rpad, float *__restrict__ y, int n) {
+    int32_t *__restrict__ rows, float *__restrict__ y, int n) {
   __shared__ int s_tmp[RT / 64];
-  __shared__ int s_match[RCHUNK];  // (position - chunk base) -> routed row
-  __shared__ float s_t[64 * RC_PITCH];  // transpose tile of the scale copy
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
 
@@ -172,7 +93,6 @@ __global__ __launch_bounds__(RT) void k_route(
     for (int j = 0; j < RPT; ++j) {
       if (v[j] == e) {
         rows[n_below + pos] = r0 + j;
-        s_match[pos] = r0 + j;
         ++pos;
       }
       // invalid ids: workgroup (row mod E) zeroes the output row
@@ -180,10 +100,6 @@ __global__ __launch_bounds__(RT) void k_route(
       if (y != nullptr && r < rows_total && (v[j] < 0 || v[j] >= n_experts) &&
           r % n_experts == e)
         for (int c = 0; c < n; ++c) y[(int64_t)r * n + c] = 0.0f;
-    }
-    if (ad32t != nullptr && n_eq > 0) {
-      __syncthreads();
-      route_copy_scales(s_match, n_eq, n_below, top_k, ad, nbk, ad32t, rpad, s_t);
     }
     return;
   }
@@ -210,8 +126,7 @@ __global__ __launch_bounds__(RT) void k_route(
     if (e == n_experts - 1) offsets[n_experts] = n_below + n_eq;
   }
 
-  // pass 2: place the matches in increasing row order; with ad32t, also copy
-  // their activation scales (fp16 -> fp32) into the block-major table
+  // pass 2: place the matches in increasing row order
   int base = n_below;
   for (int c0 = 0; c0 < rows_total && base < n_below + n_eq; c0 += RCHUNK) {
     const int r0 = c0 + tid * RPT;
@@ -228,14 +143,8 @@ __global__ __launch_bounds__(RT) void k_route(
     for (int j = 0; j < RPT; ++j)
       if (v[j] == e) {
         rows[base + pos] = r0 + j;
-        s_match[pos] = r0 + j;
         ++pos;
       }
-    if (ad32t != nullptr) {
-      __syncthreads();
-      route_copy_scales(s_match, total, base, top_k, ad, nbk, ad32t, rpad, s_t);
-      __syncthreads();
-    }
     base += total;
   }
 
@@ -250,25 +159,59 @@ __global__ __launch_bounds__(RT) void k_route(
 }
 
 // ------------------------------------------------------------ grouped GEMM --
-constexpr int GW = 12;             // waves per workgroup
+// One workgroup of GW = 4 waves per (expert, 128-column tile).  The MFMA runs with the weights as the A operand (lane = output
+// column, K half) and the gathered activation rows as the B operand (lane =
+// routed row), so in the output a lane holds one routed row and its registers
+// hold 16 columns: the activation scale is lane-uniform (one per row tile and
+// group) and the weight scales, one per register, are shared by every row
+// tile of the wave.  Routed rows are taken 64 at a time (two 32-row tiles);
+// an expert with more rows streams its weights again for the next 64 (mostly
+// from the Infinity Cache, which holds all the experts' weights).
+//
+// Three workgroups share a CU (12 waves, 168 VGPRs each), so the MoE
+// workload's 768 (expert, column tile) units run in one round.  Workgroups
+// are dispatched heaviest expert first: each workgroup ranks the experts by
+// routed-row count (descending, ties by index) and takes the expert of rank
+// blockIdx / column_tiles, which spreads the experts of more than 64 rows
+// (two chunks) over different CUs.
+//
+// Stages of GNB = 4 groups (128 K elements) go through two LDS buffers: the
+// loads of stage s+1 are issued before the compute of stage s.  Per stage
+// and thread: two 16-byte direct loads of packed weights and R of gathered
+// activation rows (the chunk's 32R rows), and 2-byte direct loads of
+// activation scales (ceil(R/2)) and weight scales (two), zero-extended into
+// 4-byte slots.  All of them go through inline asm (the compiler does not
+// count them) and are waited for explicitly; none of them writes a register.  After
+// the stage barrier each wave converts, in place, the 128 weight scales that
+// it alone reads (its 32 columns x 4 groups) to fp32 times 1/16 (the unpack
+// factor), 0 for groups past k; LDS operations of one wave complete in order,
+// so its later reads see the converted values without another barrier.
+constexpr int GW = 4;              // waves per workgroup
 constexpr int GT = GW * 64;        // threads per workgroup
 constexpr int GBN = GW * 32;       // output columns per workgroup (32 per wave)
 constexpr int GNB = 4;             // 32-element groups per stage
 constexpr int GBK = GNB * QK;      // activation bytes per row per stage
-constexpr int GRT = 3;             // 32-row MFMA tiles per chunk
+constexpr int GRT = 2;             // 32-row tiles per chunk
 constexpr int GCH = 32 * GRT;      // routed rows per chunk
-constexpr int GNS = 3;             // LDS stage buffers (two stages in flight)
-constexpr int G_AD_WAVES = GNB * GCH / 64;  // waves issuing activation-scale loads
+constexpr int GNS = 2;             // LDS stage buffers (the next stage in flight)
+constexpr int G_W_LOADS = GBN * GNB / GT;          // weight chunks per thread and stage (2)
+// A chunk of R row tiles loads only its 32R rows: R activation chunks and
+// ceil(R/2) activation-scale slots per thread and stage.
+template <int R> constexpr int g_a_loads() { return 32 * R * (GBK / 16) / GT; }
+template <int R> constexpr int g_as_loads() { return (32 * R * GNB + GT - 1) / GT; }
+constexpr int G_AS_ROWS = 64;                      // rows of activation-scale slots (>= the most loaded)
+constexpr int G_WS_LOADS = GBN * GNB / 64 / GW;    // weight-scale slots per thread and stage (2)
 
-static_assert(GNB * GCH % 64 == 0 && G_AD_WAVES <= GW, "scale loads map to whole waves");
-static_assert(GBN * GNB == 2 * GT, "two weight-scale loads per wave and stage");
-static_assert(GCH == 8 * GW, "one activation-row load per wave and stage");
+static_assert(G_W_LOADS == 2 && G_WS_LOADS == 2, "load mapping");
+static_assert(g_a_loads<GRT>() == GRT && g_as_loads<GRT>() * GT / GNB <= G_AS_ROWS, "load mapping");
+static_assert(G_AS_ROWS >= GCH, "activation-scale slots cover the chunk");
 
 struct GBuf {
-  uint8_t w[GBN * GNB * 16];  // packed weights: [column][4 groups x 16 B], swizzled
-  int8_t a[GCH * GBK];        // gathered activation rows: [row][8 x 16 B], swizzled
-  float ad[GNB][GCH];         // activation scales, fp32, [group][row]
-  uint32_t wd[GBN][GNB];      // weight scales, fp16 bits zero-extended, [column][group]
+  uint8_t w[GBN * GNB * 16];    // packed weights: [column][slot], slot = group ^ wswz(column)
+  int8_t a[GCH * GBK];          // activation rows: [row][slot], slot = chunk ^ aswz(row)
+  uint32_t as[G_AS_ROWS * GNB]; // activation scales, fp16 bits zero-extended: [row][group]
+  uint32_t ws[GNB][GBN];        // weight scales: fp16 bits zero-extended as loaded, then
+                                // converted in place to fp32 / 16 (0 past k): [group][column]
 };
 
 // Physical slot of the 16-byte activation chunk c of staged row r (rows of
@@ -295,202 +238,318 @@ __device__ __forceinline__ i32x4 unpack_w4x16(i32x4 p, int shl) {
   return r;
 }
 
-// The MFMA work of one stage for one wave: 32 columns x R 32-row tiles,
-// groups 0 .. nb_here-1 of the stage, read from LDS.  The group loop is
-// rolled and R is a compile-time constant, so the code per group is
-// straight-line: the group's fragment reads first, then all R MFMAs, then the
-// R epilogues, so that the matrix core works while the epilogues run.
-// Output register r of tile t in lane L is row 32t + 8(r/4) + 4(L/32) + r%4,
-// column L%32 of the wave's tile.
+// The MFMA work of one stage for one wave: its 32 columns x R 32-row tiles
+// over the stage's GNB groups.  Steps u = g * R + t run as a pipeline of
+// depth one (tile u's MFMA is issued before tile u-1's epilogue, into the
+// other of two result sets), each step pinned in place by empty asm
+// statements as in the Q8_0 GEMM.  Output register r of tile t in lane L is
+// column 8(r/4) + 4(L/32) + r%4 of the wave's columns, routed row 32t + L%32
+// of the chunk.  Per term: t_r = fma(F_r, da, -1.5*2^23*da) = round(da * 16P)
+// with da the lane's activation scale, then acc = fma(t_r, dw_r / 16, acc).
 template <int R>
-__device__ __forceinline__ void grouped_stage_compute(
-    const GBuf &B, int nb_here, int wave, int lane, const i32x16 &seed,
-    float (&acc)[R][16]) {
-  const int l32 = lane & 31, g = lane >> 5;
-  const int shl = g ? 0 : 4;
-  const int cl = wave * 32 + l32;
-#pragma unroll 1
-  for (int b = 0; b < nb_here; ++b) {
-    const i32x4 p = *reinterpret_cast<const i32x4 *>(&B.w[cl * (GNB * 16) + 16 * wswz(cl, b)]);
-    const uint32_t sw = B.wd[cl][b];
-    i32x4 af[R];
+__device__ __forceinline__ void grouped_stage(const GBuf &B, int wave, int lane_in,
+                                              const i32x16 &seed, f32x16 (&acc)[R]) {
+  // the lane index is laundered so that the LDS addresses below are rebuilt
+  // each stage instead of being hoisted out of the stage loop into registers
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));
+  const int l32 = lane & 31, h = lane >> 5;
+  const int shl = h ? 0 : 4;
+  const int col = wave * 32 + l32;
+  // activation scales of this stage's groups for the lane's row of each tile
+  float da[R][GNB];
 #pragma unroll
-    for (int t = 0; t < R; ++t) {
-      const int r = 32 * t + l32;
-      af[t] = *reinterpret_cast<const i32x4 *>(&B.a[r * GBK + 16 * aswz(r, 2 * b + g)]);
-    }
-    // keep the reads above ahead of the math (the scheduler would otherwise
-    // sink each next to its first use and expose the LDS latency per tile)
-    __builtin_amdgcn_sched_barrier(0);
-    const i32x4 wf = unpack_w4x16(p, shl);
-    const float dw16 = half_bits_to_float((uint16_t)sw) * 0.0625f;  // exact
-    const float ncd = -MAGIC_F * dw16;                              // exact
-    i32x16 d[R];
-#pragma unroll
-    for (int t = 0; t < R; ++t) d[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[t], wf, seed, 0, 0, 0);
-#pragma unroll
-    for (int t = 0; t < R; ++t) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(&B.ad[b][32 * t + 8 * q + 4 * g]);
-        const float da[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r2 = 4 * q + j;
-          const float tt = fmaf(bits_to_float(d[t][r2]), dw16, ncd);
-          acc[t][r2] = fmaf(tt, da[j], acc[t][r2]);
-        }
-      }
-    }
+  for (int t = 0; t < R; ++t) {
+    const i32x4 v = *reinterpret_cast<const i32x4 *>(&B.as[(32 * t + l32) * GNB]);
+    da[t][0] = half_bits_to_float((uint16_t)v.x);
+    da[t][1] = half_bits_to_float((uint16_t)v.y);
+    da[t][2] = half_bits_to_float((uint16_t)v.z);
+    da[t][3] = half_bits_to_float((uint16_t)v.w);
+    // converted once here: left to itself the compiler folds the conversion
+    // into each epilogue fma as v_fma_mix_f32, which issues at a lower rate
+    asm volatile("" : "+v"(da[t][0]), "+v"(da[t][1]), "+v"(da[t][2]), "+v"(da[t][3]));
   }
+  auto read_w = [&](int g) {
+    return *reinterpret_cast<const i32x4 *>(&B.w[col * (GNB * 16) + 16 * wswz(col, g)]);
+  };
+  // the swizzle of row 32t + l32 does not depend on t, so one lane offset per
+  // group serves every tile (the tile adds 32 * GBK bytes)
+  const int aswz_l = (l32 >> 1) & 7;
+  auto read_b = [&](int g, int t) {
+    return *reinterpret_cast<const i32x4 *>(
+        &B.a[32 * GBK * t + l32 * GBK + 16 * ((2 * g + h) ^ aswz_l)]);
+  };
+  auto read_dw = [&](int g, float (&dst)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(&B.ws[g][wave * 32 + 8 * q + 4 * h]);
+      dst[4 * q + 0] = v.x;
+      dst[4 * q + 1] = v.y;
+      dst[4 * q + 2] = v.z;
+      dst[4 * q + 3] = v.w;
+    }
+  };
+
+  i32x4 wf = unpack_w4x16(read_w(0), shl);
+  i32x4 bf[R];
+#pragma unroll
+  for (int t = 0; t < R; ++t) bf[t] = read_b(0, t);
+  i32x4 wraw_n;
+  float dwc[16];  // weight scales of the epilogue's group
+  read_dw(0, dwc);
+  i32x16 dres[2];
+  auto epilogue = [&](const i32x16 &d, int u) {
+    const int g = u / R, t = u % R;
+    const float s = da[t][g], ncd = -MAGIC_F * s;  // exact
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float tt = fmaf(bits_to_float(d[r]), s, ncd);
+      acc[t][r] = fmaf(tt, dwc[r], acc[t][r]);
+    }
+  };
+  // Step u = (g, t): the MFMA of (g, t), the epilogue of step u-1, then tile
+  // t's activation fragment of group g+1 is read into the register the MFMA
+  // has just consumed, and (at t == 0) the next group's weight fragment and
+  // this group's weight scales; at t == R-1 the next group's weight fragment
+  // is unpacked.
+#pragma unroll
+  for (int u = 0; u < GNB * R; ++u) {
+    const int g = u / R, t = u % R;
+    asm volatile("" : "+v"(wf), "+v"(bf[t]));
+    dres[u & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf, bf[t], seed, 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (u > 0) {
+      epilogue(dres[(u - 1) & 1], u - 1);
+      __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
+      asm volatile("" : "+v"(acc[(u - 1) % R]), "+v"(dres[u & 1]));
+    } else {
+      asm volatile("" : "+v"(dres[u & 1]));
+    }
+    // the epilogue just run was the last of group g-1: group g's weight
+    // scales replace its (first used at the next step)
+    if (t == 0 && g > 0) read_dw(g, dwc);
+    if (g + 1 < GNB) {
+      bf[t] = read_b(g + 1, t);
+      if (t == 0) wraw_n = read_w(g + 1);
+      if (t == R - 1) wf = unpack_w4x16(wraw_n, shl);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  epilogue(dres[(GNB * R - 1) & 1], GNB * R - 1);
 }
 
 struct GArgs {
   const int8_t *aq;
-  const float *ad32t;
-  int rpad, top_k;
+  const uint16_t *ad;
+  int top_k;
   const uint8_t *wq4;
   const uint16_t *wd;
   int n, k;
   float *y;
 };
 
-// One chunk of up to 16*R routed rows of expert e against the workgroup's
-// column tile: the whole K pipeline, then the stores.
+// One chunk of up to 32*R routed rows of expert e against the workgroup's 128
+// columns: the whole K pipeline, then the stores.
 template <int R>
-__device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS],
-                                              const int *s_tok, const int *s_row,
-                                              int64_t wrow0, int n0, int off,
-                                              int c0, int crows) {
+__device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], const int *s_tok,
+                                              const int *s_row, int e, int n0, int crows) {
   const int n = A.n, k = A.k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int nbk = k / QK;
   const int stages = (nbk + GNB - 1) / GNB;
-  const bool wave_active = n0 + wave * 32 < n;
-  const int64_t kh = k / 2;  // packed bytes per weight row
+  const int kh = k / 2;
 
   i32x16 seed;
 #pragma unroll
   for (int r = 0; r < 16; ++r) seed[r] = MAGIC_BITS;
+  asm volatile("" : "+v"(seed));  // kept resident, not rebuilt per stage
 
-  // Issue the direct loads of stage s into buffer s % GNS (5 per wave, plus
-  // one activation-scale load in waves 0 .. G_AD_WAVES-1).  They go through
-  // inline asm, invisible to the compiler's wait counting (see dma_lds16);
-  // the waits below are explicit.  Group indices past the last group of k
-  // re-read the last group (never used); columns past n re-read column n-1;
-  // rows past the chunk re-read its last row.  Addresses are rebuilt per
-  // stage from the thread index, laundered through an empty asm, so that the
-  // compiler does not hoist a dozen 64-bit addresses out of the stage loop
-  // and hold them in registers across it.
+  // per-lane load coordinates, fixed for the chunk
+  // weights: chunk e = 64 (2w + q) + L -> column e/4, slot e%4 (group slot ^ wswz)
+  int w_off[G_W_LOADS], w_g[G_W_LOADS];
+#pragma unroll
+  for (int q = 0; q < G_W_LOADS; ++q) {
+    const int ce = 64 * (G_W_LOADS * wave + q) + lane;
+    const int c = ce >> 2;
+    w_g[q] = (ce & 3) ^ ((c >> 2) & 3);
+    w_off[q] = min(n0 + c, n - 1) * kh;
+  }
+  // activations: chunk e = 64 (3w + q) + L -> row e/8, slot e%8 (chunk slot
+  // ^ aswz); 32-bit offsets from the activation base (the ABI layer
+  // guarantees n_tokens * k < 2^31)
+  constexpr int NA = g_a_loads<R>(), NAS = g_as_loads<R>();
+  int a_row[NA], a_c[NA];
+#pragma unroll
+  for (int q = 0; q < NA; ++q) {
+    const int ce = 64 * (NA * wave + q) + lane;
+    const int r = ce >> 3;
+    a_c[q] = 16 * ((ce & 7) ^ ((r >> 1) & 7));
+    a_row[q] = s_tok[r] * k;
+  }
+  // activation scales: slot e = 64 (2w + q) + L -> row e/4 (clamped to the
+  // chunk's rows), group e%4; element offsets from the scale base
+  int as_row[NAS];
+#pragma unroll
+  for (int q = 0; q < NAS; ++q) {
+    const int ce = 64 * (NAS * wave + q) + lane;
+    as_row[q] = s_tok[min(ce >> 2, GCH - 1)] * nbk + (ce & 3);
+  }
+  // weight scales: slot e = 64 (2w + q) + L -> group e/128 (= w), column
+  // e%128; element offsets from the expert's scale base
+  int ws_off[G_WS_LOADS];
+#pragma unroll
+  for (int q = 0; q < G_WS_LOADS; ++q) {
+    const int ce = 64 * (G_WS_LOADS * wave + q) + lane;
+    ws_off[q] = min(n0 + (ce & (GBN - 1)), n - 1) * nbk + (ce >> 7);
+  }
+  const uint8_t *wq_e = A.wq4 + (int64_t)e * n * kh;
+  const uint16_t *wd_e = A.wd + (int64_t)e * n * nbk;
+
+  // Issue stage s into buffer s % GNS.  Groups past the last one re-read the
+  // last group (their scales become 0).
   auto issue = [&](int s) {
-    int tl = tid;
-    asm volatile("" : "+v"(tl));
-    const int ln = tl & 63, wv = tl >> 6;
     const int g0 = s * GNB;
+    const bool full = g0 + GNB <= nbk;  // uniform
     GBuf &D = S[s % GNS];
-    // weights: wave load h (two per wave) fills columns ct .. ct+15,
-    // ct = 16 * (2w + h); lane L lands in column ct + L/4, slot L%4, which
-    // holds group (L%4) ^ swizzle(column)
+    const uint8_t *wbase = wq_e + 16 * g0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int cl = 16 * (2 * wv + h) + (ln >> 2);
-      const int lg = (ln & 3) ^ ((cl >> 2) & 3);
-      const int c = min(n0 + cl, n - 1);
-      dma_lds16(A.wq4 + (wrow0 + c) * kh + 16 * min(g0 + lg, nbk - 1),
-                &D.w[16 * (2 * wave + h) * (GNB * 16)]);
+    for (int q = 0; q < G_W_LOADS; ++q) {
+      const int off = w_off[q] + 16 * (full ? w_g[q] : min(w_g[q], nbk - 1 - g0));
+      const uint32_t lds = lds_addr(&D.w[1024 * (G_W_LOADS * wave_u + q)]);
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(wbase), "{m0}"(lds) : "memory");
     }
-    // weight scales: wave load h fills table entries e = 64 (2w + h) + L,
-    // column e / 4, group e % 4 (one fp16, zero-extended, per 4-byte slot)
+    const int8_t *abase = A.aq + 32 * g0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int e = 64 * (2 * wv + h) + ln;
-      const int c = min(n0 + (e >> 2), n - 1);
-      dma_lds_u16(A.wd + (wrow0 + c) * nbk + min(g0 + (e & 3), nbk - 1),
-                  &D.wd[0][0] + 64 * (2 * wave + h));
+    for (int q = 0; q < NA; ++q) {
+      const int off = a_row[q] + (full ? a_c[q] : min(a_c[q], k - 16 - 32 * g0));
+      const uint32_t lds = lds_addr(&D.a[1024 * (NA * wave_u + q)]);
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(abase), "{m0}"(lds) : "memory");
     }
-    // activation rows: wave w fills staged rows 8w .. 8w+7; lane L lands in
-    // row 8w + L/8, physical chunk L%8, which holds logical chunk
-    // (L%8) ^ swizzle(row)
-    {
-      const int ra = 8 * wv + (ln >> 3);
-      const int lc = (ln & 7) ^ ((ra >> 1) & 7);
-      const int kb = min(g0 + (lc >> 1), nbk - 1);
-      dma_lds16(A.aq + (int64_t)s_tok[ra] * k + 32 * kb + 16 * (lc & 1), &D.a[8 * wave * GBK]);
+    const uint16_t *asbase = A.ad + g0;
+#pragma unroll
+    for (int q = 0; q < NAS; ++q) {
+      const int ce = 64 * (NAS * wave + q) + lane;
+      const int off = as_row[q] + (full ? 0 : min(0, nbk - 1 - g0 - (ce & 3)));
+      const uint32_t lds = lds_addr(&D.as[64 * (NAS * wave_u + q)]);
+      asm volatile("s_nop 0\n\tglobal_load_lds_ushort %0, %1" :: "v"(2 * off), "s"(asbase), "{m0}"(lds) : "memory");
     }
-    // activation scales (waves 0 .. G_AD_WAVES-1): flat entry f = 64w + L of
-    // the stage's [group][row] table
-    if (wave < G_AD_WAVES) {
-      const int f = 64 * wv + ln;
-      dma_lds4(A.ad32t + (int64_t)min(g0 + f / GCH, nbk - 1) * A.rpad + (off + c0 + f % GCH),
-               &D.ad[0][0] + 64 * wave);
+    const uint16_t *wsbase = wd_e + g0;
+#pragma unroll
+    for (int q = 0; q < G_WS_LOADS; ++q) {
+      const int gq = wave_u;  // group of this wave's slots
+      const int off = ws_off[q] + (full ? 0 : min(0, nbk - 1 - g0 - gq));
+      const uint32_t lds = lds_addr(&D.ws[0][0] + 64 * (G_WS_LOADS * wave_u + q));
+      asm volatile("s_nop 0\n\tglobal_load_lds_ushort %0, %1" :: "v"(2 * off), "s"(wsbase), "{m0}"(lds) : "memory");
+    }
+  };
+  // The weight scales this wave reads in stage s (its 32 columns, all
+  // groups), converted in place: lane L takes column 32 w + L%32, groups
+  // 2 (L/32) and 2 (L/32) + 1.
+  auto convert_ws = [&](int s) {
+    GBuf &D = S[s % GNS];
+    const int c = wave * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int g = 2 * (lane >> 5) + i;
+      const uint32_t bits = D.ws[g][c];
+      const float v = s * GNB + g < nbk ? half_bits_to_float((uint16_t)bits) * 0.0625f : 0.0f;  // exact
+      D.ws[g][c] = __builtin_bit_cast(uint32_t, v);
     }
   };
 
-  float acc[R][16];
+  f32x16 acc[R];
 #pragma unroll
   for (int t = 0; t < R; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
 
+  // Stage s waits for its own loads (issued before stage s-1's compute); the
+  // barrier then makes every wave's loads of stage s visible and frees the
+  // buffer of stage s-1, which takes stage s+1's loads during this compute.
   issue(0);
-  if (stages > 1) issue(1);
   for (int s = 0; s < stages; ++s) {
-    // this wave's loads of stage s have landed (only stage s+1's, issued
-    // after them, may still be in flight)
-    if (s + 1 < stages) {
-      if (wave < G_AD_WAVES) wait_vmcnt<6>();
-      else wait_vmcnt<5>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    // every wave's loads of stage s have landed, and every wave is done with
-    // stage s-1, whose buffer the loads below refill
+    wait_vmcnt<0>();
     lds_barrier();
-    if (s + 2 < stages) issue(s + 2);
-    if (wave_active)
-      grouped_stage_compute<R>(S[s % GNS], min(GNB, nbk - s * GNB), wave, lane, seed, acc);
+    if (s + 1 < stages) issue(s + 1);
+    convert_ws(s);
+    grouped_stage<R>(S[s % GNS], wave, lane, seed, acc);
   }
 
-  // store: lane's column L%32, rows 32t + 8(r/4) + 4(L/32) + r%4 of the chunk
-  const int col = n0 + wave * 32 + (lane & 31);
-  if (wave_active && col < n) {
+  // store: lane's routed row 32t + L%32 of the chunk, columns
+  // n0 + 32 wave + 8q + 4(L/32) + (0..3) in registers 4q .. 4q+3
+  const int l32 = lane & 31, h = lane >> 5;
+  const bool vec = (n & 3) == 0 && ((uintptr_t)A.y & 15) == 0;
 #pragma unroll
-    for (int t = 0; t < R; ++t)
+  for (int t = 0; t < R; ++t) {
+    const int rr = 32 * t + l32;
+    if (rr < crows) {
+      float *yrow = A.y + (int64_t)s_row[rr] * n;
 #pragma unroll
-      for (int r2 = 0; r2 < 16; ++r2) {
-        const int rr = 32 * t + 8 * (r2 >> 2) + 4 * (lane >> 5) + (r2 & 3);
-        if (rr < crows) A.y[(int64_t)s_row[rr] * n + col] = acc[t][r2];
+      for (int q = 0; q < 4; ++q) {
+        const int c = n0 + wave * 32 + 8 * q + 4 * h;
+        if (vec && c + 3 < n) {
+          f32x4 v;
+          v.x = acc[t][4 * q + 0];
+          v.y = acc[t][4 * q + 1];
+          v.z = acc[t][4 * q + 2];
+          v.w = acc[t][4 * q + 3];
+          *reinterpret_cast<f32x4 *>(yrow + c) = v;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (c + i < n) yrow[c + i] = acc[t][4 * q + i];
+        }
       }
+    }
   }
 }
 
-__global__ __launch_bounds__(GT, 1) void k_grouped_w4a8(
-    const int8_t *__restrict__ aq, const float *__restrict__ ad32t, int rpad,
-    int top_k, const uint8_t *__restrict__ wq4, const uint16_t *__restrict__ wd,
+__global__ __launch_bounds__(GT, 3) void k_grouped_w4a8(
+    const int8_t *__restrict__ aq, const uint16_t *__restrict__ ad, int top_k,
+    const uint8_t *__restrict__ wq4, const uint16_t *__restrict__ wd,
     int n_experts, int n, int k, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ rows,
     float *__restrict__ y) {
   __shared__ __attribute__((aligned(16))) GBuf S[GNS];
   __shared__ int s_tok[GCH];  // token of each staged row
   __shared__ int s_row[GCH];  // routed row (output row) of each staged row
+  __shared__ int s_cnt[GT];
+  __shared__ int s_e;
 
-  // both column tiles of one expert share (blockIdx % n_experts), hence one
-  // XCD when n_experts is a multiple of 8, and so the expert's activation rows
-  // in that XCD's L2
-  const int e = blockIdx.x % n_experts;
-  const int tn = blockIdx.x / n_experts;
+  const int tiles_n = (n + GBN - 1) / GBN;
+  const int unit = blockIdx.x / tiles_n;
+  const int tn = blockIdx.x - unit * tiles_n;
+  const int tid = threadIdx.x;
+  int e;
+  if (n_experts <= GT) {
+    // the expert of rank `unit` by descending routed-row count (ties by index)
+    const int c = tid < n_experts ? counts[tid] : 0;
+    s_cnt[tid] = c;
+    __syncthreads();
+    if (tid < n_experts) {
+      int rank = 0;
+      for (int j = 0; j < n_experts; ++j) {
+        const int cj = s_cnt[j];
+        rank += (cj > c) || (cj == c && j < tid);
+      }
+      if (rank == unit) s_e = tid;
+    }
+    __syncthreads();
+    e = __builtin_amdgcn_readfirstlane(s_e);
+  } else {
+    e = unit;
+  }
   const int cnt = counts[e];
   if (cnt == 0) return;
   const int off = offsets[e];
-  const GArgs A{aq, ad32t, rpad, top_k, wq4, wd, n, k, y};
-  const int tid = threadIdx.x;
+  const GArgs A{aq, ad, top_k, wq4, wd, n, k, y};
   const int n0 = tn * GBN;
-  const int64_t wrow0 = (int64_t)e * n;
 
   for (int c0 = 0; c0 < cnt; c0 += GCH) {
     const int crows = min(GCH, cnt - c0);
-    // the previous chunk is done with s_tok, s_row and S (and its direct
-    // loads have all landed: each chunk ends with vmcnt(0))
+    // the previous chunk is done with s_tok, s_row and S (each chunk ends
+    // with every load landed)
     __syncthreads();
     if (tid < GCH) {
       const int rr = rows[off + c0 + min(tid, crows - 1)];
@@ -499,40 +558,33 @@ __global__ __launch_bounds__(GT, 1) void k_grouped_w4a8(
     }
     __syncthreads();
     switch ((crows + 31) / 32) {
-      case 1: grouped_chunk<1>(A, S, s_tok, s_row, wrow0, n0, off, c0, crows); break;
-      case 2: grouped_chunk<2>(A, S, s_tok, s_row, wrow0, n0, off, c0, crows); break;
-      default: grouped_chunk<3>(A, S, s_tok, s_row, wrow0, n0, off, c0, crows); break;
+      case 1: grouped_chunk<1>(A, S, s_tok, s_row, e, n0, crows); break;
+      default: grouped_chunk<2>(A, S, s_tok, s_row, e, n0, crows); break;
     }
   }
 }
 
 }  // namespace
 
-int64_t grouped_ad32_rows(int64_t rows_total) { return rows_total + GCH; }
-
 hipError_t launch_route_topk(const int32_t *ids, int64_t rows_total,
                              int64_t n_experts, int64_t top_k, int32_t *counts,
-                             int32_t *offsets, int32_t *rows,
-                             const uint16_t *ad, int64_t k, float *ad32t,
-                             float *y, int64_t n, hipStream_t stream) {
+                             int32_t *offsets, int32_t *rows, float *y,
+                             int64_t n, hipStream_t stream) {
   hipLaunchKernelGGL(k_route, dim3((unsigned)n_experts), dim3(RT), 0, stream,
                      ids, (int)rows_total, (int)n_experts, (int)top_k, counts,
-                     offsets, rows, ad, (int)(k / QK), ad32t,
-                     (int)grouped_ad32_rows(rows_total), y, (int)n);
+                     offsets, rows, y, (int)n);
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_w4a8(const int8_t *aq, const float *ad32t,
-                               int64_t rows_total, int64_t top_k,
-                               const uint8_t *wq4, const uint16_t *wd,
-                               int64_t n_experts, int64_t n, int64_t k,
-                               const int32_t *counts, const int32_t *offsets,
-                               const int32_t *rows, float *y,
-                               hipStream_t stream) {
+hipError_t launch_grouped_w4a8(const int8_t *aq, const uint16_t *ad,
+                               int64_t top_k, const uint8_t *wq4,
+                               const uint16_t *wd, int64_t n_experts, int64_t n,
+                               int64_t k, const int32_t *counts,
+                               const int32_t *offsets, const int32_t *rows,
+                               float *y, hipStream_t stream) {
   const int64_t tiles_n = (n + GBN - 1) / GBN;
   hipLaunchKernelGGL(k_grouped_w4a8, dim3((unsigned)(n_experts * tiles_n)),
-                     dim3(GT), 0, stream, aq, ad32t,
-                     (int)grouped_ad32_rows(rows_total), (int)top_k, wq4, wd,
+                     dim3(GT), 0, stream, aq, ad, (int)top_k, wq4, wd,
                      (int)n_experts, (int)n, (int)k, counts, offsets, rows, y);
   return hipGetLastError();
 }

@@ -169,9 +169,9 @@ BQI_API int route_topk(const int32_t *topk_ids, int64_t n_tokens, int64_t top_k,
                int32_t *rows, void *stream);
 
 /* Bytes of device workspace qgemm_w4a8_grouped needs for these sizes (0 for
- * sizes it rejects).  The workspace holds the routing (counts, offsets and
- * the rows of each expert) and the routed rows' activation scales widened to
- * fp32 in expert order: about 4 * (n_tokens * top_k + 96) * (k / 32) bytes. */
+ * sizes it rejects).  The workspace holds the routing: counts, offsets and
+ * the routed rows of each expert, about 4 * (n_tokens * top_k + 2 * n_experts)
+ * bytes. */
 BQI_API size_t qgemm_w4a8_grouped_workspace_size(int64_t n_tokens, int64_t top_k,
                                          int64_t n_experts, int64_t k);
 
@@ -200,7 +200,9 @@ BQI_API size_t qgemm_w4a8_grouped_workspace_size(int64_t n_tokens, int64_t top_k
  * within a token are legal and computed independently.
  *
  * Requirements: k % 32 == 0; aq and wq4 16-byte aligned; workspace 256-byte
- * aligned; n_tokens * top_k <= 2^30; n_experts <= 65536.
+ * aligned; n_tokens * top_k <= 2^30; n_experts <= 65536; n * k/2 and
+ * n_tokens * k below 2^31 (one expert's packed weights and the activations
+ * are addressed with 32-bit offsets).
  */
 BQI_API int qgemm_w4a8_grouped(const int8_t *aq, const uint16_t *ad, int64_t n_tokens,
                        const int32_t *topk_ids, int64_t top_k,
@@ -223,8 +225,7 @@ BQI_API int qgemm_w4a8_grouped(const int8_t *aq, const uint16_t *ad, int64_t n_t
  * the process ends; this call allocates nothing.  The caller still passes the
  * inputs and y.  Problems whose workspace
  * (qgemm_w4a8_grouped_workspace_size) exceeds the array return BQI_ESHAPE
- * before anything is launched (e.g. k = 2048 fits up to about 62,000 routed
- * rows).  The array belongs to the current device: `stream` must be a stream
+ * before anything is launched (it holds about 4.19 million routed rows).  The array belongs to the current device: `stream` must be a stream
  * of that device.  Calls that overlap on one GPU (several host threads, or
  * several streams) share the array and race; serialize them.  Up to 128
  * routed rows need no workspace and never touch the array.

@@ -114,3 +114,110 @@ def test_scan_catches_planted_mistakes():
     assert violations(dma) == []
     # commented-out code is ignored
     assert violations("// " + bare.replace("\n", "\n// ")) == []
+
+
+# ---------------------------------------------------------------------------
+# The same rule on the compiled code: between an asm register load and the
+# asm wait that names its destination, no instruction may read or overwrite
+# the destination register (the compiler may copy an asm output as soon as
+# the asm statement ends, e.g. to reconcile registers across a loop, and such
+# a copy reads the register before the load has written it).
+# ---------------------------------------------------------------------------
+
+import shutil
+import subprocess
+
+import pytest
+
+HIPCC = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+
+
+def _compile_to_asm(src):
+    flags = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
+             "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero", "-fhip-fp32-correctly-rounded-divide-sqrt",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"), src, "-o", "-"]
+    r = subprocess.run([HIPCC] + flags, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    assert r.returncode == 0, "hipcc failed on %s" % src
+    return r.stdout
+
+
+def _vregs(code):
+    """Numbers of the vector registers an instruction line mentions
+    (single registers such as v52 and ranges such as v[52:55])."""
+    regs = set()
+    for lo, hi in re.findall(r"\bv\[(\d+):(\d+)\]", code):
+        regs.update(range(int(lo), int(hi) + 1))
+    regs.update(int(r) for r in re.findall(r"\bv(\d+)\b", code))
+    return regs
+
+
+LOAD_LINE = re.compile(r"(?:global|buffer|flat|scratch)_load_(?!lds)\w+\s+(v\[\d+:\d+\]|v\d+)")
+
+
+def asm_load_violations(text):
+    """Scan compiled GCN assembly in program order: for each register load
+    emitted from inline asm, the lines up to the next inline-asm s_waitcnt
+    must not mention any register the load writes."""
+    bad = []
+    in_asm = False
+    pending = {}  # register number -> line of its load
+    for i, line in enumerate(text.splitlines()):
+        code = line.split(";")[0].strip()
+        if line.strip().startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if line.strip().startswith(";;#ASMEND"):
+            in_asm = False
+            continue
+        if in_asm:
+            if "s_waitcnt" in code:
+                pending.clear()
+            m = LOAD_LINE.match(code)
+            if m:
+                for r in _vregs(m.group(1)):
+                    pending[r] = i
+            continue
+        if not code or not pending:
+            continue
+        hit = _vregs(code) & set(pending)
+        for r in sorted(hit):
+            bad.append("line %d uses v%d loaded at line %d: %s" % (i + 1, r, pending.pop(r) + 1, code))
+    return bad
+
+
+@pytest.mark.skipif(shutil.which(HIPCC) is None and not os.path.exists(HIPCC), reason="hipcc not available")
+def test_compiled_kernels_leave_asm_loaded_registers_alone_until_the_wait():
+    checked = 0
+    for f in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
+        with open(f) as fh:
+            src = fh.read()
+        if not any(REG_LOAD.search(_template(b)) for _, b in asm_statements(src)):
+            continue
+        bad = asm_load_violations(_compile_to_asm(f))
+        assert not bad, "%s:\n%s" % (os.path.basename(f), "\n".join(bad[:10]))
+        checked += 1
+    assert checked >= 1
+
+
+def test_asm_scan_catches_a_copy_before_the_wait():
+    good = """
+	;;#ASMSTART
+	global_load_ushort v52, v1, s[2:3]
+	;;#ASMEND
+	v_add_u32_e32 v3, 4, v2
+	;;#ASMSTART
+	s_waitcnt vmcnt(0)
+	;;#ASMEND
+	v_cvt_f32_f16_e32 v4, v52
+"""
+    assert asm_load_violations(good) == []
+    bad = good.replace("v_add_u32_e32 v3, 4, v2", "v_mov_b32_e32 v103, v52")
+    assert len(asm_load_violations(bad)) == 1
+    # a wide load and a use through a register range that overlaps it
+    wide = good.replace("global_load_ushort v52", "global_load_dwordx2 v[52:53]")
+    assert asm_load_violations(wide) == []
+    assert len(asm_load_violations(wide.replace("v_add_u32_e32 v3, 4, v2",
+                                                "v_pk_mov_b32 v[60:61], v[53:54], v[53:54] op_sel:[0,1]"))) == 1
+    # registers that merely share digits are not the loaded one
+    assert asm_load_violations(good.replace("v_add_u32_e32 v3, 4, v2", "v_add_u32_e32 v152, v5, v520")) == []

@@ -72,8 +72,9 @@ def test_noalloc_decode_size_and_rejection():
     assert noalloc_call(qa, da, ids, wq4, wd, y) == bqi.BQI_OK
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32))
-    # a workspace larger than the array: rejected before any launch, y untouched
-    T, top_k, E, K, N = 8192, 8, 4, 2048, 32
+    # a workspace larger than the array (4 bytes per routed row: 2^22 routed
+    # rows): rejected before any launch, y untouched
+    T, top_k, E, K, N = 1 << 19, 8, 4, 32, 1
     need = bqi.workspace_size(T, top_k, E, K)
     assert need > bqi.NOALLOC_SCRATCH_BYTES
     qa = torch.zeros((T, K), dtype=torch.int8, device="cuda:0")
