@@ -11,7 +11,8 @@ than the 256 MB Infinity Cache) so every step streams its weights from HBM.
 `value` is algorithmic bytes per step / time per step (GB/s); inputs are
 resident in HBM before timing starts.
 
-Also reported (key "also"): the M=4 and M=16 decode steps, the prefill GEMM
+Also reported (key "also"): the small Q8_0 GEMM (M=16, K=256, N=512; time
+per call, launch-bound), the M=4 and M=16 decode steps, the prefill GEMM
 (M=2048, K=5120, N=17408) and a short-prompt prefill against the same weights
 (M=128), the long-prefill GEMM (M=18432, K=5120, N=5120, Student-t
 activations with outlier channels), the grouped W4A8 MoE GEMM (947 tokens,
@@ -27,8 +28,13 @@ overhead is not counted); each graph's output is first checked bit for bit
 against an eager run.  "eager_ms_per_step" is the same step launched from
 Python one call at a time.
 
-"cpu_baseline" times the CPU oracle (plain C, all host cores) on the same step
-for ~10 s; it is a reported baseline, not a target.
+"cpu_baseline" times the CPU oracle (plain C; it splits its work over output
+rows, so the single-row step runs on one thread) on the same step for ~5 s,
+and names the host CPU.  Each "also" line carries "cpu_oracle": the oracle
+timed on that configuration (the large GEMMs and the MoE GEMM on a stated
+sample of their rows), ~25 s in all.  Both are reported baselines, not
+targets.  "distribution" gives the median and 10th / 90th percentiles over
+the timed replays of the headline step.
 """
 from __future__ import annotations
 
@@ -58,8 +64,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--only-headline", action="store_true", help="skip the secondary workloads")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--workloads", default="decode,decode_m,prefill,prefill_short,long,moe,moe_decode,combine,gguf,host",
+    p.add_argument("--cpu-seconds", type=float, default=5.0,
+                   help="seconds of oracle work for the headline step's CPU baseline")
+    p.add_argument("--reps", type=int, default=15,
+                   help="timed graph replays of the headline step (each of --steps launches)")
+    p.add_argument("--workloads", default="decode,small,decode_m,prefill,prefill_short,long,moe,moe_decode,combine,gguf,host",
                    help="comma list of workloads to run (profiling); the JSON line "
                         "is printed only when decode is among them.  'copy' (never a "
                         "default) runs a plain device copy of known size, the "
@@ -86,7 +95,10 @@ class Timer:
     def __init__(self, torch):
         self.torch = torch
 
-    def loop(self, fn, iters, graph=True, check=None):
+    def loop(self, fn, iters, graph=True, check=None, reps=1):
+        """Mean ms per launch.  With reps > 1 the graph is replayed `reps`
+        times, each replay timed on its own; the median is returned and the
+        per-replay figures are kept in self.samples."""
         torch = self.torch
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         if not graph:
@@ -96,7 +108,8 @@ class Timer:
                 fn(i)
             b.record()
             torch.cuda.synchronize()
-            return a.elapsed_time(b) / iters
+            self.samples = [a.elapsed_time(b) / iters]
+            return self.samples[0]
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
@@ -123,16 +136,30 @@ class Timer:
         while time.time() - t0 < WARM_S:
             g.replay()
             torch.cuda.synchronize()
-        a.record()
-        g.replay()
-        b.record()
-        torch.cuda.synchronize()
+        self.samples = []
+        for _ in range(reps):
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            self.samples.append(a.elapsed_time(b) / iters)
         del g
-        return a.elapsed_time(b) / iters
+        return float(np.median(self.samples))
+
+
+def distribution(samples_ms):
+    """Median and 10th / 90th percentiles of per-replay means, in µs."""
+    q = np.percentile(np.asarray(samples_ms) * 1e3, [10, 50, 90])
+    return {"replays": len(samples_ms), "p10_us": round(float(q[0]), 3),
+            "median_us": round(float(q[1]), 3), "p90_us": round(float(q[2]), 3)}
 
 
 CSRC = os.path.join(ROOT, "block_quantized_integer_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_SOURCE = ("stored figure, not measured in this run: HBM bytes per launch from the "
+                  "rocprofv3 FETCH_SIZE and WRITE_SIZE passes recorded in profiles/traffic.json "
+                  "(each scaled by a plain copy's reading); null when the kernel's sources have "
+                  "changed since the counters were taken")
 
 
 def sources_sha256(files):
@@ -223,7 +250,8 @@ def bench_headline(bqi, torch, W, args):
         step(i)
     torch.cuda.synchronize()
     T = Timer(torch)
-    ms_step = T.loop(step, args.steps, check=lambda: y)
+    ms_step = T.loop(step, args.steps, check=lambda: y, reps=args.reps)
+    dist = distribution(T.samples)
     ms_step_eager = T.loop(step, args.steps, graph=False)
     ms_two = T.loop(step_two_calls, args.steps, check=lambda: y)
     gemv_mean = T.loop(gemv, args.steps, check=lambda: y)
@@ -258,12 +286,14 @@ def bench_headline(bqi, torch, W, args):
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic("k_gemv_reg<1,4,ACT_F32> decode M=1 fused"),
+                     "traffic_source": TRAFFIC_SOURCE,
                      "bytes_per_launch": step_bytes,
                      "mean_launch_us": round(ms_step * 1e3, 3),
-                     "timing": "HIP events around %d back-to-back launches replayed "
-                               "from a HIP graph, after %d eager warm-up steps and "
-                               "%.0f ms of untimed replays" % (args.steps, args.warmup,
-                                                              WARM_S * 1e3)},
+                     "timing": "median over %d timed replays of a HIP graph of %d back-to-back "
+                               "launches (HIP events on the launch stream around each replay), "
+                               "after %d eager warm-up steps and %.0f ms of untimed replays"
+                               % (args.reps, args.steps, args.warmup, WARM_S * 1e3),
+                     "distribution": dist},
         "eager_ms_per_step": round(ms_step_eager, 6),
         "two_call_step": {"calls": "quantize_q8_0 + qgemm_q8_0", "ms_per_step": round(ms_two, 6),
                           "GB/s": round(step_bytes / (ms_two * 1e-3) / 1e9, 2)},
@@ -275,6 +305,35 @@ def bench_headline(bqi, torch, W, args):
     }
     ctx = dict(s=s, wq=wq, wd=wd, x=x, step_bytes=step_bytes)
     return res, ctx
+
+
+def bench_small(bqi, torch, W, iters):
+    """The small Q8_0 GEMM configuration (M=16, K=256, N=512, seed 0): the
+    whole call (quantize the fp32 activations, then the GEMM) is a couple of
+    microseconds of launches, so it is reported as time per call."""
+    s = W.SMALL
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    _, wq, wd = device_q8(bqi, torch, s.n, s.k, 0.02, gen)
+    x = torch.randn((s.m, s.k), generator=gen, device="cuda", dtype=torch.float32)
+    aq = torch.empty((s.m, s.k), dtype=torch.int8, device="cuda")
+    ad = torch.empty((s.m, s.k // 32), dtype=torch.int16, device="cuda")
+    y = torch.empty((s.m, s.n), dtype=torch.float32, device="cuda")
+    log("small Q8_0 GEMM M=%d K=%d N=%d" % (s.m, s.k, s.n))
+    T = Timer(torch)
+    call = lambda i: bqi.quantize_qgemm_q8_0(x, wq, wd, y, aq, ad)
+    ms = T.loop(call, iters, check=lambda: y, reps=9)
+    dist = distribution(T.samples)
+    ms_gemm = T.loop(lambda i: bqi.qgemm_q8_0(aq, ad, wq, wd, y), iters, check=lambda: y)
+    ms_eager = T.loop(call, iters, graph=False)
+    return {"workload": "small Q8_0 GEMM M=%d K=%d N=%d" % (s.m, s.k, s.n),
+            "kernel": "k_quantize_q8_0 + k_gemv_mfma16",
+            "value": round(ms * 1e3, 3), "unit": "us per call (quantize + GEMM)",
+            "higher_is_better": False, "bound": "launch",
+            "distribution": dist,
+            "gemm_only_us": round(ms_gemm * 1e3, 3),
+            "eager_us_per_call": round(ms_eager * 1e3, 3),
+            "int8_equiv_TOPS": round(2.0 * s.m * s.n * s.k / (ms * 1e-3) / 1e12, 4)}
 
 
 def bench_decode_variants(bqi, torch, W, iters):
@@ -320,7 +379,7 @@ def bench_decode_variants(bqi, torch, W, iters):
                                   "GB/s": round(gemv_bytes / (ms_gemv * 1e-3) / 1e9, 1),
                                   "frac_hbm_peak": round(gemv_bytes / (ms_gemv * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                   "algorithmic_bytes": gemv_bytes,
-                                  "hbm_bytes_measured": traffic("%s decode M=%d" % (gemv.split("<")[0], s.m))}})
+                                  "hbm_bytes_stored_counters": traffic("%s decode M=%d" % (gemv.split("<")[0], s.m))}})
     return res
 
 
@@ -360,7 +419,7 @@ def bench_gemm(bqi, torch, W, name, iters):
         "frac_int8_mfma_peak": round(tops / INT8_PEAK_TOPS, 4),
         "epilogue_valu_frac": round(valu_ops / (mean * 1e-3) / VALU_LANE_OPS_PEAK, 4),
         "hbm_bytes_algorithmic": byt,
-        "hbm_bytes_measured": traffic("%s %s" % (kernel, name)),
+        "hbm_bytes_stored_counters": traffic("%s %s" % (kernel, name)),
         "quantize": {"kernel": "k_quantize_q8_0", "mean_launch_us": round(qmean * 1e3, 2),
                      "GB/s": round(qbytes / (qmean * 1e-3) / 1e9, 1),
                      "frac_hbm_peak": round(qbytes / (qmean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
@@ -401,7 +460,7 @@ def bench_moe(bqi, torch, W, iters):
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "int8_equiv_TOPS": round(ops / (mean * 1e-3) / 1e12, 2),
             "weight_copies_rotated": copies, "hbm_bytes_algorithmic": byt,
-            "hbm_bytes_measured": traffic("k_grouped_w4a8 moe")}
+            "hbm_bytes_stored_counters": traffic("k_grouped_w4a8 moe")}
 
 
 def bench_moe_decode(bqi, torch, W, iters):
@@ -441,7 +500,7 @@ def bench_moe_decode(bqi, torch, W, iters):
                     "mean_call_us": round(mean * 1e3, 2),
                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                     "hbm_bytes_algorithmic": byt, "weight_copies_rotated": copies,
-                    "hbm_bytes_measured": traffic("k_grouped_gemv moe decode T=%d" % T)})
+                    "hbm_bytes_stored_counters": traffic("k_grouped_gemv moe decode T=%d" % T)})
     return res
 
 
@@ -506,7 +565,7 @@ def bench_combine(bqi, torch, W, iters):
             "kernel": "k_moe_combine", "value": round(gbs, 1), "unit": "GB/s",
             "mean_launch_us": round(mean * 1e3, 2), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "hbm_bytes_algorithmic": byt, "y_copies_rotated": copies,
-            "hbm_bytes_measured": traffic("k_moe_combine moe")}
+            "hbm_bytes_stored_counters": traffic("k_moe_combine moe")}
 
 
 def bench_gguf(bqi, torch, W, iters):
@@ -533,34 +592,155 @@ def bench_gguf(bqi, torch, W, iters):
                     "kernel": "k_gguf_split", "value": round(gbs, 1), "unit": "GB/s",
                     "mean_launch_us": round(mean * 1e3, 2),
                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "hbm_bytes_algorithmic": byt,
-                    "hbm_bytes_measured": traffic("k_gguf_split %s %dx%d" % (fmt, rows, k))})
+                    "hbm_bytes_stored_counters": traffic("k_gguf_split %s %dx%d" % (fmt, rows, k))})
         del srcs, codes, scales
         torch.cuda.empty_cache()
     return res
 
 
+def cpu_info():
+    """The host CPU model (first /proc/cpuinfo entry) and its thread counts."""
+    model, logical = None, 0
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name") and model is None:
+                    model = line.split(":", 1)[1].strip()
+                elif line.startswith("processor"):
+                    logical += 1
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": logical, "usable_cpus": len(os.sched_getaffinity(0))}
+
+
+def _timed(fn, seconds, min_runs=1):
+    """(seconds per call, calls): fn repeated until `seconds` have passed."""
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if n >= min_runs and el >= seconds:
+            return el / n, n
+
+
 def cpu_baseline(W, step_bytes, seconds):
-    """The CPU oracle (test infrastructure, plain C, all host cores) on the
-    same decode step: quantize the activation row, then the full GEMV."""
+    """The CPU oracle (test infrastructure, plain C) on the same decode step:
+    quantize the activation row, then the full GEMV."""
     import oracle
     s = W.DECODE[0]
     threads = oracle.default_threads()
     w = W.weights("decode", s.n, s.k)
     qw, dw = oracle.quantize_q8_0(w)
     x = W.activations("decode", s.m, s.k)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def step(nt):
         qa, da = oracle.quantize_q8_0(x)
-        oracle.qgemm_q8_0(qa, da, qw, dw, nthreads=threads)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    per = el / n
-    return {"value": round(step_bytes / per / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "sample": "%d full decode steps (quantize 1x4096 + GEMV "
-            "12288x4096), %.3f s each" % (n, per)}
+        oracle.qgemm_q8_0(qa, da, qw, dw, nthreads=nt)
+    per, n = _timed(lambda: step(threads), seconds)
+    used = min(threads, s.m)  # the oracle splits its work by output row
+    cpu = cpu_info()
+    return {"value": round(step_bytes / per / 1e9, 3), "unit": "GB/s", "cores": used,
+            "kind": "oracle", "cpu_model": cpu["model"], "host_logical_cpus": cpu["logical_cpus"],
+            "sample": "%d full decode steps (quantize 1x4096 + GEMV 12288x4096), %.4f s each; "
+                      "the oracle splits the GEMV over output rows, so a single-row step runs on "
+                      "one thread" % (n, per)}
+
+
+def cpu_oracle_lines(W):
+    """The CPU oracle (plain C, threads over output rows) timed on each secondary
+    configuration, in the unit of that configuration's GPU line where the
+    sample allows it.  Large GEMMs are timed on a sample of their activation
+    rows against all weight rows (the oracle's cost is linear in the rows);
+    about 2 s of oracle work each.  Keyed by the GPU line's workload name."""
+    import oracle
+    threads = oracle.default_threads()
+    out = {}
+
+    def rec(value, unit, sample, rows, **kw):
+        # the oracle splits its work by output row: min(threads, rows) threads
+        d = {"value": value, "unit": unit, "cores": min(threads, rows), "kind": "oracle",
+             "sample": sample}
+        d.update(kw)
+        return d
+
+    # small GEMM, whole call (quantize + GEMM), all threads and one thread
+    s = W.SMALL
+    x = W.activations("small", s.m, s.k)
+    qw, dw = oracle.quantize_q8_0(W.weights("small", s.n, s.k))
+
+    def small(nt):
+        qa, da = oracle.quantize_q8_0(x)
+        oracle.qgemm_q8_0(qa, da, qw, dw, nthreads=nt)
+    per, n = _timed(lambda: small(threads), 1.0)
+    per1, n1 = _timed(lambda: small(1), 1.0)
+    out["small Q8_0 GEMM M=%d K=%d N=%d" % (s.m, s.k, s.n)] = rec(
+        round(per * 1e6, 2), "us per call (quantize + GEMM)", "%d whole calls" % n, s.m,
+        single_thread={"value": round(per1 * 1e6, 2), "unit": "us per call",
+                       "sample": "%d whole calls on 1 thread" % n1})
+
+    # decode M = 4, 16 (whole steps; bytes as in the GPU lines)
+    s1 = W.DECODE[0]
+    qw, dw = oracle.quantize_q8_0(W.weights("decode", s1.n, s1.k))
+    for sd in W.DECODE[1:]:
+        x = W.activations("decode", sd.m, sd.k)
+
+        def dstep():
+            qa, da = oracle.quantize_q8_0(x)
+            oracle.qgemm_q8_0(qa, da, qw, dw, nthreads=threads)
+        per, n = _timed(dstep, 2.0)
+        a_bytes = sd.m * sd.k + sd.m * (sd.k // 32) * 2
+        byt = sd.n * sd.k + sd.n * (sd.k // 32) * 2 + a_bytes + sd.m * sd.n * 4 + sd.m * sd.k * 4 + a_bytes
+        out["decode M=%d K=%d N=%d" % (sd.m, sd.k, sd.n)] = rec(
+            round(byt / per / 1e9, 3), "GB/s", "%d whole steps, %.4f s each" % (n, per), sd.m)
+    del qw, dw
+
+    # prefill, short prefill and long prefill: sampled activation rows
+    for name, shape, rows in (("prefill", W.PREFILL, 32), ("prefill_short", W.PREFILL_SHORT, 32),
+                              ("long", W.LONG, 96)):
+        wl = "prefill" if name == "prefill_short" else name
+        if name != "prefill_short":
+            qw, dw = oracle.quantize_q8_0(W.weights(wl, shape.n, shape.k))
+        x = W.activations(wl, rows, shape.k)
+
+        def gstep():
+            qa, da = oracle.quantize_q8_0(x)
+            oracle.qgemm_q8_0(qa, da, qw, dw, nthreads=threads)
+        per, n = _timed(gstep, 1.5)
+        tops = 2.0 * rows * shape.n * shape.k / per / 1e12
+        out["%s GEMM M=%d K=%d N=%d" % (name, shape.m, shape.k, shape.n)] = rec(
+            round(tops, 5), "int8-equiv TOPS",
+            "%d of %d activation rows against all %d weight rows (quantize + GEMM), %d runs of "
+            "%.3f s; the whole GEMM would take about %.1f s" % (rows, shape.m, shape.n, n, per,
+                                                              per * shape.m / rows), rows)
+    del qw, dw
+
+    # grouped W4A8: a sample of tokens with their top-8 routes
+    m = W.MOE
+    wq4, wd = W.random_w4_codes(m.experts, m.n, m.k)
+    ids = W.topk_ids(m.tokens, m.top_k, m.experts)
+    tok = 96
+    qa, da = oracle.quantize_q8_0(W.activations("moe", tok, m.k))
+    per, n = _timed(lambda: oracle.qgemm_w4a8_grouped(qa, da, ids[:tok], wq4, wd, nthreads=threads), 1.5)
+    out["grouped W4A8 T=%d top-%d E=%d K=%d N=%d" % (m.tokens, m.top_k, m.experts, m.k, m.n)] = rec(
+        round(2.0 * tok * m.top_k * m.n * m.k / per / 1e12, 5), "int8-equiv TOPS",
+        "%d of %d tokens (%d routed rows), %d runs of %.3f s; the whole call would take about "
+        "%.1f s" % (tok, m.tokens, tok * m.top_k, n, per, per * m.tokens / tok), tok * m.top_k)
+
+    # grouped W4A8 decode, whole calls; bytes as in the GPU lines
+    for T in (1, 4, 16):
+        ids_t = W.topk_ids(T, m.top_k, m.experts, seed=T)
+        qa, da = oracle.quantize_q8_0(W.activations("moe", T, m.k, seed=T))
+        per, n = _timed(lambda: oracle.qgemm_w4a8_grouped(qa, da, ids_t, wq4, wd, nthreads=threads), 0.5)
+        active = len(np.unique(ids_t))
+        R = T * m.top_k
+        byt = (active * m.n * (m.k // 2 + m.k // 32 * 2) + T * (m.k + m.k // 32 * 2)
+               + R * 4 + R * m.n * 4)
+        out["grouped W4A8 decode T=%d top-%d E=%d K=%d N=%d (%d active experts)"
+            % (T, m.top_k, m.experts, m.k, m.n, active)] = rec(
+            round(byt / per / 1e9, 3), "GB/s", "%d whole calls, %.4f s each" % (n, per), R)
+    del wq4, wd
+    return out
 
 
 def main():
@@ -592,6 +772,9 @@ def main():
         torch.cuda.empty_cache()
     also = []
     if not args.only_headline:
+        if "small" in wl:
+            also.append(bench_small(bqi, torch, W, 200))
+            log(json.dumps(also[-1]))
         if "decode_m" in wl:
             for r in bench_decode_variants(bqi, torch, W, 200):
                 also.append(r)
@@ -625,11 +808,17 @@ def main():
                 log(json.dumps(r))
     if res is None:
         return
-    if also:
-        res["also"] = also
     if not args.no_cpu:
         log("cpu baseline (~%.0f s)" % args.cpu_seconds)
         res["cpu_baseline"] = cpu_baseline(W, ctx["step_bytes"], args.cpu_seconds)
+        if also:
+            log("cpu oracle on the other configurations")
+            legs = cpu_oracle_lines(W)
+            for r in also:
+                if r.get("workload") in legs:
+                    r["cpu_oracle"] = legs[r["workload"]]
+    if also:
+        res["also"] = also
     print(json.dumps(res), flush=True)
 
 
