@@ -53,8 +53,12 @@ METRIC = "int8-equiv TOPS (% MFMA peak) prefill GEMM; GB/s (% HBM peak) M=1 GEMV
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0      # dense int8 MFMA, MI355X
 # fp32 vector FMA lane-ops per second: MI355X's published 157.3 TFLOP/s fp32
-# vector rate counts each FMA as two flops (256 CU x 128 lanes x 2.4 GHz)
+# vector rate counts each FMA as two flops (256 CU x 128 lanes x 2.4 GHz);
+# that rate needs packed fp32 instructions, which this library does not use.
+# Unpacked, a SIMD retires 16 fp32 FMA lanes per cycle (the published fp64
+# vector rate, 78.6 TFLOP/s): 256 CU x 64 lanes x 2.4 GHz.
 VALU_LANE_OPS_PEAK = 157.3e12 / 2
+VALU_LANE_OPS_UNPACKED = 78.6e12 / 2
 
 
 def parse():
@@ -418,6 +422,7 @@ def bench_gemm(bqi, torch, W, name, iters):
         "mean_launch_us": round(mean * 1e3, 2),
         "frac_int8_mfma_peak": round(tops / INT8_PEAK_TOPS, 4),
         "epilogue_valu_frac": round(valu_ops / (mean * 1e-3) / VALU_LANE_OPS_PEAK, 4),
+        "epilogue_valu_frac_unpacked": round(valu_ops / (mean * 1e-3) / VALU_LANE_OPS_UNPACKED, 4),
         "hbm_bytes_algorithmic": byt,
         "hbm_bytes_stored_counters": traffic("%s %s" % (kernel, name)),
         "quantize": {"kernel": "k_quantize_q8_0", "mean_launch_us": round(qmean * 1e3, 2),
@@ -459,6 +464,8 @@ def bench_moe(bqi, torch, W, iters):
             "mean_call_us": round(mean * 1e3, 2),
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "int8_equiv_TOPS": round(ops / (mean * 1e-3) / 1e12, 2),
+            "epilogue_valu_frac_unpacked": round(2.0 * R * m.n * (m.k // 32) / (mean * 1e-3)
+                                                 / VALU_LANE_OPS_UNPACKED, 4),
             "weight_copies_rotated": copies, "hbm_bytes_algorithmic": byt,
             "hbm_bytes_stored_counters": traffic("k_grouped_w4a8 moe")}
 
