@@ -58,13 +58,40 @@ __device__ __forceinline__ int route_scan(int v, int *s_tmp, int &total) {
   return wave_base + incl - v;
 }
 
+// The dispatch order of the grouped GEMM (order != nullptr, n_experts <=
+// ROUTE_RANK_MAX): every workgroup also counts all experts' routed rows into
+// LDS, takes its expert's rank by descending count (ties by index) as one
+// workgroup sum of comparisons, and writes order[rank] = e.
+constexpr int ROUTE_RANK_MAX = 256;
+
+__device__ __forceinline__ void route_rank(int e, int n_experts, const int *s_hist,
+                                           int *s_tmp, int32_t *order) {
+  const int tid = threadIdx.x;
+  const int c = s_hist[e];
+  int flag = 0;
+  if (tid < n_experts) {
+    const int cj = s_hist[tid];
+    flag = (cj > c) || (cj == c && tid < e);
+  }
+  int rank;
+  (void)route_scan(flag, s_tmp, rank);
+  if (tid == 0) order[rank] = e;
+}
+
 __global__ __launch_bounds__(RT) void k_route(
     const int32_t *__restrict__ ids, int rows_total, int n_experts, int top_k,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ rows, float *__restrict__ y, int n) {
+    int32_t *__restrict__ rows, int32_t *__restrict__ order, float *__restrict__ y,
+    int n) {
   __shared__ int s_tmp[RT / 64];
+  __shared__ int s_hist[ROUTE_RANK_MAX];
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
+  const bool rank = order != nullptr && n_experts <= ROUTE_RANK_MAX;
+  if (rank) {
+    if (tid < ROUTE_RANK_MAX) s_hist[tid] = 0;
+    __syncthreads();
+  }
 
   if (rows_total <= RCHUNK) {
     // one pass: each thread keeps its 8 ids in registers; one workgroup scan
@@ -79,9 +106,12 @@ __global__ __launch_bounds__(RT) void k_route(
       v[j] = r0 + j < rows_total ? ids[r0 + j] : -1;
       below += (v[j] >= 0 && v[j] < e);
       eq += (v[j] == e);
+      if (rank && v[j] >= 0 && v[j] < n_experts) atomicAdd(&s_hist[v[j]], 1);
     }
     int total;
-    const int excl = route_scan((below << 16) | eq, s_tmp, total);
+    const int excl = route_scan((below << 16) | eq, s_tmp, total);  // its barriers
+                                                                    // also publish s_hist
+    if (rank) route_rank(e, n_experts, s_hist, s_tmp, order);
     const int n_below = total >> 16, n_eq = total & 0xffff;
     if (tid == 0) {
       counts[e] = n_eq;
@@ -115,11 +145,13 @@ __global__ __launch_bounds__(RT) void k_route(
       const int v = r < rows_total ? ids[r] : -1;
       below += (v >= 0 && v < e);
       eq += (v == e);
+      if (rank && v >= 0 && v < n_experts) atomicAdd(&s_hist[v], 1);
     }
   }
   int n_below, n_eq;
   (void)route_scan(below, s_tmp, n_below);
   (void)route_scan(eq, s_tmp, n_eq);
+  if (rank) route_rank(e, n_experts, s_hist, s_tmp, order);
   if (tid == 0) {
     counts[e] = n_eq;
     offsets[e] = n_below;
@@ -510,36 +542,18 @@ __global__ __launch_bounds__(GT, 3) void k_grouped_w4a8(
     const uint8_t *__restrict__ wq4, const uint16_t *__restrict__ wd,
     int n_experts, int n, int k, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ rows,
-    float *__restrict__ y) {
+    const int32_t *__restrict__ order, float *__restrict__ y) {
   __shared__ __attribute__((aligned(16))) GBuf S[GNS];
   __shared__ int s_tok[GCH];  // token of each staged row
   __shared__ int s_row[GCH];  // routed row (output row) of each staged row
-  __shared__ int s_cnt[GT];
-  __shared__ int s_e;
 
   const int tiles_n = (n + GBN - 1) / GBN;
   const int unit = blockIdx.x / tiles_n;
   const int tn = blockIdx.x - unit * tiles_n;
   const int tid = threadIdx.x;
-  int e;
-  if (n_experts <= GT) {
-    // the expert of rank `unit` by descending routed-row count (ties by index)
-    const int c = tid < n_experts ? counts[tid] : 0;
-    s_cnt[tid] = c;
-    __syncthreads();
-    if (tid < n_experts) {
-      int rank = 0;
-      for (int j = 0; j < n_experts; ++j) {
-        const int cj = s_cnt[j];
-        rank += (cj > c) || (cj == c && j < tid);
-      }
-      if (rank == unit) s_e = tid;
-    }
-    __syncthreads();
-    e = __builtin_amdgcn_readfirstlane(s_e);
-  } else {
-    e = unit;
-  }
+  // the expert of rank `unit` by descending routed-row count, as the routing
+  // pass ordered them (natural order past its ranking limit)
+  const int e = n_experts <= ROUTE_RANK_MAX ? order[unit] : unit;
   const int cnt = counts[e];
   if (cnt == 0) return;
   const int off = offsets[e];
@@ -568,11 +582,11 @@ __global__ __launch_bounds__(GT, 3) void k_grouped_w4a8(
 
 hipError_t launch_route_topk(const int32_t *ids, int64_t rows_total,
                              int64_t n_experts, int64_t top_k, int32_t *counts,
-                             int32_t *offsets, int32_t *rows, float *y,
-                             int64_t n, hipStream_t stream) {
+                             int32_t *offsets, int32_t *rows, int32_t *order,
+                             float *y, int64_t n, hipStream_t stream) {
   hipLaunchKernelGGL(k_route, dim3((unsigned)n_experts), dim3(RT), 0, stream,
                      ids, (int)rows_total, (int)n_experts, (int)top_k, counts,
-                     offsets, rows, y, (int)n);
+                     offsets, rows, order, y, (int)n);
   return hipGetLastError();
 }
 
@@ -581,11 +595,11 @@ hipError_t launch_grouped_w4a8(const int8_t *aq, const uint16_t *ad,
                                const uint16_t *wd, int64_t n_experts, int64_t n,
                                int64_t k, const int32_t *counts,
                                const int32_t *offsets, const int32_t *rows,
-                               float *y, hipStream_t stream) {
+                               const int32_t *order, float *y, hipStream_t stream) {
   const int64_t tiles_n = (n + GBN - 1) / GBN;
   hipLaunchKernelGGL(k_grouped_w4a8, dim3((unsigned)(n_experts * tiles_n)),
                      dim3(GT), 0, stream, aq, ad, (int)top_k, wq4, wd,
-                     (int)n_experts, (int)n, (int)k, counts, offsets, rows, y);
+                     (int)n_experts, (int)n, (int)k, counts, offsets, rows, order, y);
   return hipGetLastError();
 }
 

@@ -611,6 +611,31 @@ def test_grouped_w4a8_beyond_one_routing_chunk():
     assert bad.sum() == 6 and (y[bad] == 0).all()
 
 
+@pytest.mark.parametrize("T,tk,E", [
+    (1024, 8, 128),   # 8192 routed rows: the routing pass in one pass over ids in registers
+    (1025, 8, 128),   # 8200: two chunks of ids
+    (2048, 4, 256),   # the most experts the routing pass orders by count
+    (1000, 4, 300)])  # more: the GEMM takes the experts in index order
+def test_grouped_w4a8_routing_paths_at_their_limits(T, tk, E):
+    """The MFMA path at the routing pass's limits (ids held in registers, and
+    the dispatch order by routed-row count), with a few invalid ids (their
+    rows must be zero), against the oracle."""
+    K, N = 256, 160
+    log("grouped routing paths T=%d top_k=%d E=%d" % (T, tk, E))
+    ids = W.topk_ids(T, tk, E, seed=T + E)
+    ids[3, 0] = -2
+    ids[T - 1, tk - 1] = E
+    ids[T // 2, 0] = 1 << 20
+    qa = W.random_int8("moe", 706, (T, K), seed=T)
+    da = W.random_scales("moe", 707, (T, K // 32), seed=T)
+    packed, wsc = W.random_w4_codes(E, N, K, seed=T)
+    y = run_grouped(qa, da, ids, packed, wsc)
+    yr, asum = oracle.qgemm_w4a8_grouped(qa, da, ids, packed, wsc, nthreads=oracle_threads())
+    assert_within_bound(y, yr, asum, K // 32, "routing paths T=%d E=%d" % (T, E))
+    bad = (ids < 0) | (ids >= E)
+    assert bad.sum() == 3 and (y[bad] == 0).all()
+
+
 def test_wrappers_on_an_explicit_side_stream():
     """Every wrapper given a stream other than the current one (a
     torch.cuda.Stream, and a raw hipStream_t handle) allocates its outputs and
