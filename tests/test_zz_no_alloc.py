@@ -1,11 +1,11 @@
 """The allocation-free grouped W4A8 entry point (qgemm_w4a8_grouped_noalloc,
 called through the C ABI) against the workspace entry point
 (qgemm_w4a8_grouped) on the same inputs: bit-identical outputs, on two calls
-in a row, the second with a smaller input.  Up to 8192 routed rows the MFMA
-kernel routes for itself and the array is not touched; past that the routing
-pass fills it, and the last pair of calls runs there, the second over what the
-first left in the array.  Also the decode size (no workspace used) and a
-problem the array cannot hold (rejected, nothing written)."""
+in a row, the second with a smaller input, so that the second runs over what
+the first left in the library's array (the last pair past 8192 routed rows,
+where the routing pass works through its ids in chunks).  Also the decode size
+(no workspace used) and a problem the array cannot hold (rejected, nothing
+written)."""
 import ctypes as C
 
 import numpy as np
@@ -54,7 +54,7 @@ def noalloc_call(qa, da, ids, wq4, wd, y):
 @pytest.mark.parametrize("first,second", [
     ((947, 8, 128, 2048, 768), (300, 8, 128, 2048, 768)),   # the MoE workload, then fewer tokens
     ((600, 4, 16, 512, 200), (150, 2, 16, 512, 200)),       # fewer slots, ragged N
-    # past 8192 routed rows: the routing pass fills the library's array
+    # past 8192 routed rows: the routing pass in chunks of ids
     ((1300, 8, 64, 256, 96), (1100, 8, 64, 256, 96))])
 def test_noalloc_matches_workspace_entry_point(first, second):
     for i, shape in enumerate((first, second)):
