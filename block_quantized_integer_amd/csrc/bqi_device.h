@@ -33,11 +33,11 @@ __device__ __forceinline__ int32_t dot4_i8(int32_t a, int32_t b, int32_t c) {
   return __builtin_amdgcn_sdot4(a, b, c, false);
 }
 
-// max(v, v of the lane that the DPP control CTRL selects)
+// max(v, v of the lane that the DPP control CTRL selects), unsigned
 template <int CTRL>
-__device__ __forceinline__ float dpp_max(float v) {
-  return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                      __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false)));
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
+  return v > o ? v : o;
 }
 
 // Q8_0 quantization of one 32-element block by the 8 consecutive lanes that
@@ -48,36 +48,63 @@ __device__ __forceinline__ float dpp_max(float v) {
 // stored d (d == 0 gives codes 0 and scale bits 0).  Returns
 // this lane's 4 codes packed (element 4*sub + i in byte i) and sets the
 // block's scale bits.  Every quantizer in the library goes through this
-// function, so all of them produce identical codes.  Never compile with
+// function, so all of them produce identical codes.  Finite inputs only (NaN
+// and Inf are outside the quantizer's contract).  Never compile with
 // fast-math.
 __device__ __forceinline__ uint32_t q8_0_quantize4(const float (&v)[4], uint16_t &d_bits) {
-  float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  // |x| as its bit pattern: for finite values the unsigned order of the
+  // magnitude bits is the order of the magnitudes
+  uint32_t am = __builtin_bit_cast(uint32_t, v[0]) & 0x7fffffffu;
+#pragma unroll
+  for (int i = 1; i < 4; ++i) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, v[i]) & 0x7fffffffu;
+    am = am > b ? am : b;
+  }
   // reduce over the 8 lanes of this block (lanes differ in bits 0..2) with
   // DPP moves, no LDS round trip: lane ^ 1 and lane ^ 2 (quad permutations),
   // then the mirror inside each 8-lane half-row, which pairs every lane of
   // one quad with a lane of the other
-  amax = dpp_max<0xb1>(amax);   // quad_perm [1, 0, 3, 2]
-  amax = dpp_max<0x4e>(amax);   // quad_perm [2, 3, 0, 1]
-  amax = dpp_max<0x141>(amax);  // row_half_mirror
+  am = dpp_max_u32<0xb1>(am);   // quad_perm [1, 0, 3, 2]
+  am = dpp_max_u32<0x4e>(am);   // quad_perm [2, 3, 0, 1]
+  am = dpp_max_u32<0x141>(am);  // row_half_mirror
+  const float amax = __builtin_bit_cast(float, am);
   const _Float16 dh = (_Float16)(amax / 127.0f);  // IEEE div, then RNE
   const float dd = (float)dh;
   uint32_t packed = 0;
   if (dd != 0.0f) {
-    // The code is round-half-away(|x| / d) with the sign of x, taken from the
-    // exact quotient without a division: a candidate k from an approximate
-    // reciprocal (relative error ~2^-22, so k is off by at most one for
-    // |x| / d < 2^20), then corrected with the exact signs of
-    // |x| - (k -/+ 1/2) d: (k +/- 1/2) d has at most 9 + 11 significant bits,
-    // so it is exact in fp32, and the fma rounds the difference once, which
-    // keeps its sign.  |x| = (k + 1/2) d exactly (a tie) rounds up.
+    // The code is round-half-away(|x| / d) with the sign of x.  First from
+    // an approximate reciprocal: u = |x| * r + 1/2 (one fma) is within
+    // 5e-5 of the exact |x| / d + 1/2 (r within 1 ulp of 1/d, |x| / d <
+    // 256, one rounding of a value below 257), so floor(u) is the exact
+    // code unless u lies within 2^-12 of an integer.  Such near-ties, rare,
+    // are decided exactly instead: the candidate k is corrected with the
+    // signs of |x| - (k -/+ 1/2) d, where (k +/- 1/2) d has at most 9 + 11
+    // significant bits, so it is exact in fp32, and the fma rounds the
+    // difference once, which keeps its sign; |x| = (k + 1/2) d exactly (a
+    // tie) rounds up.
     const float r = __builtin_amdgcn_rcpf(dd);
+    float kf[4];
+    bool near = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float ax = fabsf(v[i]);
-      float k = floorf(fmaf(ax, r, 0.5f));
-      if (fmaf(-(k - 0.5f), dd, ax) < 0.0f) k -= 1.0f;
-      if (fmaf(-(k + 0.5f), dd, ax) >= 0.0f) k += 1.0f;
-      const int32_t q = (int32_t)fminf(k, 127.0f);
+      const float u = fmaf(fabsf(v[i]), r, 0.5f);
+      kf[i] = floorf(u);
+      const float fr = u - kf[i];  // exact: in [0, 1)
+      near |= fabsf(fr - 0.5f) > 0.5f - 0x1p-12f;
+    }
+    if (near) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ax = fabsf(v[i]);
+        float k = kf[i];
+        if (fmaf(-(k - 0.5f), dd, ax) < 0.0f) k -= 1.0f;
+        if (fmaf(-(k + 0.5f), dd, ax) >= 0.0f) k += 1.0f;
+        kf[i] = k;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t q = (int32_t)fminf(kf[i], 127.0f);
       packed |= ((uint32_t)(v[i] < 0.0f ? -q : q) & 0xffu) << (8 * i);
     }
   }

@@ -23,7 +23,9 @@
 
 namespace bqi {
 
-template <bool F16, typename Idx>
+// CONTIG: rows are contiguous (ldx == k), so block blk starts at element
+// 32 * blk and no row / column split is needed.
+template <bool F16, bool CONTIG, typename Idx>
 __global__ __launch_bounds__(256) void k_quantize_q8_0(
     const void *__restrict__ x, Idx ldx, Idx blocks_per_row, Idx total_blocks,
     int8_t *__restrict__ q, uint16_t *__restrict__ d) {
@@ -31,9 +33,14 @@ __global__ __launch_bounds__(256) void k_quantize_q8_0(
   const Idx stride = (Idx)((gridDim.x * (uint32_t)blockDim.x) >> 3);
   for (Idx blk = (Idx)((blockIdx.x * (uint32_t)blockDim.x + threadIdx.x) >> 3);
        blk < total_blocks; blk += stride) {
-    const Idx row = blk / blocks_per_row;
-    const Idx b = blk - row * blocks_per_row;
-    const Idx off = row * ldx + b * QK + sub * 4;
+    Idx off;
+    if constexpr (CONTIG) {
+      off = blk * QK + sub * 4;
+    } else {
+      const Idx row = blk / blocks_per_row;
+      const Idx b = blk - row * blocks_per_row;
+      off = row * ldx + b * QK + sub * 4;
+    }
     float v[4];
     if constexpr (F16) {
       const uint2 raw = *reinterpret_cast<const uint2 *>(
@@ -70,23 +77,28 @@ hipError_t launch_quantize_q8_0(const void *x, bool f16, int64_t rows,
   if (wgs > cap) wgs = cap;
   const dim3 grid((unsigned)wgs), block(256);
   const bool small = rows * ldx < ((int64_t)1 << 31) && total < ((int64_t)1 << 28);
+  const bool contig = ldx == k;
+#define BQI_QUANT_LAUNCH(F16_, CONTIG_, IDX_)                                        \
+  hipLaunchKernelGGL((k_quantize_q8_0<F16_, CONTIG_, IDX_>), grid, block, 0, stream, x, \
+                     (IDX_)ldx, (IDX_)bpr, (IDX_)total, q, d)
   if (f16) {
-    if (small)
-      hipLaunchKernelGGL((k_quantize_q8_0<true, uint32_t>), grid, block, 0,
-                         stream, x, (uint32_t)ldx, (uint32_t)bpr,
-                         (uint32_t)total, q, d);
-    else
-      hipLaunchKernelGGL((k_quantize_q8_0<true, int64_t>), grid, block, 0,
-                         stream, x, ldx, bpr, total, q, d);
+    if (small) {
+      if (contig) BQI_QUANT_LAUNCH(true, true, uint32_t);
+      else BQI_QUANT_LAUNCH(true, false, uint32_t);
+    } else {
+      if (contig) BQI_QUANT_LAUNCH(true, true, int64_t);
+      else BQI_QUANT_LAUNCH(true, false, int64_t);
+    }
   } else {
-    if (small)
-      hipLaunchKernelGGL((k_quantize_q8_0<false, uint32_t>), grid, block, 0,
-                         stream, x, (uint32_t)ldx, (uint32_t)bpr,
-                         (uint32_t)total, q, d);
-    else
-      hipLaunchKernelGGL((k_quantize_q8_0<false, int64_t>), grid, block, 0,
-                         stream, x, ldx, bpr, total, q, d);
+    if (small) {
+      if (contig) BQI_QUANT_LAUNCH(false, true, uint32_t);
+      else BQI_QUANT_LAUNCH(false, false, uint32_t);
+    } else {
+      if (contig) BQI_QUANT_LAUNCH(false, true, int64_t);
+      else BQI_QUANT_LAUNCH(false, false, int64_t);
+    }
   }
+#undef BQI_QUANT_LAUNCH
   return hipGetLastError();
 }
 
