@@ -11,8 +11,9 @@
 // expert (its offset) and equal to it, and one workgroup scan orders the
 // matches, so rows come out in increasing row order.  Up to 8192 routed rows
 // this is a single pass over ids held in registers; beyond, a counting pass
-// and a placing pass run chunk by chunk.  No atomics, deterministic.  The
-// same pass writes zeros to the output rows of invalid ids.
+// and a placing pass run chunk by chunk.  Deterministic.  The same pass
+// writes zeros to the output rows of invalid ids and, for up to 256 experts,
+// the experts in dispatch order (descending routed-row count, ties by index).
 //
 // GEMM (k_grouped_w4a8): one workgroup of 4 waves per (expert, 128-column
 // tile), three per CU, heaviest expert first; the weights are the MFMA's A
@@ -202,10 +203,10 @@ __global__ __launch_bounds__(RT) void k_route(
 //
 // Three workgroups share a CU (12 waves, 168 VGPRs each), so the MoE
 // workload's 768 (expert, column tile) units run in one round.  Workgroups
-// are dispatched heaviest expert first: each workgroup ranks the experts by
-// routed-row count (descending, ties by index) and takes the expert of rank
-// blockIdx / column_tiles, which spreads the experts of more than 64 rows
-// (two chunks) over different CUs.
+// are dispatched heaviest expert first: workgroup blockIdx takes the expert
+// of rank blockIdx / column_tiles in the routing pass's order (descending
+// routed-row count, ties by index), which spreads the experts of more than
+// 64 rows (two chunks) over different CUs.
 //
 // Stages of GNB = 4 groups (128 K elements) go through two LDS buffers: the
 // loads of stage s+1 are issued before the compute of stage s.  Per stage
