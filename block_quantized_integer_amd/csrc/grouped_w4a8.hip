@@ -371,6 +371,61 @@ __device__ __forceinline__ void grouped_stage(const GBuf &B, int wave, int lane_
   epilogue(dres[(GNB * R - 1) & 1], GNB * R - 1);
 }
 
+// A chunk of at most 16 rows (the last rows of an expert): the same work on
+// 16-row tiles, as two v_mfma_i32_16x16x32_i8 per group (one per 16 of the
+// wave's 32 columns), which halves the epilogue against a padded 32-row
+// tile.  In lane L the A fragment is weight column 16 ct + L%16 and the B
+// fragment routed row L%16, both over K elements 8 (L/16) .. +7 of the group
+// (bytes 8 ((L/16) % 2) .. +7 of the packed group, low nibbles for L < 32);
+// output register r of lane L is column 16 ct + 4 (L/16) + r, row L%16.  The
+// int32 block dots and the epilogue per output are those of the 32-row
+// tile, so the results are bit-identical to it.
+__device__ __forceinline__ int64_t unpack_w4x8(int64_t p, int shl) {
+  const uint32_t lo = (((uint32_t)p << shl) & 0xf0f0f0f0u) ^ 0x80808080u;
+  const uint32_t hi = (((uint32_t)((uint64_t)p >> 32) << shl) & 0xf0f0f0f0u) ^ 0x80808080u;
+  return (int64_t)((uint64_t)lo | ((uint64_t)hi << 32));
+}
+
+__device__ __forceinline__ void grouped_stage_half(const GBuf &B, int wave, int lane_in,
+                                                   const i32x4 &seed4, f32x4 (&acc)[2]) {
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));
+  const int l16 = lane & 15, kg = lane >> 4;
+  const int shl = (kg >> 1) ? 0 : 4;
+  const int aswz_l = (l16 >> 1) & 7;  // aswz of row l16
+  float da[GNB];
+  {
+    const i32x4 v = *reinterpret_cast<const i32x4 *>(&B.as[l16 * GNB]);
+    da[0] = half_bits_to_float((uint16_t)v.x);
+    da[1] = half_bits_to_float((uint16_t)v.y);
+    da[2] = half_bits_to_float((uint16_t)v.z);
+    da[3] = half_bits_to_float((uint16_t)v.w);
+    asm volatile("" : "+v"(da[0]), "+v"(da[1]), "+v"(da[2]), "+v"(da[3]));
+  }
+  auto read_w = [&](int g, int ct) {
+    const int col = wave * 32 + 16 * ct + l16;
+    return *reinterpret_cast<const int64_t *>(&B.w[col * (GNB * 16) + 16 * wswz(col, g) + 8 * (kg & 1)]);
+  };
+  auto read_b = [&](int g) {
+    return *reinterpret_cast<const int64_t *>(
+        &B.a[l16 * GBK + 16 * ((2 * g + (kg >> 1)) ^ aswz_l) + 8 * (kg & 1)]);
+  };
+#pragma unroll
+  for (int g = 0; g < GNB; ++g) {
+    const int64_t b = read_b(g);
+    const i32x4 d0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(unpack_w4x8(read_w(g, 0), shl), b, seed4, 0, 0, 0);
+    const i32x4 d1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(unpack_w4x8(read_w(g, 1), shl), b, seed4, 0, 0, 0);
+    const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&B.ws[g][wave * 32 + 4 * kg]);
+    const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&B.ws[g][wave * 32 + 16 + 4 * kg]);
+    const float sa = da[g], ncd = -MAGIC_F * sa;  // exact
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      acc[0][r] = fmaf(fmaf(bits_to_float(d0[r]), sa, ncd), w0[r], acc[0][r]);
+      acc[1][r] = fmaf(fmaf(bits_to_float(d1[r]), sa, ncd), w1[r], acc[1][r]);
+    }
+  }
+}
+
 struct GArgs {
   const int8_t *aq;
   const uint16_t *ad;
@@ -383,9 +438,11 @@ struct GArgs {
 
 // One chunk of up to 32*R routed rows of expert e against the workgroup's 128
 // columns: the whole K pipeline, then the stores.
-template <int R>
+// HALF: at most 16 rows, computed on 16-row tiles (R == 1).
+template <int R, bool HALF = false>
 __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], const int *s_tok,
                                               const int *s_row, int e, int n0, int crows) {
+  static_assert(!HALF || R == 1, "16-row tiles stage one 32-row tile's loads");
   const int n = A.n, k = A.k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -397,6 +454,8 @@ __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], co
 #pragma unroll
   for (int r = 0; r < 16; ++r) seed[r] = MAGIC_BITS;
   asm volatile("" : "+v"(seed));  // kept resident, not rebuilt per stage
+  i32x4 seed4 = {MAGIC_BITS, MAGIC_BITS, MAGIC_BITS, MAGIC_BITS};
+  asm volatile("" : "+v"(seed4));
 
   // per-lane load coordinates, fixed for the chunk
   // weights: chunk e = 64 (2w + q) + L -> column e/4, slot e%4 (group slot ^ wswz)
@@ -492,10 +551,16 @@ __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], co
   };
 
   f32x16 acc[R];
+  f32x4 acc16[2];
+  if constexpr (HALF) {
 #pragma unroll
-  for (int t = 0; t < R; ++t)
+    for (int ct = 0; ct < 2; ++ct) acc16[ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
+    for (int t = 0; t < R; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
+  }
 
   // Stage s waits for its own loads (issued before stage s-1's compute); the
   // barrier then makes every wave's loads of stage s visible and frees the
@@ -506,13 +571,35 @@ __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], co
     lds_barrier();
     if (s + 1 < stages) issue(s + 1);
     convert_ws(s);
-    grouped_stage<R>(S[s % GNS], wave, lane, seed, acc);
+    if constexpr (HALF)
+      grouped_stage_half(S[s % GNS], wave, lane, seed4, acc16);
+    else
+      grouped_stage<R>(S[s % GNS], wave, lane, seed, acc);
   }
 
+  const bool vec = (n & 3) == 0 && ((uintptr_t)A.y & 15) == 0;
+  if constexpr (HALF) {
+    // store: lane's routed row L%16, columns n0 + 32 wave + 16 ct + 4 (L/16) + (0..3)
+    const int rr = lane & 15;
+    if (rr < crows) {
+      float *yrow = A.y + (int64_t)s_row[rr] * n;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int c = n0 + wave * 32 + 16 * ct + 4 * (lane >> 4);
+        if (vec && c + 3 < n) {
+          *reinterpret_cast<f32x4 *>(yrow + c) = acc16[ct];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (c + i < n) yrow[c + i] = acc16[ct][i];
+        }
+      }
+    }
+    return;
+  }
   // store: lane's routed row 32t + L%32 of the chunk, columns
   // n0 + 32 wave + 8q + 4(L/32) + (0..3) in registers 4q .. 4q+3
   const int l32 = lane & 31, h = lane >> 5;
-  const bool vec = (n & 3) == 0 && ((uintptr_t)A.y & 15) == 0;
 #pragma unroll
   for (int t = 0; t < R; ++t) {
     const int rr = 32 * t + l32;
@@ -572,10 +659,12 @@ __global__ __launch_bounds__(GT, 3) void k_grouped_w4a8(
       s_tok[tid] = rr / top_k;
     }
     __syncthreads();
-    switch ((crows + 31) / 32) {
-      case 1: grouped_chunk<1>(A, S, s_tok, s_row, e, n0, crows); break;
-      default: grouped_chunk<2>(A, S, s_tok, s_row, e, n0, crows); break;
-    }
+    if (crows <= 16)
+      grouped_chunk<1, true>(A, S, s_tok, s_row, e, n0, crows);
+    else if (crows <= 32)
+      grouped_chunk<1>(A, S, s_tok, s_row, e, n0, crows);
+    else
+      grouped_chunk<2>(A, S, s_tok, s_row, e, n0, crows);
   }
 }
 

@@ -578,12 +578,34 @@ def grouped_one_hot_probe(T, top_k, E, K, N, seed):
 
 @pytest.mark.parametrize("T,top_k,E,K,N", [
     (160, 4, 16, 256, 96),     # k_grouped_w4a8: ~40 rows per expert (one 32-row tile or two)
-    (300, 2, 4, 2048, 130),    # k_grouped_w4a8: ~150 rows per expert (two 96-row chunks), ragged N
+    (300, 2, 4, 2048, 130),    # k_grouped_w4a8: ~150 rows per expert (64-row chunks), ragged N
+    (300, 1, 4, 256, 160),     # k_grouped_w4a8: ~75 rows per expert, tails on 16-row tiles
     (12, 8, 32, 256, 96),      # k_grouped_gemv: 96 routed rows
     (16, 8, 128, 2048, 768)])  # k_grouped_gemv at the MoE expert shape (128 routed rows)
 def test_grouped_block_dots_bitexact_probe(T, top_k, E, K, N):
     log("grouped probe T=%d top_k=%d E=%d K=%d N=%d" % (T, top_k, E, K, N))
     grouped_one_hot_probe(T, top_k, E, K, N, seed=T + K)
+
+
+@pytest.mark.parametrize("counts", [(65, 80, 16, 1, 15, 17), (96, 81, 33, 48, 64, 32)])
+def test_grouped_w4a8_chunk_tails(counts):
+    """Experts whose last chunk of rows has 1..16 rows (the 16-row tiles), 17..32
+    rows or a full 64, with exact row counts (top_k = 1, tokens assigned to
+    experts in a shuffled order), against the oracle."""
+    E, K, N = len(counts), 256, 160
+    g = np.random.default_rng(zlib.crc32(repr(counts).encode()))
+    ids = np.repeat(np.arange(E, dtype=np.int32), counts)
+    g.shuffle(ids)
+    ids = ids.reshape(-1, 1)
+    T = ids.shape[0]
+    log("grouped chunk tails %s" % (counts,))
+    qa = W.random_int8("moe", 708, (T, K), seed=T)
+    da = W.random_scales("moe", 709, (T, K // 32), seed=T)
+    packed = g.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    wsc = W.random_scales("moe", 710, (E, N, K // 32), seed=T)
+    y = run_grouped(qa, da, ids, packed, wsc)
+    yr, asum = oracle.qgemm_w4a8_grouped(qa, da, ids, packed, wsc, nthreads=oracle_threads())
+    assert_within_bound(y, yr, asum, K // 32, "chunk tails %s" % (counts,))
 
 
 def test_grouped_w4a8_beyond_one_routing_chunk():
