@@ -158,6 +158,29 @@ def distribution(samples_ms):
             "median_us": round(float(q[1]), 3), "p90_us": round(float(q[2]), 3)}
 
 
+# Workload names of the secondary lines; the CPU-oracle lines attach to the
+# GPU lines by these names.
+def name_small(s):
+    return "small Q8_0 GEMM M=%d K=%d N=%d" % (s.m, s.k, s.n)
+
+
+def name_decode(s):
+    return "decode M=%d K=%d N=%d" % (s.m, s.k, s.n)
+
+
+def name_gemm(name, s):
+    return "%s GEMM M=%d K=%d N=%d" % (name, s.m, s.k, s.n)
+
+
+def name_moe(m):
+    return "grouped W4A8 T=%d top-%d E=%d K=%d N=%d" % (m.tokens, m.top_k, m.experts, m.k, m.n)
+
+
+def name_moe_decode(m, T, active):
+    return ("grouped W4A8 decode T=%d top-%d E=%d K=%d N=%d (%d active experts)"
+            % (T, m.top_k, m.experts, m.k, m.n, active))
+
+
 CSRC = os.path.join(ROOT, "block_quantized_integer_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 TRAFFIC_SOURCE = ("stored figure, not measured in this run: HBM bytes per launch from the "
@@ -330,7 +353,7 @@ def bench_small(bqi, torch, W, iters):
     dist = distribution(T.samples)
     ms_gemm = T.loop(lambda i: bqi.qgemm_q8_0(aq, ad, wq, wd, y), iters, check=lambda: y)
     ms_eager = T.loop(call, iters, graph=False)
-    return {"workload": "small Q8_0 GEMM M=%d K=%d N=%d" % (s.m, s.k, s.n),
+    return {"workload": name_small(s),
             "kernel": "k_quantize_q8_0 + k_gemv_mfma16",
             "value": round(ms * 1e3, 3), "unit": "us per call (quantize + GEMM)",
             "higher_is_better": False, "bound": "launch",
@@ -374,7 +397,7 @@ def bench_decode_variants(bqi, torch, W, iters):
         a_bytes = s.m * s.k + s.m * (s.k // 32) * 2
         gemv_bytes = w_bytes + a_bytes + s.m * s.n * 4
         step_bytes = gemv_bytes + s.m * s.k * 4 + a_bytes
-        res.append({"workload": "decode M=%d K=%d N=%d" % (s.m, s.k, s.n), "kernel": kernel,
+        res.append({"workload": name_decode(s), "kernel": kernel,
                     "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s",
                     "ms_per_step": round(ms_step, 6),
                     "frac_hbm_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -417,7 +440,7 @@ def bench_gemm(bqi, torch, W, name, iters):
     qbytes = s.m * s.k * 4 + s.m * (s.k + s.k // 32 * 2)
     del xa
     return {
-        "workload": "%s GEMM M=%d K=%d N=%d" % (name, s.m, s.k, s.n),
+        "workload": name_gemm(name, s),
         "kernel": kernel, "value": round(tops, 2), "unit": "int8-equiv TOPS",
         "mean_launch_us": round(mean * 1e3, 2),
         "frac_int8_mfma_peak": round(tops / INT8_PEAK_TOPS, 4),
@@ -458,8 +481,7 @@ def bench_moe(bqi, torch, W, iters):
            + R * 4 + R * m.n * 4)
     ops = 2.0 * R * m.n * m.k
     gbs = byt / (mean * 1e-3) / 1e9
-    return {"workload": "grouped W4A8 T=%d top-%d E=%d K=%d N=%d" % (m.tokens, m.top_k, m.experts,
-                                                                    m.k, m.n),
+    return {"workload": name_moe(m),
             "kernel": "k_route + k_grouped_w4a8", "value": round(gbs, 1), "unit": "GB/s",
             "mean_call_us": round(mean * 1e3, 2),
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
@@ -501,8 +523,7 @@ def bench_moe_decode(bqi, torch, W, iters):
         byt = (active * m.n * (m.k // 2 + m.k // 32 * 2) + T * (m.k + m.k // 32 * 2)
                + R * 4 + R * m.n * 4)
         gbs = byt / (mean * 1e-3) / 1e9
-        res.append({"workload": "grouped W4A8 decode T=%d top-%d E=%d K=%d N=%d (%d active experts)"
-                                % (T, m.top_k, m.experts, m.k, m.n, active),
+        res.append({"workload": name_moe_decode(m, T, active),
                     "kernel": "k_grouped_gemv (no routing pass)", "value": round(gbs, 1), "unit": "GB/s",
                     "mean_call_us": round(mean * 1e3, 2),
                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
@@ -654,7 +675,7 @@ def cpu_baseline(W, step_bytes, seconds):
                       "one thread" % (n, per)}
 
 
-def cpu_oracle_lines(W):
+def cpu_oracle_lines(W, time_scale=1.0):
     """The CPU oracle (plain C, threads over output rows) timed on each secondary
     configuration, in the unit of that configuration's GPU line where the
     sample allows it.  Large GEMMs are timed on a sample of their activation
@@ -679,9 +700,9 @@ def cpu_oracle_lines(W):
     def small(nt):
         qa, da = oracle.quantize_q8_0(x)
         oracle.qgemm_q8_0(qa, da, qw, dw, nthreads=nt)
-    per, n = _timed(lambda: small(threads), 1.0)
-    per1, n1 = _timed(lambda: small(1), 1.0)
-    out["small Q8_0 GEMM M=%d K=%d N=%d" % (s.m, s.k, s.n)] = rec(
+    per, n = _timed(lambda: small(threads), 1.0 * time_scale)
+    per1, n1 = _timed(lambda: small(1), 1.0 * time_scale)
+    out[name_small(s)] = rec(
         round(per * 1e6, 2), "us per call (quantize + GEMM)", "%d whole calls" % n, s.m,
         single_thread={"value": round(per1 * 1e6, 2), "unit": "us per call",
                        "sample": "%d whole calls on 1 thread" % n1})
@@ -695,10 +716,10 @@ def cpu_oracle_lines(W):
         def dstep():
             qa, da = oracle.quantize_q8_0(x)
             oracle.qgemm_q8_0(qa, da, qw, dw, nthreads=threads)
-        per, n = _timed(dstep, 2.0)
+        per, n = _timed(dstep, 2.0 * time_scale)
         a_bytes = sd.m * sd.k + sd.m * (sd.k // 32) * 2
         byt = sd.n * sd.k + sd.n * (sd.k // 32) * 2 + a_bytes + sd.m * sd.n * 4 + sd.m * sd.k * 4 + a_bytes
-        out["decode M=%d K=%d N=%d" % (sd.m, sd.k, sd.n)] = rec(
+        out[name_decode(sd)] = rec(
             round(byt / per / 1e9, 3), "GB/s", "%d whole steps, %.4f s each" % (n, per), sd.m)
     del qw, dw
 
@@ -713,9 +734,9 @@ def cpu_oracle_lines(W):
         def gstep():
             qa, da = oracle.quantize_q8_0(x)
             oracle.qgemm_q8_0(qa, da, qw, dw, nthreads=threads)
-        per, n = _timed(gstep, 1.5)
+        per, n = _timed(gstep, 1.5 * time_scale)
         tops = 2.0 * rows * shape.n * shape.k / per / 1e12
-        out["%s GEMM M=%d K=%d N=%d" % (name, shape.m, shape.k, shape.n)] = rec(
+        out[name_gemm(name, shape)] = rec(
             round(tops, 5), "int8-equiv TOPS",
             "%d of %d activation rows against all %d weight rows (quantize + GEMM), %d runs of "
             "%.3f s; the whole GEMM would take about %.1f s" % (rows, shape.m, shape.n, n, per,
@@ -728,8 +749,9 @@ def cpu_oracle_lines(W):
     ids = W.topk_ids(m.tokens, m.top_k, m.experts)
     tok = 96
     qa, da = oracle.quantize_q8_0(W.activations("moe", tok, m.k))
-    per, n = _timed(lambda: oracle.qgemm_w4a8_grouped(qa, da, ids[:tok], wq4, wd, nthreads=threads), 1.5)
-    out["grouped W4A8 T=%d top-%d E=%d K=%d N=%d" % (m.tokens, m.top_k, m.experts, m.k, m.n)] = rec(
+    per, n = _timed(lambda: oracle.qgemm_w4a8_grouped(qa, da, ids[:tok], wq4, wd, nthreads=threads),
+                    1.5 * time_scale)
+    out[name_moe(m)] = rec(
         round(2.0 * tok * m.top_k * m.n * m.k / per / 1e12, 5), "int8-equiv TOPS",
         "%d of %d tokens (%d routed rows), %d runs of %.3f s; the whole call would take about "
         "%.1f s" % (tok, m.tokens, tok * m.top_k, n, per, per * m.tokens / tok), tok * m.top_k)
@@ -738,13 +760,13 @@ def cpu_oracle_lines(W):
     for T in (1, 4, 16):
         ids_t = W.topk_ids(T, m.top_k, m.experts, seed=T)
         qa, da = oracle.quantize_q8_0(W.activations("moe", T, m.k, seed=T))
-        per, n = _timed(lambda: oracle.qgemm_w4a8_grouped(qa, da, ids_t, wq4, wd, nthreads=threads), 0.5)
+        per, n = _timed(lambda: oracle.qgemm_w4a8_grouped(qa, da, ids_t, wq4, wd, nthreads=threads),
+                        0.5 * time_scale)
         active = len(np.unique(ids_t))
         R = T * m.top_k
         byt = (active * m.n * (m.k // 2 + m.k // 32 * 2) + T * (m.k + m.k // 32 * 2)
                + R * 4 + R * m.n * 4)
-        out["grouped W4A8 decode T=%d top-%d E=%d K=%d N=%d (%d active experts)"
-            % (T, m.top_k, m.experts, m.k, m.n, active)] = rec(
+        out[name_moe_decode(m, T, active)] = rec(
             round(byt / per / 1e9, 3), "GB/s", "%d whole calls, %.4f s each" % (n, per), R)
     del wq4, wd
     return out
