@@ -17,8 +17,9 @@
 // Scale epilogue (per 32x32 tile and block), two fp32 FMAs per output:
 //   the MFMA accumulator is seeded with the bit pattern of 1.5*2^23, so its
 //   int32 result reads as the fp32 value F = 1.5*2^23 + P exactly;
-//   t   = fma(F, dw, -1.5*2^23*dw)  = round(dw * P)   (dw is lane-uniform)
-//   acc = fma(t, da, acc)                               (da per register)
+//   t   = fma(F, dw, -1.5*2^23*dw)  = round(dw * P)   (dw: the lane's column,
+//                                                       one for all its outputs)
+//   acc = fma(t, da, acc)                               (da: per register row)
 // -1.5*2^23*dw is exact in fp32, so every term carries one rounding before
 // it joins the fp32 sum, and the result stays within
 // (nb + 1) * 2^-24 * sum|terms| of the exact value (nb = k/32).  Both FMAs
