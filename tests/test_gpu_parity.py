@@ -205,6 +205,36 @@ def test_qgemm_random_codes_full_range(m, k, n):
     assert_within_bound(y, yr, asum, k // 32, "m=%d k=%d n=%d" % (m, k, n))
 
 
+def seeded_shapes(count, seed=20261202):
+    """Random (m, k, n) spread over every dispatch path: 1-4 rows (v_dot4),
+    5-16 (thin-M MFMA), 17-300 (MFMA GEMM), k a multiple of 32 up to 8192,
+    n up to 3000; m * n * k capped so the oracle stays quick."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        band = len(out) % 3
+        m = int(g.integers(1, 5) if band == 0 else g.integers(5, 17) if band == 1 else g.integers(17, 301))
+        k = 32 * int(g.integers(1, 257))
+        n = int(g.integers(1, 3001))
+        if m * n * k <= 150_000_000:
+            out.append((m, k, n))
+    return out
+
+
+@pytest.mark.parametrize("m,k,n", seeded_shapes(24))
+def test_qgemm_seeded_shape_sweep(m, k, n):
+    """Seeded random shapes through every path of qgemm_q8_0, full-range codes
+    and normal-range scales, against the oracle."""
+    log("qgemm sweep m=%d k=%d n=%d" % (m, k, n))
+    aq = W.random_int8(0, 900 + m, (m, k), seed=n)
+    wq = W.random_int8(0, 901, (n, k), seed=n + k)
+    ad = W.random_scales(0, 902, (m, k // 32), seed=m + n)
+    wd = W.random_scales(0, 903, (n, k // 32), seed=k)
+    y = run_gemm(aq, ad, wq, wd)
+    yr, asum = oracle.qgemm_q8_0(aq, ad, wq, wd, nthreads=oracle_threads())
+    assert_within_bound(y, yr, asum, k // 32, "sweep m=%d k=%d n=%d" % (m, k, n))
+
+
 @pytest.mark.parametrize("m,n", [
     (1, 96), (2, 96), (3, 96), (4, 96),   # k_gemv_reg, one to four rows
     (4, 12288),                           # k_gemv_reg at the decode width
