@@ -638,6 +638,42 @@ def test_grouped_w4a8_chunk_tails(counts):
     assert_within_bound(y, yr, asum, K // 32, "chunk tails %s" % (counts,))
 
 
+def seeded_grouped_cases(count, seed=20261203):
+    """Random (T, top_k, E, K, N): routed rows from a few (the v_dot4 GEMV)
+    to a few thousand (the MFMA kernel, one or several chunks per expert),
+    up to 300 experts (past 256 the GEMM takes them in index order)."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        top_k = int(g.integers(1, 9))
+        T = int(g.integers(1, 600))
+        E = int(g.integers(max(top_k, 2), 301))
+        K = 32 * int(g.integers(1, 81))
+        N = int(g.integers(1, 400))
+        if T * top_k * N * K <= 200_000_000:
+            out.append((T, top_k, E, K, N))
+    return out
+
+
+@pytest.mark.parametrize("T,top_k,E,K,N", seeded_grouped_cases(12))
+def test_grouped_w4a8_seeded_sweep(T, top_k, E, K, N):
+    """Seeded random problems through every grouped path, with a few invalid
+    ids (zero rows), against the oracle."""
+    log("grouped sweep T=%d top_k=%d E=%d K=%d N=%d" % (T, top_k, E, K, N))
+    g = np.random.default_rng(T * 1000 + E)
+    ids = W.topk_ids(T, top_k, E, seed=T + K)
+    bad_rows = g.integers(0, T, size=min(3, T))
+    ids[bad_rows, 0] = -1
+    qa = W.random_int8("moe", 711, (T, K), seed=T + N)
+    da = W.random_scales("moe", 712, (T, K // 32), seed=T + N)
+    packed = g.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    wsc = W.random_scales("moe", 713, (E, N, K // 32), seed=E + K)
+    y = run_grouped(qa, da, ids, packed, wsc)
+    yr, asum = oracle.qgemm_w4a8_grouped(qa, da, ids, packed, wsc, nthreads=oracle_threads())
+    assert_within_bound(y, yr, asum, K // 32, "grouped sweep T=%d E=%d" % (T, E))
+    assert (y[ids < 0] == 0).all()
+
+
 def test_grouped_w4a8_beyond_one_routing_chunk():
     """2048 tokens x top-8 of 128 experts: 16384 routed rows, more than the
     8192 that the routing pass holds in registers, so it counts and places
