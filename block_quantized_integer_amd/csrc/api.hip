@@ -27,16 +27,17 @@ hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t counts, offsets, order, rows, total;
+  size_t counts, offsets, rows, total;
 };
 
+// counts [E], offsets [E+1] and rows [rows_total] (int32), each section
+// 256-byte aligned
 WsLayout ws_layout(int64_t rows_total, int64_t n_experts, int64_t k) {
   (void)k;
   WsLayout L;
   L.counts = 0;
   L.offsets = round256((size_t)n_experts * 4);
-  L.order = L.offsets + round256((size_t)(n_experts + 1) * 4);
-  L.rows = L.order + round256((size_t)n_experts * 4);
+  L.rows = L.offsets + round256((size_t)(n_experts + 1) * 4);
   L.total = L.rows + round256((size_t)rows_total * 4);
   return L;
 }
@@ -136,12 +137,11 @@ int grouped_impl(const int8_t *aq, const uint16_t *ad, int64_t n_tokens,
   int32_t *counts = reinterpret_cast<int32_t *>(ws + L.counts);
   int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
   int32_t *rows = reinterpret_cast<int32_t *>(ws + L.rows);
-  int32_t *order = reinterpret_cast<int32_t *>(ws + L.order);
-  hipError_t e = bqi::launch_route_topk(topk_ids, rows_total, n_experts, top_k,
-                                        counts, offsets, rows, order, y, n, s);
+  hipError_t e = bqi::launch_route_topk(topk_ids, rows_total, n_experts, top_k, counts,
+                                        offsets, rows, y, n, s);
   if (e != hipSuccess) return BQI_EHIP;
-  return hip_status(bqi::launch_grouped_w4a8(aq, ad, top_k, wq4, wd, n_experts,
-                                             n, k, counts, offsets, rows, order, y, s));
+  return hip_status(bqi::launch_grouped_w4a8(aq, ad, top_k, wq4, wd, n_experts, n, k,
+                                             rows_total, counts, offsets, rows, y, s));
 }
 
 }  // namespace
@@ -251,7 +251,7 @@ int route_topk(const int32_t *topk_ids, int64_t n_tokens, int64_t top_k,
     return BQI_EALIGN;
   return hip_status(bqi::launch_route_topk(topk_ids, n_tokens * top_k,
                                            n_experts, top_k, counts, offsets,
-                                           rows, nullptr, nullptr, 0, as_stream(stream)));
+                                           rows, nullptr, 0, as_stream(stream)));
 }
 
 size_t qgemm_w4a8_grouped_workspace_size(int64_t n_tokens, int64_t top_k,

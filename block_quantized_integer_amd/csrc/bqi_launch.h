@@ -48,23 +48,20 @@ hipError_t launch_gemm_mfma(const int8_t *aq, const uint16_t *ad, int64_t m,
                             int64_t k, float *y, hipStream_t stream);
 
 // routing (counting sort by expert); y != nullptr also zeroes the output
-// rows of invalid ids ([rows_total][n] floats); order != nullptr (and at most
-// 256 experts) also gives the experts by descending routed-row count, ties by
-// index: order[rank] = expert
+// rows of invalid ids ([rows_total][n] floats)
 hipError_t launch_route_topk(const int32_t *ids, int64_t rows_total,
                              int64_t n_experts, int64_t top_k, int32_t *counts,
-                             int32_t *offsets, int32_t *rows, int32_t *order,
-                             float *y, int64_t n, hipStream_t stream);
+                             int32_t *offsets, int32_t *rows, float *y, int64_t n,
+                             hipStream_t stream);
 
-// grouped W4A8 GEMM reading a routing produced by launch_route_topk, with its
-// order for up to 256 experts (ad: the fp16 activation scales
-// [n_tokens][k/32]); needs n * k/2 < 2^31
+// grouped W4A8 GEMM reading a routing produced by launch_route_topk (ad: the
+// fp16 activation scales [n_tokens][k/32]); needs n * k/2 < 2^31
 hipError_t launch_grouped_w4a8(const int8_t *aq, const uint16_t *ad,
                                int64_t top_k, const uint8_t *wq4,
                                const uint16_t *wd, int64_t n_experts, int64_t n,
-                               int64_t k, const int32_t *counts,
-                               const int32_t *offsets, const int32_t *rows,
-                               const int32_t *order, float *y, hipStream_t stream);
+                               int64_t k, int64_t rows_total, const int32_t *counts,
+                               const int32_t *offsets, const int32_t *rows, float *y,
+                               hipStream_t stream);
 
 // grouped W4A8 for a few routed rows (decode): v_dot4 GEMV per routed row,
 // no routing pass

@@ -12,17 +12,20 @@
 // matches, so rows come out in increasing row order.  Up to 8192 routed rows
 // this is a single pass over ids held in registers; beyond, a counting pass
 // and a placing pass run chunk by chunk.  Deterministic.  The same pass
-// writes zeros to the output rows of invalid ids and, for up to 256 experts,
-// the experts in dispatch order (descending routed-row count, ties by index).
+// writes zeros to the output rows of invalid ids.
 //
 // GEMM (k_grouped_w4a8): one workgroup of 4 waves per (expert, 128-column
-// tile), three per CU, heaviest expert first; the weights are the MFMA's A
-// operand and the gathered activation rows its B operand (details below).
+// tile), three per CU, for an expert's first 64 routed rows; its further rows
+// (up to 256 experts) go in 16-row pieces to more workgroups, which split K
+// over their waves.  The weights are the MFMA's A operand and the gathered
+// activation rows its B operand (details below).
 // The products run on v_mfma_i32_32x32x32_i8 (one instruction = one 32x32
 // tile for exactly one group).  Per group a lane unpacks its 16 codes (low or
 // high nibbles by lane half) into the int8 values 16*(c - 8) with a shift, a
 // mask and an xor; the factor 16 is folded into the weight scale.  The scale
 // epilogue is the one of the Q8_0 MFMA GEMM (one rounding per term).
+#include <algorithm>
+
 #include "bqi_device.h"
 #include "bqi_launch.h"
 
@@ -59,40 +62,23 @@ __device__ __forceinline__ int route_scan(int v, int *s_tmp, int &total) {
   return wave_base + incl - v;
 }
 
-// The dispatch order of the grouped GEMM (order != nullptr, n_experts <=
-// ROUTE_RANK_MAX): every workgroup also counts all experts' routed rows into
-// LDS, takes its expert's rank by descending count (ties by index) as one
-// workgroup sum of comparisons, and writes order[rank] = e.
-constexpr int ROUTE_RANK_MAX = 256;
+// Rows of an expert that its own GEMM workgroups take; the rest go to the
+// split pieces of SPLIT_ROWS rows (see the grouped GEMM below).
+constexpr int SPLIT_FIRST = 64;
+constexpr int SPLIT_ROWS = 16;
+constexpr int SPLIT_MAX_EXPERTS = 256;  // up to 4 experts per lane of one wave
 
-__device__ __forceinline__ void route_rank(int e, int n_experts, const int *s_hist,
-                                           int *s_tmp, int32_t *order) {
-  const int tid = threadIdx.x;
-  const int c = s_hist[e];
-  int flag = 0;
-  if (tid < n_experts) {
-    const int cj = s_hist[tid];
-    flag = (cj > c) || (cj == c && tid < e);
-  }
-  int rank;
-  (void)route_scan(flag, s_tmp, rank);
-  if (tid == 0) order[rank] = e;
+__device__ __forceinline__ int split_pieces(int cnt) {
+  return cnt > SPLIT_FIRST ? (cnt - SPLIT_FIRST + SPLIT_ROWS - 1) / SPLIT_ROWS : 0;
 }
 
 __global__ __launch_bounds__(RT) void k_route(
     const int32_t *__restrict__ ids, int rows_total, int n_experts, int top_k,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ rows, int32_t *__restrict__ order, float *__restrict__ y,
-    int n) {
+    int32_t *__restrict__ rows, float *__restrict__ y, int n) {
   __shared__ int s_tmp[RT / 64];
-  __shared__ int s_hist[ROUTE_RANK_MAX];
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
-  const bool rank = order != nullptr && n_experts <= ROUTE_RANK_MAX;
-  if (rank) {
-    if (tid < ROUTE_RANK_MAX) s_hist[tid] = 0;
-    __syncthreads();
-  }
 
   if (rows_total <= RCHUNK) {
     // one pass: each thread keeps its 8 ids in registers; one workgroup scan
@@ -107,12 +93,9 @@ __global__ __launch_bounds__(RT) void k_route(
       v[j] = r0 + j < rows_total ? ids[r0 + j] : -1;
       below += (v[j] >= 0 && v[j] < e);
       eq += (v[j] == e);
-      if (rank && v[j] >= 0 && v[j] < n_experts) atomicAdd(&s_hist[v[j]], 1);
     }
     int total;
-    const int excl = route_scan((below << 16) | eq, s_tmp, total);  // its barriers
-                                                                    // also publish s_hist
-    if (rank) route_rank(e, n_experts, s_hist, s_tmp, order);
+    const int excl = route_scan((below << 16) | eq, s_tmp, total);
     const int n_below = total >> 16, n_eq = total & 0xffff;
     if (tid == 0) {
       counts[e] = n_eq;
@@ -146,13 +129,11 @@ __global__ __launch_bounds__(RT) void k_route(
       const int v = r < rows_total ? ids[r] : -1;
       below += (v >= 0 && v < e);
       eq += (v == e);
-      if (rank && v >= 0 && v < n_experts) atomicAdd(&s_hist[v], 1);
     }
   }
   int n_below, n_eq;
   (void)route_scan(below, s_tmp, n_below);
   (void)route_scan(eq, s_tmp, n_eq);
-  if (rank) route_rank(e, n_experts, s_hist, s_tmp, order);
   if (tid == 0) {
     counts[e] = n_eq;
     offsets[e] = n_below;
@@ -197,16 +178,22 @@ __global__ __launch_bounds__(RT) void k_route(
 // routed row), so in the output a lane holds one routed row and its registers
 // hold 16 columns: the activation scale is lane-uniform (one per row tile and
 // group) and the weight scales, one per register, are shared by every row
-// tile of the wave.  Routed rows are taken 64 at a time (two 32-row tiles);
-// an expert with more rows streams its weights again for the next 64 (mostly
-// from the Infinity Cache, which holds all the experts' weights).
+// tile of the wave.  Routed rows are taken 64 at a time (two 32-row tiles).
 //
 // Three workgroups share a CU (12 waves, 168 VGPRs each), so the MoE
-// workload's 768 (expert, column tile) units run in one round.  Workgroups
-// are dispatched heaviest expert first: workgroup blockIdx takes the expert
-// of rank blockIdx / column_tiles in the routing pass's order (descending
-// routed-row count, ties by index), which spreads the experts of more than
-// 64 rows (two chunks) over different CUs.
+// workload's 768 (expert, column tile) units run in one round.  Workgroup
+// blockIdx takes expert blockIdx / column_tiles and, up to 256 experts, only
+// its first 64 routed rows.  The rows past them form pieces of 16 rows; each
+// 32-column strip of a piece is an item for the workgroups launched after
+// the (expert, column tile) ones, which start as those finish.  An item's
+// four waves take one quarter of K each over the same 16 rows and 32 columns
+// and add their partial sums through LDS in wave order, so a heavy expert's
+// extra rows are spread over many CUs instead of running after its first 64
+// on the same workgroups.  (Ordering the experts by routed-row count made no
+// difference once no workgroup takes more than 64 rows.)  Past 256 experts a
+// workgroup takes all its expert's rows, 64 at a time; an expert with more
+// rows streams its weights again for the next 64 (mostly from the Infinity
+// Cache).
 //
 // Stages of GNB = 4 groups (128 K elements) go through two LDS buffers: the
 // loads of stage s+1 are issued before the compute of stage s.  Per stage
@@ -238,6 +225,8 @@ constexpr int G_WS_LOADS = GBN * GNB / 64 / GW;    // weight-scale slots per thr
 static_assert(G_W_LOADS == 2 && G_WS_LOADS == 2, "load mapping");
 static_assert(g_a_loads<GRT>() == GRT && g_as_loads<GRT>() * GT / GNB <= G_AS_ROWS, "load mapping");
 static_assert(G_AS_ROWS >= GCH, "activation-scale slots cover the chunk");
+static_assert(SPLIT_FIRST == GCH && 4 * SPLIT_ROWS == GCH,
+              "an expert's own workgroups take one chunk; a split piece stages four quarters of 16 rows");
 
 struct GBuf {
   uint8_t w[GBN * GNB * 16];    // packed weights: [column][slot], slot = group ^ wswz(column)
@@ -386,16 +375,19 @@ __device__ __forceinline__ int64_t unpack_w4x8(int64_t p, int shl) {
   return (int64_t)((uint64_t)lo | ((uint64_t)hi << 32));
 }
 
-__device__ __forceinline__ void grouped_stage_half(const GBuf &B, int wave, int lane_in,
+// arow0 (a multiple of 16): the first of the 16 staged rows that the wave
+// reads.
+__device__ __forceinline__ void grouped_stage_half(const GBuf &B, int wave, int lane_in, int arow0,
                                                    const i32x4 &seed4, f32x4 (&acc)[2]) {
   int lane = lane_in;
   asm volatile("" : "+v"(lane));
   const int l16 = lane & 15, kg = lane >> 4;
   const int shl = (kg >> 1) ? 0 : 4;
-  const int aswz_l = (l16 >> 1) & 7;  // aswz of row l16
+  const int aswz_l = (l16 >> 1) & 7;  // aswz of row arow0 + l16
+  const int arow = arow0 + l16;
   float da[GNB];
   {
-    const i32x4 v = *reinterpret_cast<const i32x4 *>(&B.as[l16 * GNB]);
+    const i32x4 v = *reinterpret_cast<const i32x4 *>(&B.as[arow * GNB]);
     da[0] = half_bits_to_float((uint16_t)v.x);
     da[1] = half_bits_to_float((uint16_t)v.y);
     da[2] = half_bits_to_float((uint16_t)v.z);
@@ -408,7 +400,7 @@ __device__ __forceinline__ void grouped_stage_half(const GBuf &B, int wave, int 
   };
   auto read_b = [&](int g) {
     return *reinterpret_cast<const int64_t *>(
-        &B.a[l16 * GBK + 16 * ((2 * g + (kg >> 1)) ^ aswz_l) + 8 * (kg & 1)]);
+        &B.a[arow * GBK + 16 * ((2 * g + (kg >> 1)) ^ aswz_l) + 8 * (kg & 1)]);
   };
 #pragma unroll
   for (int g = 0; g < GNB; ++g) {
@@ -436,18 +428,36 @@ struct GArgs {
   float *y;
 };
 
-// One chunk of up to 32*R routed rows of expert e against the workgroup's 128
-// columns: the whole K pipeline, then the stores.
-// HALF: at most 16 rows, computed on 16-row tiles (R == 1).
-template <int R, bool HALF = false>
+// The work shapes of grouped_chunk.
+enum GMode {
+  G_FULL = 0,   // up to 32 R rows x the workgroup's 128 columns, 32-row tiles
+  G_HALF = 1,   // up to 16 rows x 128 columns, 16-row tiles (R == 1)
+  G_SPLIT = 2,  // up to 16 rows x 32 columns, K split four ways over the waves
+};
+
+// One chunk of routed rows of expert e from column n0 on: the whole K
+// pipeline, then the stores.
+//
+// G_SPLIT: every wave computes the same 32 columns and 16 rows over its own
+// quarter of K (qg groups, a multiple of GNB, from group qg * wave on) on
+// 16-row tiles.  The stage buffers keep their layout: wave w's 32 columns
+// (columns 32w .. 32w+31 of the buffer) and staged rows 16w .. 16w+15 hold
+// the workgroup's columns and rows over quarter w, so each wave loads exactly
+// what it reads.  The four partial sums are added through LDS in wave order.
+template <int R, int MODE>
 __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], const int *s_tok,
                                               const int *s_row, int e, int n0, int crows) {
-  static_assert(!HALF || R == 1, "16-row tiles stage one 32-row tile's loads");
+  constexpr bool HALF = MODE != G_FULL;   // 16-row tiles
+  constexpr bool SPLIT = MODE == G_SPLIT;
+  static_assert(MODE == G_FULL || (MODE == G_HALF && R == 1) || (SPLIT && R == 2),
+                "16-row tiles stage one 32-row tile's loads, split chunks four 16-row quarters");
   const int n = A.n, k = A.k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int nbk = k / QK;
-  const int stages = (nbk + GNB - 1) / GNB;
+  const int qg = SPLIT ? GNB * ((nbk + 4 * GNB - 1) / (4 * GNB)) : 0;
+  const int gq0 = qg * wave_u;  // first group of the wave's loads and reads
+  const int stages = SPLIT ? qg / GNB : (nbk + GNB - 1) / GNB;
   const int kh = k / 2;
 
   i32x16 seed;
@@ -459,13 +469,15 @@ __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], co
 
   // per-lane load coordinates, fixed for the chunk
   // weights: chunk e = 64 (2w + q) + L -> column e/4, slot e%4 (group slot ^ wswz)
+  // (split: the wave's buffer columns 32w.. are the workgroup's columns over
+  // its quarter of K)
   int w_off[G_W_LOADS], w_g[G_W_LOADS];
 #pragma unroll
   for (int q = 0; q < G_W_LOADS; ++q) {
     const int ce = 64 * (G_W_LOADS * wave + q) + lane;
     const int c = ce >> 2;
     w_g[q] = (ce & 3) ^ ((c >> 2) & 3);
-    w_off[q] = min(n0 + c, n - 1) * kh;
+    w_off[q] = min(n0 + (SPLIT ? (c & 31) : c), n - 1) * kh + 16 * gq0;
   }
   // activations: chunk e = 64 (3w + q) + L -> row e/8, slot e%8 (chunk slot
   // ^ aswz); 32-bit offsets from the activation base (the ABI layer
@@ -476,7 +488,7 @@ __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], co
   for (int q = 0; q < NA; ++q) {
     const int ce = 64 * (NA * wave + q) + lane;
     const int r = ce >> 3;
-    a_c[q] = 16 * ((ce & 7) ^ ((r >> 1) & 7));
+    a_c[q] = 16 * ((ce & 7) ^ ((r >> 1) & 7)) + 32 * gq0;  // split: rows 16w.. of quarter w
     a_row[q] = s_tok[r] * k;
   }
   // activation scales: slot e = 64 (2w + q) + L -> row e/4 (clamped to the
@@ -485,15 +497,18 @@ __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], co
 #pragma unroll
   for (int q = 0; q < NAS; ++q) {
     const int ce = 64 * (NAS * wave + q) + lane;
-    as_row[q] = s_tok[min(ce >> 2, GCH - 1)] * nbk + (ce & 3);
+    as_row[q] = s_tok[min(ce >> 2, GCH - 1)] * nbk + (ce & 3) + gq0;
   }
   // weight scales: slot e = 64 (2w + q) + L -> group e/128 (= w), column
-  // e%128; element offsets from the expert's scale base
-  int ws_off[G_WS_LOADS];
+  // e%128; element offsets from the expert's scale base (split: buffer column
+  // c is column c%32 over quarter c/32, which differs between lanes)
+  int ws_off[G_WS_LOADS], ws_q0[G_WS_LOADS];
 #pragma unroll
   for (int q = 0; q < G_WS_LOADS; ++q) {
     const int ce = 64 * (G_WS_LOADS * wave + q) + lane;
-    ws_off[q] = min(n0 + (ce & (GBN - 1)), n - 1) * nbk + (ce >> 7);
+    const int c = ce & (GBN - 1);
+    ws_q0[q] = SPLIT ? qg * (c >> 5) : 0;
+    ws_off[q] = min(n0 + (SPLIT ? (c & 31) : c), n - 1) * nbk + (ce >> 7) + ws_q0[q];
   }
   const uint8_t *wq_e = A.wq4 + (int64_t)e * n * kh;
   const uint16_t *wd_e = A.wd + (int64_t)e * n * nbk;
@@ -502,12 +517,12 @@ __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], co
   // last group (their scales become 0).
   auto issue = [&](int s) {
     const int g0 = s * GNB;
-    const bool full = g0 + GNB <= nbk;  // uniform
+    const bool full = gq0 + g0 + GNB <= nbk;  // uniform in the wave
     GBuf &D = S[s % GNS];
     const uint8_t *wbase = wq_e + 16 * g0;
 #pragma unroll
     for (int q = 0; q < G_W_LOADS; ++q) {
-      const int off = w_off[q] + 16 * (full ? w_g[q] : min(w_g[q], nbk - 1 - g0));
+      const int off = w_off[q] + 16 * (full ? w_g[q] : min(w_g[q], nbk - 1 - g0 - gq0));
       const uint32_t lds = lds_addr(&D.w[1024 * (G_W_LOADS * wave_u + q)]);
       asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(wbase), "{m0}"(lds) : "memory");
     }
@@ -522,7 +537,7 @@ __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], co
 #pragma unroll
     for (int q = 0; q < NAS; ++q) {
       const int ce = 64 * (NAS * wave + q) + lane;
-      const int off = as_row[q] + (full ? 0 : min(0, nbk - 1 - g0 - (ce & 3)));
+      const int off = as_row[q] + (full ? 0 : min(0, nbk - 1 - g0 - (ce & 3) - gq0));
       const uint32_t lds = lds_addr(&D.as[64 * (NAS * wave_u + q)]);
       asm volatile("s_nop 0\n\tglobal_load_lds_ushort %0, %1" :: "v"(2 * off), "s"(asbase), "{m0}"(lds) : "memory");
     }
@@ -530,7 +545,7 @@ __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], co
 #pragma unroll
     for (int q = 0; q < G_WS_LOADS; ++q) {
       const int gq = wave_u;  // group of this wave's slots
-      const int off = ws_off[q] + (full ? 0 : min(0, nbk - 1 - g0 - gq));
+      const int off = ws_off[q] + (full && !SPLIT ? 0 : min(0, nbk - 1 - g0 - gq - ws_q0[q]));
       const uint32_t lds = lds_addr(&D.ws[0][0] + 64 * (G_WS_LOADS * wave_u + q));
       asm volatile("s_nop 0\n\tglobal_load_lds_ushort %0, %1" :: "v"(2 * off), "s"(wsbase), "{m0}"(lds) : "memory");
     }
@@ -545,7 +560,7 @@ __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], co
     for (int i = 0; i < 2; ++i) {
       const int g = 2 * (lane >> 5) + i;
       const uint32_t bits = D.ws[g][c];
-      const float v = s * GNB + g < nbk ? half_bits_to_float((uint16_t)bits) * 0.0625f : 0.0f;  // exact
+      const float v = gq0 + s * GNB + g < nbk ? half_bits_to_float((uint16_t)bits) * 0.0625f : 0.0f;  // exact
       D.ws[g][c] = __builtin_bit_cast(uint32_t, v);
     }
   };
@@ -572,11 +587,39 @@ __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], co
     if (s + 1 < stages) issue(s + 1);
     convert_ws(s);
     if constexpr (HALF)
-      grouped_stage_half(S[s % GNS], wave, lane, seed4, acc16);
+      grouped_stage_half(S[s % GNS], wave, lane, SPLIT ? 16 * wave : 0, seed4, acc16);
     else
       grouped_stage<R>(S[s % GNS], wave, lane, seed, acc);
   }
 
+  if constexpr (SPLIT) {
+    // the four quarters' partial sums, added in wave order: wave w finishes
+    // outputs 2w, 2w+1 of the lane's eight (columns 16 (w/2) + 4 (L/16) +
+    // 2 (w%2) + 0..1, row L%16)
+    __syncthreads();  // every wave is done with the stage buffers
+    f32x4 *red = reinterpret_cast<f32x4 *>(&S[0]);  // [wave][lane][2]
+    red[(wave * 64 + lane) * 2 + 0] = acc16[0];
+    red[(wave * 64 + lane) * 2 + 1] = acc16[1];
+    __syncthreads();
+    const float *redf = reinterpret_cast<const float *>(&S[0]);
+    const int i0 = 2 * wave;
+    float v[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float sum = redf[lane * 8 + i0 + i];
+#pragma unroll
+      for (int w = 1; w < GW; ++w) sum += redf[(w * 64 + lane) * 8 + i0 + i];
+      v[i] = sum;
+    }
+    const int rr = lane & 15;
+    if (rr < crows) {
+      float *yrow = A.y + (int64_t)s_row[rr] * n;
+      const int c = n0 + 16 * (wave >> 1) + 4 * (lane >> 4) + 2 * (wave & 1);
+      if (c < n) yrow[c] = v[0];
+      if (c + 1 < n) yrow[c + 1] = v[1];
+    }
+    return;
+  }
   const bool vec = (n & 3) == 0 && ((uintptr_t)A.y & 15) == 0;
   if constexpr (HALF) {
     // store: lane's routed row L%16, columns n0 + 32 wave + 16 ct + 4 (L/16) + (0..3)
@@ -625,31 +668,107 @@ __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], co
   }
 }
 
+// Inclusive sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
 __global__ __launch_bounds__(GT, 3) void k_grouped_w4a8(
     const int8_t *__restrict__ aq, const uint16_t *__restrict__ ad, int top_k,
     const uint8_t *__restrict__ wq4, const uint16_t *__restrict__ wd,
     int n_experts, int n, int k, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ rows,
-    const int32_t *__restrict__ order, float *__restrict__ y) {
+    float *__restrict__ y) {
   __shared__ __attribute__((aligned(16))) GBuf S[GNS];
   __shared__ int s_tok[GCH];  // token of each staged row
   __shared__ int s_row[GCH];  // routed row (output row) of each staged row
 
   const int tiles_n = (n + GBN - 1) / GBN;
-  const int unit = blockIdx.x / tiles_n;
-  const int tn = blockIdx.x - unit * tiles_n;
+  const int main_wgs = n_experts * tiles_n;
   const int tid = threadIdx.x;
-  // the expert of rank `unit` by descending routed-row count, as the routing
-  // pass ordered them (natural order past its ranking limit)
-  const int e = n_experts <= ROUTE_RANK_MAX ? order[unit] : unit;
+  const GArgs A{aq, ad, top_k, wq4, wd, n, k, y};
+  const bool split = n_experts <= SPLIT_MAX_EXPERTS;
+
+  if ((int)blockIdx.x >= main_wgs) {
+    // The split pieces, numbered expert by expert: expert e's pieces follow
+    // those of the experts below it.  Every wave finds them from the routed-row
+    // counts alone: lane l holds experts 4l .. 4l+3, and two wave sums give,
+    // per lane, the pieces and the rows of the experts up to its own.  Item t
+    // is 32-column strip t % strips of piece t / strips; the workgroups past
+    // the (expert, column tile) ones take items blockIdx - main_wgs, then
+    // every gridDim - main_wgs further.
+    const int lane = tid & 63;
+    int c4[4], rsum = 0, psum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ex = 4 * lane + j;
+      c4[j] = ex < n_experts ? counts[ex] : 0;
+      rsum += c4[j];
+      psum += split_pieces(c4[j]);
+    }
+    const int rinc = wave_inclusive_sum(rsum), pinc = wave_inclusive_sum(psum);
+    const int strips = (n + 31) / 32;
+    const int step = (int)gridDim.x - main_wgs;
+    const int64_t items = (int64_t)__builtin_amdgcn_readlane(pinc, 63) * strips;
+    for (int64_t t = (int)blockIdx.x - main_wgs; t < items; t += step) {
+      const int piece = (int)(t / strips);
+      const int strip = (int)(t - (int64_t)piece * strips);
+      // the lane holding the piece's expert: the first whose running piece
+      // count passes it (one exists, as piece < the wave's total)
+      const int src = __builtin_ctzll(__ballot(pinc > piece));
+      int pbase = __builtin_amdgcn_readlane(pinc - psum, src);
+      int rbase = __builtin_amdgcn_readlane(rinc - rsum, src);
+      int e = 4 * src, c = 0, i = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int cj = __builtin_amdgcn_readlane(c4[j], src);
+        const int pj = split_pieces(cj);
+        if (c == 0 && piece < pbase + pj) {
+          e = 4 * src + j;
+          c = cj;
+          i = piece - pbase;
+        } else if (c == 0) {
+          pbase += pj;
+          rbase += cj;
+        }
+      }
+      // rows of expert e start at rbase (the routed rows of the experts below
+      // it); the piece is rows c0 .. c0 + crows - 1 of the expert
+      const int c0 = SPLIT_FIRST + SPLIT_ROWS * i;
+      const int crows = min(SPLIT_ROWS, c - c0);
+      const int r0 = rbase + c0;
+      // the previous item is done with s_tok, s_row and S
+      __syncthreads();
+      if (tid < GCH) {
+        // staged row r is row r % 16 of the piece (for K quarter r / 16)
+        const int rr = rows[r0 + min(tid & (SPLIT_ROWS - 1), crows - 1)];
+        s_row[tid] = rr;
+        s_tok[tid] = rr / top_k;
+      }
+      __syncthreads();
+      grouped_chunk<2, G_SPLIT>(A, S, s_tok, s_row, e, 32 * strip, crows);
+    }
+    return;
+  }
+
+  const int e = blockIdx.x / tiles_n;
+  const int tn = blockIdx.x - e * tiles_n;
   const int cnt = counts[e];
   if (cnt == 0) return;
   const int off = offsets[e];
-  const GArgs A{aq, ad, top_k, wq4, wd, n, k, y};
   const int n0 = tn * GBN;
+  // with the split pieces, rows past the first SPLIT_FIRST go to the split
+  // workgroups
+  const int own = split ? min(cnt, SPLIT_FIRST) : cnt;
 
-  for (int c0 = 0; c0 < cnt; c0 += GCH) {
-    const int crows = min(GCH, cnt - c0);
+  for (int c0 = 0; c0 < own; c0 += GCH) {
+    const int crows = min(GCH, own - c0);
     // the previous chunk is done with s_tok, s_row and S (each chunk ends
     // with every load landed)
     __syncthreads();
@@ -660,11 +779,11 @@ __global__ __launch_bounds__(GT, 3) void k_grouped_w4a8(
     }
     __syncthreads();
     if (crows <= 16)
-      grouped_chunk<1, true>(A, S, s_tok, s_row, e, n0, crows);
+      grouped_chunk<1, G_HALF>(A, S, s_tok, s_row, e, n0, crows);
     else if (crows <= 32)
-      grouped_chunk<1>(A, S, s_tok, s_row, e, n0, crows);
+      grouped_chunk<1, G_FULL>(A, S, s_tok, s_row, e, n0, crows);
     else
-      grouped_chunk<2>(A, S, s_tok, s_row, e, n0, crows);
+      grouped_chunk<2, G_FULL>(A, S, s_tok, s_row, e, n0, crows);
   }
 }
 
@@ -672,24 +791,34 @@ __global__ __launch_bounds__(GT, 3) void k_grouped_w4a8(
 
 hipError_t launch_route_topk(const int32_t *ids, int64_t rows_total,
                              int64_t n_experts, int64_t top_k, int32_t *counts,
-                             int32_t *offsets, int32_t *rows, int32_t *order,
-                             float *y, int64_t n, hipStream_t stream) {
+                             int32_t *offsets, int32_t *rows, float *y, int64_t n,
+                             hipStream_t stream) {
   hipLaunchKernelGGL(k_route, dim3((unsigned)n_experts), dim3(RT), 0, stream,
                      ids, (int)rows_total, (int)n_experts, (int)top_k, counts,
-                     offsets, rows, order, y, (int)n);
+                     offsets, rows, y, (int)n);
   return hipGetLastError();
 }
+
+// Workgroups for the split pieces: one per item while the items fit in
+// G_SPLIT_WGS (those without an item exit at once), else a loop over items.
+constexpr int64_t G_SPLIT_WGS = 1536;
 
 hipError_t launch_grouped_w4a8(const int8_t *aq, const uint16_t *ad,
                                int64_t top_k, const uint8_t *wq4,
                                const uint16_t *wd, int64_t n_experts, int64_t n,
-                               int64_t k, const int32_t *counts,
-                               const int32_t *offsets, const int32_t *rows,
-                               const int32_t *order, float *y, hipStream_t stream) {
+                               int64_t k, int64_t rows_total, const int32_t *counts,
+                               const int32_t *offsets, const int32_t *rows, float *y,
+                               hipStream_t stream) {
   const int64_t tiles_n = (n + GBN - 1) / GBN;
-  hipLaunchKernelGGL(k_grouped_w4a8, dim3((unsigned)(n_experts * tiles_n)),
+  // at most rows_total / 16 pieces (each covers 16 rows past an expert's
+  // first 64), each of (n + 31) / 32 strips
+  const int64_t most = n_experts <= SPLIT_MAX_EXPERTS && rows_total > SPLIT_FIRST
+                           ? rows_total / SPLIT_ROWS * ((n + 31) / 32)
+                           : 0;
+  const int64_t split_wgs = std::min(most, G_SPLIT_WGS);
+  hipLaunchKernelGGL(k_grouped_w4a8, dim3((unsigned)(n_experts * tiles_n + split_wgs)),
                      dim3(GT), 0, stream, aq, ad, (int)top_k, wq4, wd,
-                     (int)n_experts, (int)n, (int)k, counts, offsets, rows, order, y);
+                     (int)n_experts, (int)n, (int)k, counts, offsets, rows, y);
   return hipGetLastError();
 }
 

@@ -169,10 +169,10 @@ BQI_API int route_topk(const int32_t *topk_ids, int64_t n_tokens, int64_t top_k,
                int32_t *rows, void *stream);
 
 /* Bytes of device workspace qgemm_w4a8_grouped needs for these sizes (0 for
- * sizes it rejects).  The workspace holds the routing: counts, offsets, the
- * experts in dispatch order and the routed rows of each expert, about
- * 4 * (n_tokens * top_k + 3 * n_experts) bytes.  k is only validated (it must
- * be a nonnegative multiple of 32): the size no longer depends on it. */
+ * sizes it rejects).  The workspace holds the routing: counts, offsets and
+ * the routed rows of each expert, about 4 * (n_tokens * top_k + 2 * n_experts)
+ * bytes.  k is only validated (it must be a nonnegative multiple of 32): the
+ * size no longer depends on it. */
 BQI_API size_t qgemm_w4a8_grouped_workspace_size(int64_t n_tokens, int64_t top_k,
                                          int64_t n_experts, int64_t k);
 

@@ -578,7 +578,7 @@ def test_grouped_w4a8_moe_workload_full(weights):
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
 
 
-def grouped_one_hot_probe(T, top_k, E, K, N, seed):
+def grouped_one_hot_probe(T, top_k, E, K, N, seed, ids=None):
     """One-hot-block probe through the grouped W4A8 path: token t's
     activation codes are nonzero only in group t % nb and every scale is a
     power of two, so each output is 2^-6 * P exactly, where P is the int32
@@ -586,7 +586,8 @@ def grouped_one_hot_probe(T, top_k, E, K, N, seed):
     read back and compared bit-exactly with the oracle's block dots."""
     nb = K // 32
     g = np.random.default_rng(seed)
-    ids = W.topk_ids(T, top_k, E, seed=seed)
+    if ids is None:
+        ids = W.topk_ids(T, top_k, E, seed=seed)
     aq = W.random_int8("moe", 740, (T, K), seed=seed)
     keep = (np.arange(K)[None, :] // 32) == (np.arange(T)[:, None] % nb)
     aq = np.where(keep, aq, 0).astype(np.int8)
@@ -615,6 +616,47 @@ def grouped_one_hot_probe(T, top_k, E, K, N, seed):
 def test_grouped_block_dots_bitexact_probe(T, top_k, E, K, N):
     log("grouped probe T=%d top_k=%d E=%d K=%d N=%d" % (T, top_k, E, K, N))
     grouped_one_hot_probe(T, top_k, E, K, N, seed=T + K)
+
+
+def skewed_ids(T, top_k, E, hot, seed):
+    """Routed ids where each slot goes to expert 0 with probability `hot`,
+    else to a uniform random expert (duplicates within a token allowed)."""
+    g = np.random.default_rng(seed)
+    ids = g.integers(0, E, size=(T, top_k)).astype(np.int32)
+    ids[g.random((T, top_k)) < hot] = 0
+    return ids
+
+
+@pytest.mark.parametrize("T,top_k,E,K,N,hot", [
+    (700, 2, 5, 1184, 200, 0.6),   # ~840 rows on one expert (49 pieces); K quarters of 12, 12, 12, 1 groups; ragged strip
+    (4000, 1, 2, 256, 768, 0.97),  # ~3900 rows on one expert: more split items than split workgroups
+    (180, 1, 2, 64, 96, 0.9),      # k = 64: three of the four K quarters hold no group
+])
+def test_grouped_w4a8_split_pieces(T, top_k, E, K, N, hot):
+    """Experts with far more than 64 routed rows: past its first 64 rows an
+    expert's rows run as 16-row pieces, each 32-column strip of a piece on
+    one workgroup with K split over its four waves.  Against the oracle, and
+    invalid ids still give zero rows."""
+    log("grouped split pieces T=%d top_k=%d E=%d K=%d N=%d" % (T, top_k, E, K, N))
+    ids = skewed_ids(T, top_k, E, hot, seed=T + K)
+    ids[1, 0] = -1
+    counts = np.bincount(ids[ids >= 0].ravel(), minlength=E)
+    assert counts.max() > 64 + 16
+    qa = W.random_int8("moe", 714, (T, K), seed=T)
+    da = W.random_scales("moe", 715, (T, K // 32), seed=T)
+    packed, wsc = W.random_w4_codes(E, N, K, seed=T + 1)
+    y = run_grouped(qa, da, ids, packed, wsc)
+    yr, asum = oracle.qgemm_w4a8_grouped(qa, da, ids, packed, wsc, nthreads=oracle_threads())
+    assert_within_bound(y, yr, asum, K // 32, "split pieces T=%d" % T)
+    assert (y[ids < 0] == 0).all()
+
+
+def test_grouped_block_dots_bitexact_probe_split():
+    """The one-hot probe through the split pieces: one expert takes ~90% of
+    400 routed rows, K = 1184 (quarters of 12, 12, 12 and 1 groups)."""
+    T, top_k, E, K, N = 400, 1, 2, 1184, 200
+    log("grouped probe, split pieces")
+    grouped_one_hot_probe(T, top_k, E, K, N, seed=5, ids=skewed_ids(T, top_k, E, 0.9, seed=5))
 
 
 @pytest.mark.parametrize("counts", [(65, 80, 16, 1, 15, 17), (96, 81, 33, 48, 64, 32)])
