@@ -229,7 +229,7 @@ int quantize_qgemm_q8_0(const void *x, int x_dtype, int64_t m, int64_t k,
   if (m > 16 && ((m + 127) / 128 * ((n + 127) / 128) > kI32Max ||
                  m * k > kI32Max || n * k > kI32Max))
     return BQI_ESHAPE;
-  if (n > 0 && bqi::gemv_fused_supported(m, k) && ldx <= kI32Max)
+  if (n > 0 && m <= 16 && bqi::gemv_fused_supported(m, n, k, wd) && ldx <= kI32Max)
     return hip_status(bqi::launch_gemv_fused(x, x_dtype == BQI_F16, ldx, m, wq,
                                              wd, n, k, y, q, d, s));
   const int st = hip_status(bqi::launch_quantize_q8_0(x, x_dtype == BQI_F16, m,

@@ -35,8 +35,9 @@ hipError_t launch_gemv_thin(const int8_t *aq, const uint16_t *ad, int64_t m,
                             const int8_t *wq, const uint16_t *wd, int64_t n,
                             int64_t k, float *y, hipStream_t stream);
 
-// fused quantize + thin-M GEMM (one launch) for the sizes it covers
-bool gemv_fused_supported(int64_t m, int64_t k);
+// fused quantize + thin-M GEMM (one launch, bit-identical to the quantizer
+// and launch_gemv_thin) for the sizes it covers
+bool gemv_fused_supported(int64_t m, int64_t n, int64_t k, const uint16_t *wd);
 hipError_t launch_gemv_fused(const void *x, bool f16, int64_t ldx, int64_t m,
                              const int8_t *wq, const uint16_t *wd, int64_t n,
                              int64_t k, float *y, int8_t *q_out,

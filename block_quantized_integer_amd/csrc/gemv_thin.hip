@@ -527,10 +527,22 @@ __device__ __forceinline__ long mf_pair(uint32_t lo, uint32_t hi) {
 
 // (no __restrict__ on the inputs: with it the compiler may move loads across
 // the compiler barriers that fix their issue order)
-template <int RG>
+//
+// SRC = ACT_F32 / ACT_F16 (quantize_qgemm_q8_0 on a few small rows, one K
+// part: k <= 1 KB and m * k <= MF_FUSED_ELEMS): instead of loading Q8_0
+// codes, the waves of a workgroup (MF_FUSED_GROUPS row groups) quantize the m
+// activation rows between them (the quantizer's device routine, so the codes
+// are those of quantize_q8_0) into the LDS stage, behind one barrier, and
+// workgroup 0 writes the codes and scales out.  Each lane loads its elements
+// before the weight stream and quantizes once the weight loads are issued.
+constexpr int MF_FUSED_ELEMS = 4096;
+constexpr int MF_FUSED_GROUPS = 4;
+
+template <int RG, int SRC>
 __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
-    const int8_t *aq, const uint16_t *ad, int m, const int8_t *wq,
-    const uint16_t *wd, int n, int k, int ks, float *y) {
+    const int8_t *aq, const uint16_t *ad, const void *x, int ldx, int m,
+    const int8_t *wq, const uint16_t *wd, int n, int k, int ks, float *y,
+    int8_t *q_out, uint16_t *d_out) {
   // weight load pairs in flight per wave: MF_DEPTH for RG = 1 (12 waves per
   // CU); two whole chunks (six pairs) for RG = 3, one wave per SIMD
   // (measured: four pairs, which split a chunk, 14.1 us at m = 16; six 11.9;
@@ -560,17 +572,42 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
   // order matters (loads retire in order): the activation codes (L2, straight
   // to LDS, invisible to the compiler), their scales, the weight scales, then
   // the weight chunks in the order they are multiplied.
-  // 1. activation codes: row r, bytes [1024 part + 16 lane, +16) (lanes past
-  //    k re-read the row's last 16 bytes, never used)
-  const int aoff = min(1024 * part + 16 * lane, k - 16);
-  for (int r = 0; r < m; ++r) dma_lds16(aq + (int64_t)r * k + aoff, sA + r * lda + 1024 * part);
-  // 2. activation scales of the part: value c = lane + 64 u is row c / 32,
-  //    block c % 32 (past m or the part: re-read a valid one, not stored)
+  // fused source: round u of the quantizer, lane l of wave w takes elements
+  // 4 (l % 8) .. +3 of block c = 8 (u nwaves + w) + l / 8 of the part's
+  // m x pb blocks (row c / pb, block c % pb; past them: element 0, not
+  // stored); the launch gives the workgroup MF_FUSED_GROUPS waves, so QR
+  // rounds cover m * k <= MF_FUSED_ELEMS
+  constexpr int QR = SRC == ACT_Q8 ? 1 : MF_FUSED_ELEMS / 256 / MF_FUSED_GROUPS;
+  float xv[QR][4];
   uint16_t h[8];
+  if constexpr (SRC == ACT_Q8) {
+    // 1. activation codes: row r, bytes [1024 part + 16 lane, +16) (lanes
+    //    past k re-read the row's last 16 bytes, never used)
+    const int aoff = min(1024 * part + 16 * lane, k - 16);
+    for (int r = 0; r < m; ++r) dma_lds16(aq + (int64_t)r * k + aoff, sA + r * lda + 1024 * part);
+    // 2. activation scales of the part: value c = lane + 64 u is row c / 32,
+    //    block c % 32 (past m or the part: re-read a valid one, not stored)
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int c = lane + 64 * u, i = c >> 5, b = c & 31;
-    h[u] = ad[(int64_t)min(i, m - 1) * nbk + pb0 + min(b, pb - 1)];
+    for (int u = 0; u < 8; ++u) {
+      const int c = lane + 64 * u, i = c >> 5, b = c & 31;
+      h[u] = ad[(int64_t)min(i, m - 1) * nbk + pb0 + min(b, pb - 1)];
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < QR; ++u) {
+      const int c = 8 * (u * nwaves + wave) + (lane >> 3), i = c / pb, b = c - i * pb;
+      const int64_t off = i < m ? (int64_t)i * ldx + QK * (pb0 + b) + 4 * (lane & 7) : 0;
+      if constexpr (SRC == ACT_F32) {
+        const f32x4 r = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(x) + off);
+        xv[u][0] = r.x; xv[u][1] = r.y; xv[u][2] = r.z; xv[u][3] = r.w;
+      } else {
+        const uint2 r = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(x) + off);
+        xv[u][0] = half_bits_to_float((uint16_t)(r.x & 0xffffu));
+        xv[u][1] = half_bits_to_float((uint16_t)(r.x >> 16));
+        xv[u][2] = half_bits_to_float((uint16_t)(r.y & 0xffffu));
+        xv[u][3] = half_bits_to_float((uint16_t)(r.y >> 16));
+      }
+    }
   }
   __asm__ volatile("" ::: "memory");
   // 3. weight scales of the part as dwords: instruction (j, i), lane l -> row
@@ -610,14 +647,38 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
 #pragma unroll
   for (int q = 0; q < DEPTH; ++q) load_pair(q);
   __asm__ volatile("" ::: "memory");
-  // the loads above are the only ones issued after the scales (2.), so this
-  // waits for the scales and the activation codes but not the weights
-  wait_vmcnt<4 * RG + 2 * DEPTH>();
+  if constexpr (SRC == ACT_Q8) {
+    // the loads above are the only ones issued after the scales (2.), so
+    // this waits for the scales and the activation codes but not the weights
+    wait_vmcnt<4 * RG + 2 * DEPTH>();
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int c = lane + 64 * u, i = c >> 5, b = c & 31;
-    // blocks past the part are zeros (the last part reads whole chunks)
-    if (i < m) sD[(pb0 + b) * 16 + i] = b < pb ? half_bits_to_float(h[u]) : 0.0f;
+    for (int u = 0; u < 8; ++u) {
+      const int c = lane + 64 * u, i = c >> 5, b = c & 31;
+      // blocks past the part are zeros (the last part reads whole chunks)
+      if (i < m) sD[(pb0 + b) * 16 + i] = b < pb ? half_bits_to_float(h[u]) : 0.0f;
+    }
+  } else {
+    const bool out = blockIdx.x == 0;
+#pragma unroll
+    for (int u = 0; u < QR; ++u) {
+      const int c = 8 * (u * nwaves + wave) + (lane >> 3), i = c / pb, b = c - i * pb, sub = lane & 7;
+      uint16_t dbits;
+      const uint32_t packed = q8_0_quantize4(xv[u], dbits);  // every lane (DPP inside)
+      if (i < m) {
+        *reinterpret_cast<uint32_t *>(sA + i * lda + QK * (pb0 + b) + 4 * sub) = packed;
+        if (sub == 0) sD[(pb0 + b) * 16 + i] = half_bits_to_float(dbits);
+        if (out) {
+          *reinterpret_cast<uint32_t *>(q_out + (int64_t)i * k + QK * (pb0 + b) + 4 * sub) = packed;
+          if (sub == 0) d_out[(int64_t)i * nbk + pb0 + b] = dbits;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = lane + 64 * u, i = c >> 5, b = c & 31;
+      if (i < m && b >= pb) sD[(pb0 + b) * 16 + i] = 0.0f;
+    }
+    __syncthreads();  // every wave's share of the stage
   }
 #pragma unroll
   for (int j = 0; j < RG; ++j)
@@ -772,44 +833,59 @@ bool mf_shape(int64_t n, int64_t k, MfShape *out) {
   return true;
 }
 
-template <int RG>
-hipError_t launch_mfma16_rg(const int8_t *aq, const uint16_t *ad, int64_t m,
-                            const int8_t *wq, const uint16_t *wd, int64_t n, int64_t k,
-                            const MfShape &sh, float *y, hipStream_t stream) {
+template <int RG, int SRC>
+hipError_t launch_mfma16_rg(const int8_t *aq, const uint16_t *ad, const void *x, int64_t ldx,
+                            int64_t m, const int8_t *wq, const uint16_t *wd, int64_t n,
+                            int64_t k, const MfShape &sh, float *y, int8_t *q_out,
+                            uint16_t *d_out, hipStream_t stream) {
   // LDS: the stages plus one weight-scale slot per row group of every wave
   const int64_t lds = mf_lds_bytes(k, (int64_t)sh.ks * sh.groups * RG);
   static bool raised[64];
   if (lds > 65536) {
-    const hipError_t e = raise_dynamic_lds((const void *)k_gemv_mfma16<RG>, (int)MF_LDS_MAX, raised);
+    const hipError_t e = raise_dynamic_lds((const void *)k_gemv_mfma16<RG, SRC>, (int)MF_LDS_MAX, raised);
     if (e != hipSuccess) return e;
   }
   const int64_t rows_per_wg = 16 * RG * sh.groups;
   const int64_t wgs = (n + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL(k_gemv_mfma16<RG>, dim3((unsigned)wgs), dim3(64 * sh.ks * sh.groups),
-                     (unsigned)lds, stream, aq, ad, (int)m, wq, wd, (int)n, (int)k, sh.ks, y);
+  hipLaunchKernelGGL((k_gemv_mfma16<RG, SRC>), dim3((unsigned)wgs), dim3(64 * sh.ks * sh.groups),
+                     (unsigned)lds, stream, aq, ad, x, (int)ldx, (int)m, wq, wd, (int)n, (int)k,
+                     sh.ks, y, q_out, d_out);
   return hipGetLastError();
 }
 
 hipError_t launch_mfma16(const int8_t *aq, const uint16_t *ad, int64_t m,
                          const int8_t *wq, const uint16_t *wd, int64_t n, int64_t k,
                          const MfShape &sh, float *y, hipStream_t stream) {
-  if (sh.rg == 3) return launch_mfma16_rg<3>(aq, ad, m, wq, wd, n, k, sh, y, stream);
-  return launch_mfma16_rg<1>(aq, ad, m, wq, wd, n, k, sh, y, stream);
+  if (sh.rg == 3)
+    return launch_mfma16_rg<3, ACT_Q8>(aq, ad, nullptr, 0, m, wq, wd, n, k, sh, y, nullptr, nullptr, stream);
+  return launch_mfma16_rg<1, ACT_Q8>(aq, ad, nullptr, 0, m, wq, wd, n, k, sh, y, nullptr, nullptr, stream);
+}
+}  // namespace
+
+namespace {
+// The kernel that the thin-M dispatch takes: more than 4 rows, int8 MFMA
+// while its stages fit (k a multiple of 64 and wd 4-byte aligned: the weight
+// scales load in aligned pairs); otherwise the register kernel while the m
+// rows of codes fit its LDS stage; otherwise the LDS kernel.
+enum class ThinPath { MFMA16, REG, LDS };
+
+ThinPath thin_path(int64_t m, int64_t n, int64_t k, const uint16_t *wd, MfShape *sh) {
+  if (m > 4 && ((uintptr_t)wd & 3) == 0 && mf_shape(n, k, sh)) return ThinPath::MFMA16;
+  const int64_t ch = pow2_ceil((k + 1023) / 1024);
+  if (pow2_ceil(m) <= 16 && reg_fits((int)pow2_ceil(m), (int)std::min<int64_t>(ch, 1 << 20), ACT_Q8))
+    return ThinPath::REG;
+  return ThinPath::LDS;
 }
 }  // namespace
 
 hipError_t launch_gemv_thin(const int8_t *aq, const uint16_t *ad, int64_t m,
                             const int8_t *wq, const uint16_t *wd, int64_t n,
                             int64_t k, float *y, hipStream_t stream) {
-  // more than 4 rows: int8 MFMA while its stages fit (k a multiple of 64 and
-  // wd 4-byte aligned: the weight scales load in aligned pairs)
   MfShape sh;
-  if (m > 4 && ((uintptr_t)wd & 3) == 0 && mf_shape(n, k, &sh))
-    return launch_mfma16(aq, ad, m, wq, wd, n, k, sh, y, stream);
-  // otherwise the register kernel while the m rows of codes fit its LDS stage
-  const int64_t ch = pow2_ceil((k + 1023) / 1024);
+  const ThinPath path = thin_path(m, n, k, wd, &sh);
+  if (path == ThinPath::MFMA16) return launch_mfma16(aq, ad, m, wq, wd, n, k, sh, y, stream);
   const int64_t mt = pow2_ceil(m);
-  if (mt <= 16 && reg_fits((int)mt, (int)std::min<int64_t>(ch, 1 << 20), ACT_Q8)) {
+  if (path == ThinPath::REG) {
     switch (mt) {
       case 1: return launch_reg_ch<1, ACT_Q8>(aq, ad, nullptr, 0, m, wq, wd, n, k, y, nullptr, nullptr, stream);
       case 2: return launch_reg_ch<2, ACT_Q8>(aq, ad, nullptr, 0, m, wq, wd, n, k, y, nullptr, nullptr, stream);
@@ -825,21 +901,52 @@ hipError_t launch_gemv_thin(const int8_t *aq, const uint16_t *ad, int64_t m,
   return launch_mt<16>(aq, ad, m, wq, wd, n, k, y, stream);
 }
 
-// The fused launch pays off for one activation row only: every workgroup
-// quantizes all m rows again (m = 4: 19.9 us against 13.4 us for the two
-// calls on the decode shape), so larger m takes the quantizer and then the
-// GEMV.
-bool gemv_fused_supported(int64_t m, int64_t k) {
-  const int64_t ch = (k + 1023) / 1024;
-  return m <= 1 && ch <= 16;
+// The fused launch runs the kernel that the two calls would run, with the
+// quantizer inside, so its results are bit-identical to theirs.  Every
+// workgroup (the MFMA kernel: every wave) quantizes the activation rows
+// again, which pays off for one row at any k up to 16 K, and for a few rows
+// while m * k <= MF_FUSED_ELEMS (16 KB of fp32).  Larger problems take the
+// quantizer and then the GEMV (m = 4 on the decode shape: 19.9 us fused
+// against 13.4 us for the two calls).
+bool gemv_fused_supported(int64_t m, int64_t n, int64_t k, const uint16_t *wd) {
+  MfShape sh;
+  switch (thin_path(m, n, k, wd, &sh)) {
+    case ThinPath::MFMA16:
+      // (one row group per wave: the three-group shape would spill the
+      // quantizer's registers)
+      return sh.ks == 1 && sh.rg == 1 && m * k <= MF_FUSED_ELEMS;
+    case ThinPath::REG:
+      return m == 1 || (m <= 4 && m * k <= MF_FUSED_ELEMS);
+    default:
+      return false;
+  }
 }
 
 hipError_t launch_gemv_fused(const void *x, bool f16, int64_t ldx, int64_t m,
                              const int8_t *wq, const uint16_t *wd, int64_t n,
                              int64_t k, float *y, int8_t *q_out,
                              uint16_t *d_out, hipStream_t stream) {
-  if (f16) return launch_reg_ch<1, ACT_F16>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
-  return launch_reg_ch<1, ACT_F32>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
+  MfShape sh;
+  if (thin_path(m, n, k, wd, &sh) == ThinPath::MFMA16) {
+    // one K part (k <= 1 KB) and one row group per wave, as the two-call
+    // path runs it; MF_FUSED_GROUPS row groups per workgroup share the
+    // quantization (the workgroup shape does not change any result)
+    // (waves past the last row group compute clamped rows and store nothing)
+    sh.groups = MF_FUSED_GROUPS;
+    return f16 ? launch_mfma16_rg<1, ACT_F16>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, sh, y, q_out, d_out, stream)
+               : launch_mfma16_rg<1, ACT_F32>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, sh, y, q_out, d_out, stream);
+  }
+  switch (pow2_ceil(m)) {
+    case 1:
+      return f16 ? launch_reg_ch<1, ACT_F16>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream)
+                 : launch_reg_ch<1, ACT_F32>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
+    case 2:
+      return f16 ? launch_reg_ch<2, ACT_F16>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream)
+                 : launch_reg_ch<2, ACT_F32>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
+    default:
+      return f16 ? launch_reg_ch<4, ACT_F16>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream)
+                 : launch_reg_ch<4, ACT_F32>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, y, q_out, d_out, stream);
+  }
 }
 
 }  // namespace bqi

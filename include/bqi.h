@@ -137,11 +137,13 @@ BQI_API int qgemm_q8_0(const int8_t *aq, const uint16_t *ad, int64_t m,
  *   q  [m][k] int8, d [m][k/32] fp16 bits (output): the Q8_0 activations,
  *      bit-identical to quantize_q8_0(x)
  *
- * For m == 1 with k <= 16384 it is one launch: every workgroup quantizes the
- * activation row itself while its weight loads are in flight, which saves
- * the quantizer's launch on the decode path.  Other sizes (including m > 1,
- * where repeating the quantization in every workgroup costs more than the
- * launch) run quantize_q8_0 and qgemm_q8_0 back to back on `stream`.
+ * It is one launch for m == 1 with k <= 16384, and for 1 < m <= 16 with
+ * m * k <= 4096 (16 KB of fp32) where the thin-M kernel of qgemm_q8_0 has a
+ * quantizing form (the register kernel for m <= 4; the MFMA thin-M kernel
+ * with k <= 1024 for m > 4): that kernel quantizes the activation rows itself
+ * while its weight loads are in flight, which saves the quantizer's launch.
+ * Other sizes (where repeating the quantization in every workgroup costs more
+ * than the launch) run quantize_q8_0 and qgemm_q8_0 back to back on `stream`.
  * n == 0 only quantizes.  Requirements: those of quantize_q8_0 and
  * qgemm_q8_0.
  */

@@ -340,7 +340,13 @@ def test_decode_workload_full(decode_weights, m):
     (1, 96, 40, "f32"),         # fused, K shorter than one 1 KB chunk
     (4, 4096, 12288, "f32"),    # not fused: quantize + thin-M GEMM, four rows
     (2, 8192, 300, "f16"),      # not fused, fp16 input, ragged N
-    (3, 96, 40, "f32"),         # not fused, K shorter than one 1 KB chunk
+    (3, 96, 40, "f32"),         # fused (m * k <= 4096): register kernel, K shorter than one 1 KB chunk
+    (2, 2048, 77, "f32"),       # fused: register kernel, two 1 KB chunks
+    (4, 1024, 96, "f16"),       # fused: register kernel, fp16 input
+    (16, 256, 512, "f32"),      # fused: the MFMA thin-M kernel (the small GEMM configuration)
+    (8, 512, 300, "f16"),       # fused: MFMA thin-M kernel, fp16 input, ragged N
+    (5, 768, 130, "f32"),       # fused: MFMA thin-M kernel, 5 of 16 rows, 24 blocks
+    (16, 192, 70, "f32"),       # fused: MFMA thin-M kernel, 6 blocks (a chunk partly past k)
     (16, 4096, 512, "f32"),     # not fused: quantize + thin-M GEMM (m = 16)
     (40, 256, 130, "f16"),      # not fused: quantize + MFMA GEMM
 ])
@@ -363,6 +369,20 @@ def test_fused_quantize_qgemm(decode_weights, m, k, n, dtype):
     assert torch.equal(y, y2), "fused y differs from qgemm_q8_0 on the same codes"
     yr, asum = oracle.qgemm_q8_0(qr, dr, qw, dw, nthreads=oracle_threads())
     assert_within_bound(host(y), yr, asum, k // 32, "fused m=%d k=%d" % (m, k))
+
+
+def test_fused_quantize_qgemm_small_strided():
+    """The fused MFMA thin-M path (16 rows, k = 256) on rows with a stride
+    ldx > k: codes and scales as the oracle's, y bit-identical to the two
+    calls."""
+    m, k, n = 16, 256, 512
+    qw_g, dw_g, qw, dw = check_quantize(W.weights("decode", n, k, seed=99), "small strided W")
+    wide = W.activations("decode", m, k + 96, seed=12)
+    x = dev_tensor(wide)[:, 32:32 + k]
+    y, q, d = bqi.quantize_qgemm_q8_0(x, qw_g, dw_g)
+    qr, dr = oracle.quantize_q8_0(np.ascontiguousarray(wide[:, 32:32 + k]))
+    assert np.array_equal(host(q), qr) and np.array_equal(host(d), dr)
+    assert torch.equal(y, bqi.qgemm_q8_0(q, d, qw_g, dw_g))
 
 
 @pytest.mark.parametrize("rows", [1, 3])
