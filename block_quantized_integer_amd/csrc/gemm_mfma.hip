@@ -39,6 +39,8 @@
 // leave one.  With the CU to itself it keeps three stage buffers in (dynamic)
 // LDS and issues the loads two stages ahead.  Larger grids stay on the 4-wave
 // kernel, whose two workgroups per CU cover each other's stalls.
+#include <type_traits>
+
 #include "bqi_device.h"
 #include "bqi_launch.h"
 
@@ -138,14 +140,16 @@ __global__ __launch_bounds__(THREADS, 2) void k_gemm_mfma(
     sw_off[h] = min(n0 + row, n - 1) * nbk + blk;
   }
   uint16_t sa_reg[SCALES_PER_THREAD], sw_reg[SCALES_PER_THREAD];
-  auto issue_stage = [&](int s, int buf) {
+  // full: stage s lies inside k (a compile-time flag, so that a full stage
+  // issues its loads with the loop-invariant offsets and no clamping)
+  auto issue_stage = [&](int s, int buf, auto full_c) {
+    constexpr bool full = decltype(full_c)::value;
     const int k0 = s * BK;
-    const bool full = k0 + BK <= k;  // uniform
     const int8_t *abase = aq + k0, *wbase = wq + k0;
 #pragma unroll
     for (int q = 0; q < LOADS_PER_WAVE; ++q) {
       int ao = aoff[q], wo = woff[q];
-      if (!full) {
+      if constexpr (!full) {
         const int fix = min(c16[q], k - 16 - k0) - c16[q];
         ao += fix;
         wo += fix;
@@ -159,7 +163,7 @@ __global__ __launch_bounds__(THREADS, 2) void k_gemm_mfma(
 #pragma unroll
     for (int h = 0; h < SCALES_PER_THREAD; ++h) {
       int ao = sa_off[h], wo = sw_off[h];
-      if (!full) {
+      if constexpr (!full) {
         const int blk = (tid + THREADS * h) % NBS;
         const int fix = min(blk, nbk - 1 - s * NBS) - blk;
         ao += fix;
@@ -195,7 +199,14 @@ __global__ __launch_bounds__(THREADS, 2) void k_gemm_mfma(
 #pragma unroll
   for (int r = 0; r < 16; ++r) seed[r] = MAGIC_BITS;
 
-  issue_stage(0, 0);
+  // stage s is full while (s + 1) * BK <= k (the branch is uniform)
+  auto issue = [&](int s, int buf) {
+    if ((s + 1) * BK <= k)
+      issue_stage(s, buf, std::true_type{});
+    else
+      issue_stage(s, buf, std::false_type{});
+  };
+  issue(0, 0);
   store_scales(0, 0);
   wait_vmcnt<0>();  // direct loads of stage 0 have landed
   __syncthreads();
@@ -203,7 +214,7 @@ __global__ __launch_bounds__(THREADS, 2) void k_gemm_mfma(
   for (int s = 0; s < stages; ++s) {
     const int buf = s & 1;
     const Tiles &TB = T[buf];
-    if (s + 1 < stages) issue_stage(s + 1, buf ^ 1);
+    if (s + 1 < stages) issue(s + 1, buf ^ 1);
 
     // The stage's 16 MFMAs (4 blocks x 2x2 tiles) run as a pipeline of depth
     // one: tile u's MFMA is issued before tile u-1's epilogue, into the other
