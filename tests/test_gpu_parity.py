@@ -703,7 +703,8 @@ def test_grouped_w4a8_chunk_tails(counts):
 def seeded_grouped_cases(count, seed=20261203):
     """Random (T, top_k, E, K, N): routed rows from a few (the v_dot4 GEMV)
     to a few thousand (the MFMA kernel, one or several chunks per expert),
-    up to 300 experts (past 256 the GEMM takes them in index order)."""
+    up to 300 experts (past 256 the GEMM takes every expert's rows on its
+    own workgroups, without split pieces)."""
     g = np.random.default_rng(seed)
     out = []
     while len(out) < count:
@@ -764,11 +765,11 @@ def test_grouped_w4a8_beyond_one_routing_chunk():
 @pytest.mark.parametrize("T,tk,E", [
     (1024, 8, 128),   # 8192 routed rows: the routing pass in one pass over ids in registers
     (1025, 8, 128),   # 8200: two chunks of ids
-    (2048, 4, 256),   # the most experts the routing pass orders by count
-    (1000, 4, 300)])  # more: the GEMM takes the experts in index order
+    (2048, 4, 256),   # the most experts with split pieces (four experts per lane of one wave)
+    (1000, 4, 300)])  # more: every expert's rows on its own workgroups, 64 at a time
 def test_grouped_w4a8_routing_paths_at_their_limits(T, tk, E):
-    """The MFMA path at the routing pass's limits (ids held in registers, and
-    the dispatch order by routed-row count), with a few invalid ids (their
+    """The MFMA path at the routing pass's limits (ids held in registers) and
+    at the split pieces' limit of 256 experts, with a few invalid ids (their
     rows must be zero), against the oracle."""
     K, N = 256, 160
     log("grouped routing paths T=%d top_k=%d E=%d" % (T, tk, E))
