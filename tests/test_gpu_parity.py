@@ -385,6 +385,43 @@ def test_fused_quantize_qgemm_small_strided():
     assert torch.equal(y, bqi.qgemm_q8_0(q, d, qw_g, dw_g))
 
 
+def seeded_fused_cases(count, seed=20261204):
+    """Random (m, k, n, fp16 input, row padding) around the sizes that
+    quantize_qgemm_q8_0 runs as one launch (m <= 16 with m * k <= 4096, and
+    m = 1), with some larger ones that take the two calls."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        if g.random() < 0.7:  # within the one-launch sizes of 2..16 rows
+            m = int(g.integers(2, 17))
+            k = 32 * int(g.integers(1, 4096 // (32 * m) + 1))
+        else:
+            m = int(g.integers(1, 21))
+            k = 32 * int(g.integers(1, 140))
+        n = int(g.integers(1, 1500))
+        out.append((m, k, n, bool(g.integers(0, 2)), int(g.choice([0, 32, 96]))))
+    return out
+
+
+@pytest.mark.parametrize("m,k,n,f16,pad", seeded_fused_cases(16))
+def test_fused_quantize_qgemm_seeded_sweep(m, k, n, f16, pad):
+    """quantize_qgemm_q8_0 on seeded random sizes, fp32 or fp16 rows with a
+    stride: codes and scales as the oracle's quantizer, y bit-identical to
+    qgemm_q8_0 on those codes and within the bound of the oracle's value."""
+    log("fused sweep m=%d k=%d n=%d f16=%s pad=%d" % (m, k, n, f16, pad))
+    g = np.random.default_rng(m * 100000 + k + n)
+    x = (g.standard_normal((m, k + pad)) * float(g.choice([1.0, 1e-3, 50.0])))
+    x = x.astype(np.float16 if f16 else np.float32)
+    qw_g, dw_g, qw, dw = check_quantize(W.weights("decode", n, k, seed=n + k), "fused sweep W")
+    off = 32 if pad else 0
+    y, q, d = bqi.quantize_qgemm_q8_0(dev_tensor(x)[:, off:off + k], qw_g, dw_g)
+    qr, dr = oracle.quantize_q8_0(np.ascontiguousarray(x[:, off:off + k]))
+    assert np.array_equal(host(q), qr) and np.array_equal(host(d), dr), "fused codes/scales"
+    assert torch.equal(y, bqi.qgemm_q8_0(q, d, qw_g, dw_g)), "fused y differs from the two calls"
+    yr, asum = oracle.qgemm_q8_0(qr, dr, qw, dw, nthreads=oracle_threads())
+    assert_within_bound(host(y), yr, asum, k // 32, "fused sweep m=%d k=%d" % (m, k))
+
+
 @pytest.mark.parametrize("rows", [1, 3])
 def test_fused_quantize_qgemm_strided_rows(decode_weights, rows):
     """Row stride ldx > k (a column slice of a wider fp32 tensor); one row
@@ -734,6 +771,43 @@ def test_grouped_w4a8_seeded_sweep(T, top_k, E, K, N):
     y = run_grouped(qa, da, ids, packed, wsc)
     yr, asum = oracle.qgemm_w4a8_grouped(qa, da, ids, packed, wsc, nthreads=oracle_threads())
     assert_within_bound(y, yr, asum, K // 32, "grouped sweep T=%d E=%d" % (T, E))
+    assert (y[ids < 0] == 0).all()
+
+
+def seeded_skewed_grouped_cases(count, seed=20261205):
+    """Random (T, top_k, E, K, N, hot, expert) with up to 256 experts where
+    each token's first slot goes to one expert with probability hot: experts
+    with many more than 64 routed rows (the split pieces), K down to 32."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        top_k = int(g.integers(1, 9))
+        E = int(g.integers(max(2, top_k), 257))
+        T = int(g.integers(20, 1500))
+        K = 32 * int(g.integers(1, 65))
+        N = int(g.integers(1, 300))
+        if T * top_k * N * K > 100_000_000 or T * top_k <= 128:
+            continue
+        out.append((T, top_k, E, K, N, float(g.choice([0.3, 0.7, 1.0])), int(g.integers(0, E))))
+    return out
+
+
+@pytest.mark.parametrize("T,top_k,E,K,N,hot,hot_e", seeded_skewed_grouped_cases(12))
+def test_grouped_w4a8_seeded_skewed_sweep(T, top_k, E, K, N, hot, hot_e):
+    """Seeded random skewed routings through the grouped GEMM (one expert
+    takes a share `hot` of the first slots), with a few invalid ids, against
+    the oracle."""
+    log("grouped skewed sweep T=%d top_k=%d E=%d K=%d N=%d hot=%.1f" % (T, top_k, E, K, N, hot))
+    g = np.random.default_rng(T * 1000 + E + K)
+    ids = W.topk_ids(T, top_k, E, seed=T + K)
+    ids[:, 0] = np.where(g.random(T) < hot, hot_e, ids[:, 0])
+    ids[g.integers(0, T), 0] = -1
+    qa = W.random_int8("moe", 716, (T, K), seed=T + N)
+    da = W.random_scales("moe", 717, (T, K // 32), seed=T + N)
+    packed, wsc = W.random_w4_codes(E, N, K, seed=E + K)
+    y = run_grouped(qa, da, ids, packed, wsc)
+    yr, asum = oracle.qgemm_w4a8_grouped(qa, da, ids, packed, wsc, nthreads=oracle_threads())
+    assert_within_bound(y, yr, asum, K // 32, "grouped skewed sweep T=%d E=%d" % (T, E))
     assert (y[ids < 0] == 0).all()
 
 
