@@ -119,26 +119,16 @@ __device__ __forceinline__ uint32_t q8_0_quantize4(const float (&v)[4], uint16_t
 constexpr int32_t MAGIC_BITS = 0x4B400000;
 constexpr float MAGIC_F = 12582912.0f;
 
-// Direct global -> LDS loads (gfx950 LDS DMA).  Lane L's 16 (or 4) bytes
-// land at lds_wave_base + 16 * L (4 * L); lds_wave_base must be wave-uniform
-// (it travels in M0).  The compiler counts these loads in vmcnt like any other
-// global load, so its own waits for register loads issued around them stay
-// exact, but it does not see their LDS writes: every kernel waits for them
-// explicitly (s_waitcnt vmcnt and a barrier) before any wave reads the
-// destination.
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void load_lds16(const void *gsrc, void *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void *)lds_wave_base, 16, 0, 0);
-}
-
-// The same loads issued through inline asm, invisible to the compiler: it
-// neither counts them in vmcnt nor sees their LDS writes.  A kernel whose
-// loop keeps several stages of such loads in flight uses these instead of the
-// builtin, because the compiler, seeing a builtin direct load, conservatively
-// waits for all of them (vmcnt(0)) before the next LDS read, which would drain
-// the pipeline every stage.  Every kernel that uses them waits for them
-// explicitly (wait_vmcnt and a barrier) before any wave reads the destination.
+// Direct global -> LDS loads (gfx950 LDS DMA), issued through inline asm:
+// lane L's 16 bytes land at lds_wave_base + 16 * L; lds_wave_base must be
+// wave-uniform (it travels in M0).  The compiler neither counts these loads
+// in vmcnt nor sees their LDS writes.  A kernel whose loop keeps several
+// stages of such loads in flight uses them instead of the compiler's
+// direct-load builtin, because the compiler, seeing a builtin direct load,
+// conservatively waits for all of them (vmcnt(0)) before the next LDS read,
+// which would drain the pipeline every stage.  Every kernel that uses them
+// waits for them explicitly (wait_vmcnt, and a barrier when another wave
+// reads the destination).
 // M0 carries the LDS base; the leading s_nop is the wait state GFX9 requires
 // between an SALU write of M0 and an LDS DMA that reads it (the compiler
 // places that write just before the asm and cannot see the DMA inside it).
@@ -150,22 +140,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void *generic_lds_ptr) {
 
 __device__ __forceinline__ void dma_lds16(const void *gsrc, void *lds_wave_base) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base)))
-               : "memory");
-}
-
-__device__ __forceinline__ void dma_lds4(const void *gsrc, void *lds_wave_base) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
-               :
-               : "v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base)))
-               : "memory");
-}
-
-// 2 bytes per lane, zero-extended: lane L's value lands in the 4-byte slot
-// lds_wave_base + 4 * L.
-__device__ __forceinline__ void dma_lds_u16(const void *gsrc, void *lds_wave_base) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_ushort %0, off"
                :
                : "v"(gsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base)))
                : "memory");
