@@ -385,6 +385,65 @@ def test_fused_quantize_qgemm_small_strided():
     assert torch.equal(y, bqi.qgemm_q8_0(q, d, qw_g, dw_g))
 
 
+def test_graph_replays_match_eager():
+    """The library's calls captured in one HIP graph (the fused decode step,
+    the MFMA GEMM, and the routing pass plus grouped W4A8 GEMM with split
+    pieces on a skewed routing), replayed three times with eager work between
+    the replays: every replay bit-identical to the eager results."""
+    log("graph replay: setup")
+    # fused decode step (one row) and the MFMA GEMM (48 rows)
+    k, n = 1024, 640
+    qw_g, dw_g, _, _ = check_quantize(W.weights("decode", n, k, seed=5), "graph W")
+    x = dev_tensor(W.activations("decode", 1, k, seed=6))
+    qa48, da48, _, _ = check_quantize(W.activations("decode", 48, k, seed=7), "graph A")
+    # grouped W4A8 on a skewed routing (expert 3 takes most first slots)
+    T, tk, E, K, N = 400, 4, 16, 512, 96
+    ids = skewed_ids(T, tk, E, 0.8, seed=8)
+    ids[ids == 0] = 3
+    ids[2, 1] = -1
+    qa, da = oracle.quantize_q8_0(W.activations("moe", T, K, seed=9))
+    packed, wsc = W.random_w4_codes(E, N, K, seed=10)
+    qa_g, da_g, ids_g, pk_g, ws_g = (dev_tensor(a) for a in (qa, da, ids, packed, wsc))
+    outs = {
+        "y1": torch.empty((1, n), device="cuda"),
+        "q1": torch.empty((1, k), dtype=torch.int8, device="cuda"),
+        "d1": torch.empty((1, k // 32), dtype=torch.int16, device="cuda"),
+        "y48": torch.empty((48, n), device="cuda"),
+        "yg": torch.empty((T, tk, N), device="cuda"),
+    }
+    work = torch.empty(bqi.workspace_size(T, tk, E, K), dtype=torch.uint8, device="cuda")
+
+    def calls():
+        bqi.quantize_qgemm_q8_0(x, qw_g, dw_g, outs["y1"], outs["q1"], outs["d1"])
+        bqi.qgemm_q8_0(qa48, da48, qw_g, dw_g, outs["y48"])
+        bqi.qgemm_w4a8_grouped(qa_g, da_g, ids_g, pk_g, ws_g, outs["yg"], work)
+
+    calls()
+    torch.cuda.synchronize()
+    ref = {name: t.clone() for name, t in outs.items()}
+    assert (ref["yg"][2, 1] == 0).all()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        calls()
+    for r in range(3):
+        # eager work between the replays: poison every output and the workspace
+        for t in outs.values():
+            t.fill_(float("nan") if t.is_floating_point() else 77)
+        work.fill_(0xA5)
+        torch.cuda.synchronize()
+        log("graph replay %d" % r)
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, t in outs.items():
+            assert torch.equal(t.view(torch.uint8), ref[name].view(torch.uint8)), "replay %d: %s" % (r, name)
+
+
 def seeded_fused_cases(count, seed=20261204):
     """Random (m, k, n, fp16 input, row padding) around the sizes that
     quantize_qgemm_q8_0 runs as one launch (m <= 16 with m * k <= 4096, and
