@@ -19,8 +19,12 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <unistd.h>
+
 #include <algorithm>
 #include <cmath>
+#include <condition_variable>
+#include <mutex>
 #include <thread>
 #include <vector>
 
@@ -113,6 +117,78 @@ __attribute__((target("avx2,fma"))) void run(const Job &J) {
   }
 }
 
+// Worker threads kept across calls: starting them anew in every call cost
+// about as much as a one-token decode step's work.  The pool starts on first
+// use and grows to the largest thread count asked for; one call at a time
+// uses it (concurrent callers wait on `call`), and the calling thread runs
+// job 0 itself.  Workers wait for a new generation, run their job if the
+// call has one for them, and count down `pending`.  The pool is never torn
+// down (its threads end with the process); a child made by fork() builds its
+// own, since the parent's workers do not exist there.
+struct Pool {
+  std::mutex call;
+  std::mutex m;
+  std::condition_variable go, done;
+  std::vector<std::thread> workers;
+  const Job *jobs = nullptr;
+  int n_jobs = 0, pending = 0;
+  uint64_t gen = 0;
+  pid_t pid = getpid();
+
+  void work(int i) {  // worker i runs job i (i >= 1)
+    uint64_t seen = 0;
+    for (;;) {
+      const Job *job = nullptr;
+      {
+        std::unique_lock<std::mutex> l(m);
+        go.wait(l, [&] { return gen != seen; });
+        seen = gen;
+        if (i < n_jobs) job = &jobs[i];
+      }
+      if (!job) continue;
+      run(*job);
+      std::lock_guard<std::mutex> l(m);
+      if (--pending == 0) done.notify_one();
+    }
+  }
+
+  // Runs jobs 0 .. n-1; jobs that no worker can take (a thread could not be
+  // started) run on the calling thread after job 0.
+  void run_all(const Job *js, int n) {
+    std::lock_guard<std::mutex> c(call);
+    try {
+      while ((int)workers.size() < n - 1) {
+        const int i = (int)workers.size() + 1;
+        workers.emplace_back([this, i] { work(i); });
+      }
+    } catch (...) {
+      // no more threads: the calling thread takes the rest
+    }
+    const int shared = std::min(n, (int)workers.size() + 1);
+    {
+      std::lock_guard<std::mutex> l(m);
+      jobs = js;
+      n_jobs = shared;
+      pending = shared - 1;
+      ++gen;
+    }
+    go.notify_all();
+    run(js[0]);
+    for (int i = shared; i < n; ++i) run(js[i]);
+    std::unique_lock<std::mutex> l(m);
+    done.wait(l, [&] { return pending == 0; });
+    jobs = nullptr;
+  }
+};
+
+Pool *pool_for_this_process() {
+  static std::mutex guard;
+  static Pool *pool = nullptr;
+  std::lock_guard<std::mutex> l(guard);
+  if (!pool || pool->pid != getpid()) pool = new Pool;  // (a forked child's copy is left alone)
+  return pool;
+}
+
 }  // namespace
 
 extern "C" {
@@ -145,15 +221,15 @@ BQI_API int qgemm_w4a8_grouped_host(const int8_t *aq, const uint16_t *ad,
   const int64_t col_chunk = 64;
   const int64_t items = R * ((n + col_chunk - 1) / col_chunk);
   if (nthreads > items) nthreads = (int)items;
-  std::vector<std::thread> pool;
   std::vector<Job> jobs((size_t)nthreads);
   for (int i = 0; i < nthreads; ++i)
     jobs[(size_t)i] = Job{aq, ad, topk_ids, top_k, wq4, wd, n_experts, n, k, y,
                           asum.data(), items * i / nthreads, items * (i + 1) / nthreads,
                           col_chunk};
-  for (int i = 1; i < nthreads; ++i) pool.emplace_back(run, std::cref(jobs[(size_t)i]));
-  run(jobs[0]);
-  for (auto &th : pool) th.join();
+  if (nthreads == 1)
+    run(jobs[0]);
+  else
+    pool_for_this_process()->run_all(jobs.data(), nthreads);
   return BQI_OK;
 }
 

@@ -288,9 +288,12 @@ BQI_API int gguf_q4_0_to_planar(const void *blocks, int64_t rows, int64_t k,
  * HOST pointers, same layouts and the same function as qgemm_w4a8_grouped
  * (ids outside [0, n_experts) give zero rows), within the same bound.  Runs
  * synchronously on `nthreads` threads (<= 0: all hardware threads); the
- * result does not depend on the thread count.  This is a separate entry
- * point for data in host memory, never a substitute for the GPU path.
- * Returns BQI_ENOTSUP on a CPU without AVX2 and FMA.
+ * result does not depend on the thread count.  The calling thread takes a
+ * share itself; the others are worker threads that the library starts on
+ * first use and keeps for the rest of the process (calls from several host
+ * threads at once take turns).  This is a separate entry point for data in
+ * host memory, never a substitute for the GPU path.  Returns BQI_ENOTSUP on
+ * a CPU without AVX2 and FMA.
  */
 BQI_API int qgemm_w4a8_grouped_host(const int8_t *aq, const uint16_t *ad,
                             int64_t n_tokens, const int32_t *topk_ids,
