@@ -38,7 +38,11 @@
  *    arrays 2-byte aligned; fp32 outputs 4-byte aligned.
  *  - Results are deterministic: the same inputs give bit-identical outputs
  *    (no atomics in any floating-point reduction).
- *  - The library keeps no state between calls; calls are thread-safe.
+ *  - Calls are thread-safe, except overlapping calls of
+ *    qgemm_w4a8_grouped_noalloc on one GPU (they share its workspace array).
+ *    State kept between calls: that array, the worker threads of
+ *    qgemm_w4a8_grouped_host, and kernel attributes (larger LDS limits) set
+ *    once per device; none of it changes a result.
  */
 #ifndef BQI_H
 #define BQI_H
