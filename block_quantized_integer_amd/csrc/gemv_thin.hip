@@ -578,6 +578,10 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
   // stored); the launch gives the workgroup MF_FUSED_GROUPS waves, so QR
   // rounds cover m * k <= MF_FUSED_ELEMS
   constexpr int QR = SRC == ACT_Q8 ? 1 : MF_FUSED_ELEMS / 256 / MF_FUSED_GROUPS;
+  // c / pb as (c * pb_inv) >> 16: exact for every c < 1024 and pb <= 32
+  // (checked exhaustively); c stays below 8 QR MF_FUSED_GROUPS = 128
+  static_assert(8 * QR * MF_FUSED_GROUPS <= 1024, "block index range of the reciprocal");
+  const uint32_t pb_inv = (65536u + (uint32_t)pb - 1) / (uint32_t)pb;
   float xv[QR][4];
   uint16_t h[8];
   if constexpr (SRC == ACT_Q8) {
@@ -595,7 +599,8 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
   } else {
 #pragma unroll
     for (int u = 0; u < QR; ++u) {
-      const int c = 8 * (u * nwaves + wave) + (lane >> 3), i = c / pb, b = c - i * pb;
+      const int c = 8 * (u * nwaves + wave) + (lane >> 3);
+      const int i = (int)(((uint32_t)c * pb_inv) >> 16), b = c - i * pb;
       const int64_t off = i < m ? (int64_t)i * ldx + QK * (pb0 + b) + 4 * (lane & 7) : 0;
       if constexpr (SRC == ACT_F32) {
         const f32x4 r = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(x) + off);
@@ -661,7 +666,8 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
     const bool out = blockIdx.x == 0;
 #pragma unroll
     for (int u = 0; u < QR; ++u) {
-      const int c = 8 * (u * nwaves + wave) + (lane >> 3), i = c / pb, b = c - i * pb, sub = lane & 7;
+      const int c = 8 * (u * nwaves + wave) + (lane >> 3), sub = lane & 7;
+      const int i = (int)(((uint32_t)c * pb_inv) >> 16), b = c - i * pb;
       uint16_t dbits;
       const uint32_t packed = q8_0_quantize4(xv[u], dbits);  // every lane (DPP inside)
       if (i < m) {
