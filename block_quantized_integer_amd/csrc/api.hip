@@ -42,12 +42,30 @@ WsLayout ws_layout(int64_t rows_total, int64_t n_experts, int64_t k) {
   return L;
 }
 
-// Launch of a validated Q8_0 GEMM: the thin-M kernel for m <= 16, the MFMA
-// kernel otherwise.
+// 16 < m <= 128: the MFMA GEMM runs one 128-row tile per column tile, so its
+// time hardly depends on m there (about 4 + 13.1 k / 1024 us per round of 256
+// tiles on MI355X), while the thin-M MFMA kernel takes the rows in chunks of
+// 16 and reads the weights once per chunk (at most about 4 us plus the
+// chunks' weight bytes at 4.5 TB/s).  The chunks run where that estimate is
+// lower.  Measured over k = 256 .. 5120 and n = 512 .. 17408: 1.7-5.1x
+// faster where they run (27.7 -> 5.4 us at m = 17, k = 2048, n = 768), never
+// slower; weight-heavy shapes keep the GEMM from 64-80 rows up.
+bool thin_chunks_faster(int64_t m, int64_t n, int64_t k, const uint16_t *wd) {
+  if (m <= 16 || m > 128 || !bqi::gemv_thin_chunks_ok(m, n, k, wd)) return false;
+  const double chunks = (double)((m + 15) / 16);
+  const double weight_bytes = (double)n * (double)k * (1.0 + 1.0 / 16.0);
+  const double rounds = (double)(((n + 127) / 128 + 255) / 256);
+  const double t_gemm = 4.0 + 13.1 * (double)k / 1024.0 * rounds;
+  const double t_chunks = 4.0 + chunks * weight_bytes / 4.5e6;
+  return t_chunks < t_gemm;
+}
+
+// Launch of a validated Q8_0 GEMM: the thin-M kernels for m <= 16 (and in
+// chunks of 16 rows where that is faster), the MFMA GEMM otherwise.
 int qgemm_launch(const int8_t *aq, const uint16_t *ad, int64_t m,
                  const int8_t *wq, const uint16_t *wd, int64_t n, int64_t k,
                  float *y, hipStream_t s) {
-  if (m <= 16)
+  if (m <= 16 || thin_chunks_faster(m, n, k, wd))
     return hip_status(bqi::launch_gemv_thin(aq, ad, m, wq, wd, n, k, y, s));
   return hip_status(bqi::launch_gemm_mfma(aq, ad, m, wq, wd, n, k, y, s));
 }

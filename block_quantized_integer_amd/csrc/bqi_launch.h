@@ -30,7 +30,9 @@ hipError_t launch_quantize_q8_0(const void *x, bool f16, int64_t rows,
 
 hipError_t launch_zero_f32(float *y, int64_t count, hipStream_t stream);
 
-// thin-M (m <= 16) Q8_0 GEMM/GEMV
+// thin-M Q8_0 GEMM/GEMV: m <= 16, or more rows in chunks of 16 where
+// gemv_thin_chunks_ok (the MFMA thin-M kernel)
+bool gemv_thin_chunks_ok(int64_t m, int64_t n, int64_t k, const uint16_t *wd);
 hipError_t launch_gemv_thin(const int8_t *aq, const uint16_t *ad, int64_t m,
                             const int8_t *wq, const uint16_t *wd, int64_t n,
                             int64_t k, float *y, hipStream_t stream);

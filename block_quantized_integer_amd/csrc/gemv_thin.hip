@@ -25,7 +25,8 @@
 //
 // k_gemv_mfma16 (4 < m <= 16 with k a multiple of 64 whose stages fit LDS):
 // the same streaming loads, turned into int8 MFMA operands in registers; one
-// MFMA per block replaces the m rows of dot4 work.
+// MFMA per block replaces the m rows of dot4 work.  It also takes up to a few
+// hundred rows as chunks of 16, one workgroup per (chunk, weight-row slot).
 //
 // k_gemv_lds (the rest of m <= 16: longer rows): the m activation rows of the
 // current K chunk sit in LDS; a group of LPR lanes shares one weight row and each lane
@@ -538,11 +539,14 @@ __device__ __forceinline__ long mf_pair(uint32_t lo, uint32_t hi) {
 constexpr int MF_FUSED_ELEMS = 4096;
 constexpr int MF_FUSED_GROUPS = 4;
 
-template <int RG, int SRC>
+// CHUNKED: more than 16 rows of Q8_0 codes, taken in chunks (the weights load
+// with the default cache policy, since the other chunks read them again;
+// one chunk streams them past the caches)
+template <int RG, int SRC, bool CHUNKED>
 __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
     const int8_t *aq, const uint16_t *ad, const void *x, int ldx, int m,
     const int8_t *wq, const uint16_t *wd, int n, int k, int ks, float *y,
-    int8_t *q_out, uint16_t *d_out) {
+    int8_t *q_out, uint16_t *d_out, int chunks, int xcd_group) {
   // weight load pairs in flight per wave: MF_DEPTH for RG = 1 (12 waves per
   // CU); two whole chunks (six pairs) for RG = 3, one wave per SIMD
   // (measured: four pairs, which split a chunk, 14.1 us at m = 16; six 11.9;
@@ -552,6 +556,31 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
   extern __shared__ __attribute__((aligned(16))) int8_t mf_lds[];
   const int nbk = k / QK;
   const int lda = (int)mf_lda(k);
+  // CHUNKED: chunks of 16 rows; each chunk is the m <= 16 computation of its
+  // rows.  The chunks that read the same weight rows (one slot) are
+  // dispatched side by side.  With xcd_group they also share an XCD (and
+  // its L2): workgroups are dealt to the 8 XCDs in turn, so blockIdx b runs
+  // on XCD b % 8 and takes chunk (b / 8) % chunks of slot
+  // 8 (b / 8 / chunks) + b % 8 (the grid is padded to a multiple of 8 slots;
+  // a padding slot's workgroups return at once).  Without it, blockIdx b
+  // takes chunk b % chunks of slot b / chunks.
+  int wg = (int)blockIdx.x;
+  if constexpr (CHUNKED) {
+    int chunk;
+    if (xcd_group) {  // uniform
+      const int idx = wg >> 3;
+      chunk = idx % chunks;
+      wg = (idx / chunks) * 8 + (wg & 7);
+      if ((int64_t)wg * (((int)blockDim.x >> 6) / ks) * 16 * RG >= n) return;
+    } else {
+      chunk = wg % chunks;
+      wg /= chunks;
+    }
+    aq += (int64_t)chunk * 16 * k;
+    ad += (int64_t)chunk * 16 * nbk;
+    y += (int64_t)chunk * 16 * n;
+    m = min(16, m - 16 * chunk);
+  }
   int8_t *sA = mf_lds;                                        // [16][lda], rows < m
   float *sD = reinterpret_cast<float *>(mf_lds + 16 * lda);   // [nbk + 32][16], rows < m
   const int nthreads = (int)blockDim.x;
@@ -562,7 +591,7 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
   int8_t *slotD = mf_lds + 16 * lda + (nbk + 32) * 64 + wave * (RG * MF_SLOT);  // [16 RG][MF_DSTRIDE]
   const int grp = wave / ks, part = wave - grp * ks;
   const int l16 = lane & 15, g = lane >> 4;
-  const int n0 = ((int)blockIdx.x * groups + grp) * 16 * RG;
+  const int n0 = (wg * groups + grp) * 16 * RG;
   const int pb0 = 32 * part;              // first block of this K part
   const int pb = min(32, nbk - pb0);      // blocks in it (even: k % 64 == 0)
 
@@ -646,8 +675,13 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
   auto load_pair = [&](int q) {
     const int p = q / RG, j = q % RG;
     const int off = min(woff + 128 * p, k - 16);
-    w[q][0] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(wr[j][0] + off));
-    w[q][1] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(wr[j][1] + off));
+    if constexpr (CHUNKED) {
+      w[q][0] = *reinterpret_cast<const i32x4 *>(wr[j][0] + off);
+      w[q][1] = *reinterpret_cast<const i32x4 *>(wr[j][1] + off);
+    } else {
+      w[q][0] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(wr[j][0] + off));
+      w[q][1] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(wr[j][1] + off));
+    }
   };
 #pragma unroll
   for (int q = 0; q < DEPTH; ++q) load_pair(q);
@@ -663,7 +697,7 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma16(
       if (i < m) sD[(pb0 + b) * 16 + i] = b < pb ? half_bits_to_float(h[u]) : 0.0f;
     }
   } else {
-    const bool out = blockIdx.x == 0;
+    const bool out = blockIdx.x == 0;  // (fused sources come in one chunk)
 #pragma unroll
     for (int u = 0; u < QR; ++u) {
       const int c = 8 * (u * nwaves + wave) + (lane >> 3), sub = lane & 7;
@@ -839,7 +873,13 @@ bool mf_shape(int64_t n, int64_t k, MfShape *out) {
   return true;
 }
 
-template <int RG, int SRC>
+// weights of at least this many bytes: the chunks of one weight-row slot
+// share an XCD, so that the later ones find the weights in that XCD's L2
+// (measured: 8-20% faster from 8 MB of weights up, 0.1-0.2 us slower at
+// 1.6 MB and below, where one slot's weights hardly fill the L2's queues)
+constexpr int64_t MF_XCD_GROUP_BYTES = 4 << 20;
+
+template <int RG, int SRC, bool CHUNKED>
 hipError_t launch_mfma16_rg(const int8_t *aq, const uint16_t *ad, const void *x, int64_t ldx,
                             int64_t m, const int8_t *wq, const uint16_t *wd, int64_t n,
                             int64_t k, const MfShape &sh, float *y, int8_t *q_out,
@@ -848,14 +888,18 @@ hipError_t launch_mfma16_rg(const int8_t *aq, const uint16_t *ad, const void *x,
   const int64_t lds = mf_lds_bytes(k, (int64_t)sh.ks * sh.groups * RG);
   static bool raised[64];
   if (lds > 65536) {
-    const hipError_t e = raise_dynamic_lds((const void *)k_gemv_mfma16<RG, SRC>, (int)MF_LDS_MAX, raised);
+    const hipError_t e = raise_dynamic_lds((const void *)k_gemv_mfma16<RG, SRC, CHUNKED>, (int)MF_LDS_MAX, raised);
     if (e != hipSuccess) return e;
   }
   const int64_t rows_per_wg = 16 * RG * sh.groups;
   const int64_t wgs = (n + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL((k_gemv_mfma16<RG, SRC>), dim3((unsigned)wgs), dim3(64 * sh.ks * sh.groups),
-                     (unsigned)lds, stream, aq, ad, x, (int)ldx, (int)m, wq, wd, (int)n, (int)k,
-                     sh.ks, y, q_out, d_out);
+  const int64_t chunks = (m + 15) / 16;
+  const bool xcd_group = CHUNKED && n * k >= MF_XCD_GROUP_BYTES;
+  const int64_t grid = xcd_group ? (wgs + 7) / 8 * 8 * chunks : wgs * chunks;
+  hipLaunchKernelGGL((k_gemv_mfma16<RG, SRC, CHUNKED>), dim3((unsigned)grid),
+                     dim3(64 * sh.ks * sh.groups), (unsigned)lds, stream, aq, ad, x, (int)ldx,
+                     (int)m, wq, wd, (int)n, (int)k, sh.ks, y, q_out, d_out, (int)chunks,
+                     (int)xcd_group);
   return hipGetLastError();
 }
 
@@ -863,8 +907,10 @@ hipError_t launch_mfma16(const int8_t *aq, const uint16_t *ad, int64_t m,
                          const int8_t *wq, const uint16_t *wd, int64_t n, int64_t k,
                          const MfShape &sh, float *y, hipStream_t stream) {
   if (sh.rg == 3)
-    return launch_mfma16_rg<3, ACT_Q8>(aq, ad, nullptr, 0, m, wq, wd, n, k, sh, y, nullptr, nullptr, stream);
-  return launch_mfma16_rg<1, ACT_Q8>(aq, ad, nullptr, 0, m, wq, wd, n, k, sh, y, nullptr, nullptr, stream);
+    return m > 16 ? launch_mfma16_rg<3, ACT_Q8, true>(aq, ad, nullptr, 0, m, wq, wd, n, k, sh, y, nullptr, nullptr, stream)
+                  : launch_mfma16_rg<3, ACT_Q8, false>(aq, ad, nullptr, 0, m, wq, wd, n, k, sh, y, nullptr, nullptr, stream);
+  return m > 16 ? launch_mfma16_rg<1, ACT_Q8, true>(aq, ad, nullptr, 0, m, wq, wd, n, k, sh, y, nullptr, nullptr, stream)
+                : launch_mfma16_rg<1, ACT_Q8, false>(aq, ad, nullptr, 0, m, wq, wd, n, k, sh, y, nullptr, nullptr, stream);
 }
 }  // namespace
 
@@ -884,12 +930,18 @@ ThinPath thin_path(int64_t m, int64_t n, int64_t k, const uint16_t *wd, MfShape 
 }
 }  // namespace
 
+bool gemv_thin_chunks_ok(int64_t m, int64_t n, int64_t k, const uint16_t *wd) {
+  MfShape sh;
+  return m > 16 && thin_path(m, n, k, wd, &sh) == ThinPath::MFMA16;
+}
+
 hipError_t launch_gemv_thin(const int8_t *aq, const uint16_t *ad, int64_t m,
                             const int8_t *wq, const uint16_t *wd, int64_t n,
                             int64_t k, float *y, hipStream_t stream) {
   MfShape sh;
   const ThinPath path = thin_path(m, n, k, wd, &sh);
   if (path == ThinPath::MFMA16) return launch_mfma16(aq, ad, m, wq, wd, n, k, sh, y, stream);
+  if (m > 16) return hipErrorInvalidValue;  // only the MFMA kernel takes row chunks
   const int64_t mt = pow2_ceil(m);
   if (path == ThinPath::REG) {
     switch (mt) {
@@ -939,8 +991,8 @@ hipError_t launch_gemv_fused(const void *x, bool f16, int64_t ldx, int64_t m,
     // quantization (the workgroup shape does not change any result)
     // (waves past the last row group compute clamped rows and store nothing)
     sh.groups = MF_FUSED_GROUPS;
-    return f16 ? launch_mfma16_rg<1, ACT_F16>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, sh, y, q_out, d_out, stream)
-               : launch_mfma16_rg<1, ACT_F32>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, sh, y, q_out, d_out, stream);
+    return f16 ? launch_mfma16_rg<1, ACT_F16, false>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, sh, y, q_out, d_out, stream)
+               : launch_mfma16_rg<1, ACT_F32, false>(nullptr, nullptr, x, ldx, m, wq, wd, n, k, sh, y, q_out, d_out, stream);
   }
   switch (pow2_ceil(m)) {
     case 1:

@@ -121,7 +121,11 @@ BQI_API int quantize_q8_0(const void *x, int x_dtype, int64_t rows, int64_t k,
  * passing through at most nb = k/32 additions, so
  * |y - exact| <= (nb + 1) * 2^-24 * sum_b |term_b|  (below 1e-5 * sum|terms|
  * for k <= 5312).
- * m <= 16 runs the thin-M (decode) kernel, larger m the MFMA (prefill) kernel.
+ * m <= 16 runs the thin-M (decode) kernel, larger m the MFMA (prefill)
+ * kernel, except that 16 < m <= 128 runs the thin-M MFMA kernel in chunks of
+ * 16 rows where an estimate of both times (from m, n and k alone) favours
+ * it; each chunk of at least 5 rows then comes out bit-identical to a call
+ * on its rows alone.
  *
  * Requirements: k % 32 == 0; aq, wq 16-byte aligned; y 4-byte aligned.
  */

@@ -207,8 +207,10 @@ def test_qgemm_random_codes_full_range(m, k, n):
 
 def seeded_shapes(count, seed=20261202):
     """Random (m, k, n) spread over every dispatch path: 1-4 rows (v_dot4),
-    5-16 (thin-M MFMA), 17-300 (MFMA GEMM), k a multiple of 32 up to 8192,
-    n up to 3000; m * n * k capped so the oracle stays quick."""
+    5-16 (thin-M MFMA), 17-300 (MFMA GEMM, or up to 128 rows the thin-M
+    MFMA kernel in chunks of 16 where that is estimated faster), k a
+    multiple of 32 up to 8192, n up to 3000; m * n * k capped so the oracle
+    stays quick."""
     g = np.random.default_rng(seed)
     out = []
     while len(out) < count:
@@ -239,7 +241,8 @@ def test_qgemm_seeded_shape_sweep(m, k, n):
     (1, 96), (2, 96), (3, 96), (4, 96),   # k_gemv_reg, one to four rows
     (4, 12288),                           # k_gemv_reg at the decode width
     (5, 96), (16, 96), (8, 12288), (16, 12288),  # k_gemv_mfma16, one and three row groups per wave
-    (40, 96), (128, 96),                  # k_gemm_mfma_w8 (at most one tile per CU)
+    (40, 96), (128, 96), (17, 12288),     # k_gemv_mfma16 in 16-row chunks
+    (128, 12288),                         # k_gemm_mfma_w8 (96 tiles: at most one per CU)
     (2304, 2048)])                        # k_gemm_mfma: 288 tiles, more than one per CU
 def test_block_dots_bitexact_probe(m, n):
     """One-hot-block probe: each activation row has codes only in block
@@ -348,7 +351,8 @@ def test_decode_workload_full(decode_weights, m):
     (5, 768, 130, "f32"),       # fused: MFMA thin-M kernel, 5 of 16 rows, 24 blocks
     (16, 192, 70, "f32"),       # fused: MFMA thin-M kernel, 6 blocks (a chunk partly past k)
     (16, 4096, 512, "f32"),     # not fused: quantize + thin-M GEMM (m = 16)
-    (40, 256, 130, "f16"),      # not fused: quantize + MFMA GEMM
+    (40, 256, 130, "f16"),      # not fused: quantize + thin-M MFMA kernel in 16-row chunks
+    (200, 512, 96, "f32"),      # not fused: quantize + MFMA GEMM
 ])
 def test_fused_quantize_qgemm(decode_weights, m, k, n, dtype):
     """quantize_qgemm_q8_0: codes and scales bit-exact to the oracle's
@@ -387,15 +391,18 @@ def test_fused_quantize_qgemm_small_strided():
 
 def test_graph_replays_match_eager():
     """The library's calls captured in one HIP graph (the fused decode step,
-    the MFMA GEMM, and the routing pass plus grouped W4A8 GEMM with split
+    the thin-M kernel in 16-row chunks, the MFMA GEMM, and the routing pass
+    plus grouped W4A8 GEMM with split
     pieces on a skewed routing), replayed three times with eager work between
     the replays: every replay bit-identical to the eager results."""
     log("graph replay: setup")
-    # fused decode step (one row) and the MFMA GEMM (48 rows)
+    # fused decode step (one row), 48 rows (three 16-row chunks of the thin-M
+    # kernel) and 200 rows (the MFMA GEMM)
     k, n = 1024, 640
     qw_g, dw_g, _, _ = check_quantize(W.weights("decode", n, k, seed=5), "graph W")
     x = dev_tensor(W.activations("decode", 1, k, seed=6))
     qa48, da48, _, _ = check_quantize(W.activations("decode", 48, k, seed=7), "graph A")
+    qa200, da200, _, _ = check_quantize(W.activations("decode", 200, k, seed=11), "graph A200")
     # grouped W4A8 on a skewed routing (expert 3 takes most first slots)
     T, tk, E, K, N = 400, 4, 16, 512, 96
     ids = skewed_ids(T, tk, E, 0.8, seed=8)
@@ -409,6 +416,7 @@ def test_graph_replays_match_eager():
         "q1": torch.empty((1, k), dtype=torch.int8, device="cuda"),
         "d1": torch.empty((1, k // 32), dtype=torch.int16, device="cuda"),
         "y48": torch.empty((48, n), device="cuda"),
+        "y200": torch.empty((200, n), device="cuda"),
         "yg": torch.empty((T, tk, N), device="cuda"),
     }
     work = torch.empty(bqi.workspace_size(T, tk, E, K), dtype=torch.uint8, device="cuda")
@@ -416,6 +424,7 @@ def test_graph_replays_match_eager():
     def calls():
         bqi.quantize_qgemm_q8_0(x, qw_g, dw_g, outs["y1"], outs["q1"], outs["d1"])
         bqi.qgemm_q8_0(qa48, da48, qw_g, dw_g, outs["y48"])
+        bqi.qgemm_q8_0(qa200, da200, qw_g, dw_g, outs["y200"])
         bqi.qgemm_w4a8_grouped(qa_g, da_g, ids_g, pk_g, ws_g, outs["yg"], work)
 
     calls()
@@ -550,6 +559,36 @@ def test_qgemm_ragged_more_tiles_than_slots(k):
     assert_within_bound(y, yr, asum, k // 32, "ragged")
     y2 = run_gemm(aq, ad, wq, wd)
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+# (m, k, n) that qgemm_q8_0 runs on the thin-M MFMA kernel in chunks of 16
+# rows: ragged last chunks of 1, 4, 5 and 15 rows, one to five K parts, one and
+# three row groups per wave (n >= 12288), ragged n
+CHUNKED = [(17, 768, 2048), (33, 1024, 300), (34, 2048, 3000), (100, 512, 513),
+           (128, 256, 96), (48, 5120, 640), (127, 4096, 1000), (50, 256, 12290),
+           (21, 1088, 700), (20, 5120, 5120)]
+
+
+@pytest.mark.parametrize("m,k,n", CHUNKED)
+def test_qgemm_thin_row_chunks(m, k, n):
+    """More than 16 rows on the thin-M MFMA kernel, 16 rows per chunk: every
+    output within the bound of the oracle's exact value, and each chunk of 5
+    or more rows bit-identical to the same rows given alone (a chunk is the
+    16-row computation of its rows; a chunk of at most 4 rows alone would take
+    the register kernel, which sums in another order)."""
+    log("qgemm row chunks m=%d k=%d n=%d" % (m, k, n))
+    aq = W.random_int8(0, 530 + m, (m, k), seed=n)
+    wq = W.random_int8(0, 531, (n, k), seed=k)
+    ad = W.random_scales(0, 532, (m, k // 32), seed=m)
+    wd = W.random_scales(0, 533, (n, k // 32), seed=n + k)
+    y = run_gemm(aq, ad, wq, wd)
+    yr, asum = oracle.qgemm_q8_0(aq, ad, wq, wd, nthreads=oracle_threads())
+    assert_within_bound(y, yr, asum, k // 32, "chunks m=%d k=%d n=%d" % (m, k, n))
+    for r0 in range(0, m, 16):
+        r1 = min(m, r0 + 16)
+        if r1 - r0 >= 5:
+            yc = run_gemm(aq[r0:r1], ad[r0:r1], wq, wd)
+            assert np.array_equal(y[r0:r1].view(np.uint32), yc.view(np.uint32)), "chunk %d" % r0
 
 
 SPECIAL_SCALES = np.array([0x0000, 0x8000, 0x0001, 0x0002, 0x0155, 0x03FF, 0x0400, 0x8001,
