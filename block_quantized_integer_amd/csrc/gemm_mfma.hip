@@ -10,8 +10,16 @@
 // LDS buffers.  The operand tiles travel HBM -> LDS with gfx950's direct
 // loads (global_load_lds_dwordx4: each wave instruction fills 1 KB of LDS, 16
 // bytes per lane), so they occupy no registers and need no LDS stores; lane L
-// fetches the global chunk that the XOR swizzle assigns to LDS slot L.  Only
-// the scales pass through registers, where they are converted to fp32 once.
+// fetches the global chunk that the XOR swizzle assigns to LDS slot L.  The
+// fp16 scales are converted to fp32 once, on their way into the stage's LDS
+// scale arrays.  When k is a multiple of 256 and both scale arrays are 16-byte
+// aligned (PAIRED), each row's scales for two stages (16 bytes) arrive in LDS
+// with one direct load per lane, four such wave loads per workgroup every
+// other stage, and the lane that loaded a row converts it; otherwise every
+// thread loads 2-byte scales into registers each stage.  Both give the same
+// LDS contents.  The load instructions, not their bytes, are what a CU takes
+// slowly (one 64-lane load per ~32-38 cycles), so the paired path's 2 scale
+// loads per stage instead of 16 make the GEMM ~4% faster.
 // The loads of stage s+1 are in flight while stage s computes.
 //
 // Scale epilogue (per 32x32 tile and block), two fp32 FMAs per output:
@@ -93,11 +101,15 @@ __device__ __forceinline__ void tile_origin(int tiles_m, int tiles_n, int &m0, i
   n0 = (in_group / gm) * BN;
 }
 
+template <bool PAIRED>
 __global__ __launch_bounds__(THREADS, 2) void k_gemm_mfma(
     const int8_t *__restrict__ aq, const uint16_t *__restrict__ ad, int m,
     const int8_t *__restrict__ wq, const uint16_t *__restrict__ wd, int n,
     int k, float *__restrict__ y, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) Tiles T[2];
+  // PAIRED: the fp16 scales of a pair of stages (2 NBS blocks per row) as
+  // loaded: [operand][row][block], the A tile's rows, then the W tile's
+  __shared__ __attribute__((aligned(16))) uint16_t raw[PAIRED ? 2 * BM * 2 * NBS : 8];
 
   int m0, n0;
   tile_origin(tiles_m, tiles_n, m0, n0);
@@ -169,8 +181,38 @@ __global__ __launch_bounds__(THREADS, 2) void k_gemm_mfma(
         ao += fix;
         wo += fix;
       }
-      sa_reg[h] = sabase[(uint32_t)ao];
-      sw_reg[h] = swbase[(uint32_t)wo];
+      if constexpr (!PAIRED) {
+        sa_reg[h] = sabase[(uint32_t)ao];
+        sw_reg[h] = swbase[(uint32_t)wo];
+      }
+    }
+  };
+  // PAIRED: wave w < 2 loads the scales of A tile rows 64 w .. +63, wave
+  // w >= 2 those of W tile rows 64 (w - 2) .. +63 (rows past m or n re-read
+  // the last one), 16 bytes (a pair of stages) per lane; the lane converts
+  // its row's four scales of each stage itself, after its own wait, so no
+  // other barrier is needed.  Pair p is loaded at the start of stage 2p - 1,
+  // after the end of stage 2p - 2 read the previous pair for the last time.
+  const bool sc_a = wave_u < 2;
+  const int sc_row = 64 * (wave_u & 1) + lane;
+  const int sc_goff = 2 * ((sc_a ? min(m0 + sc_row, m - 1) : min(n0 + sc_row, n - 1)) * nbk);
+  const uint16_t *sc_base = sc_a ? ad : wd;
+  uint16_t *sc_raw = &raw[PAIRED ? (sc_a ? 0 : BM * 2 * NBS) : 0];
+  auto issue_raw = [&](int pair) {
+    const uint32_t lds = lds_addr(sc_raw + 2 * NBS * 64 * (wave_u & 1));
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(sc_goff + 4 * NBS * pair), "s"(sc_base), "{m0}"(lds) : "memory");
+  };
+  auto convert_raw = [&](int s, int buf) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(sc_raw + 2 * NBS * sc_row + NBS * (s & 1));
+    const float f0 = half_bits_to_float((uint16_t)(v.x & 0xffffu)), f1 = half_bits_to_float((uint16_t)(v.x >> 16));
+    const float f2 = half_bits_to_float((uint16_t)(v.y & 0xffffu)), f3 = half_bits_to_float((uint16_t)(v.y >> 16));
+    if (sc_a) {
+      T[buf].ad[0][sc_row] = f0;
+      T[buf].ad[1][sc_row] = f1;
+      T[buf].ad[2][sc_row] = f2;
+      T[buf].ad[3][sc_row] = f3;
+    } else {
+      *reinterpret_cast<f32x4 *>(&T[buf].wd[sc_row][0]) = f32x4{f0, f1, f2, f3};
     }
   };
   // Blocks past k (a short last stage) get activation scale 0: the stage
@@ -206,15 +248,20 @@ __global__ __launch_bounds__(THREADS, 2) void k_gemm_mfma(
     else
       issue_stage(s, buf, std::false_type{});
   };
+  if constexpr (PAIRED) issue_raw(0);
   issue(0, 0);
-  store_scales(0, 0);
+  if constexpr (!PAIRED) store_scales(0, 0);
   wait_vmcnt<0>();  // direct loads of stage 0 have landed
+  if constexpr (PAIRED) convert_raw(0, 0);
   __syncthreads();
 
   for (int s = 0; s < stages; ++s) {
     const int buf = s & 1;
     const Tiles &TB = T[buf];
     if (s + 1 < stages) issue(s + 1, buf ^ 1);
+    if constexpr (PAIRED) {
+      if ((s & 1) && s + 1 < stages) issue_raw((s + 1) >> 1);
+    }
 
     // The stage's 16 MFMAs (4 blocks x 2x2 tiles) run as a pipeline of depth
     // one: tile u's MFMA is issued before tile u-1's epilogue, into the other
@@ -313,8 +360,13 @@ __global__ __launch_bounds__(THREADS, 2) void k_gemm_mfma(
     }
     epilogue(dres[(4 * NBS - 1) & 1], 4 * NBS - 1);
 
-    if (s + 1 < stages) store_scales(s + 1, buf ^ 1);
+    if constexpr (!PAIRED) {
+      if (s + 1 < stages) store_scales(s + 1, buf ^ 1);
+    }
     wait_vmcnt<0>();  // this wave's direct loads have landed
+    if constexpr (PAIRED) {
+      if (s + 1 < stages) convert_raw(s + 1, buf ^ 1);
+    }
     __syncthreads();
   }
 
@@ -530,9 +582,15 @@ hipError_t launch_gemm_mfma(const int8_t *aq, const uint16_t *ad, int64_t m,
                        aq, ad, (int)m, wq, wd, (int)n, (int)k, y, tiles_m, tiles_n);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_gemm_mfma, dim3((unsigned)tiles), dim3(THREADS),
-                     0, stream, aq, ad, (int)m, wq, wd, (int)n, (int)k, y,
-                     tiles_m, tiles_n);
+  const bool paired = (k / QK) % (2 * NBS) == 0 && ((uintptr_t)ad & 15) == 0 && ((uintptr_t)wd & 15) == 0;
+  if (paired)
+    hipLaunchKernelGGL(k_gemm_mfma<true>, dim3((unsigned)tiles), dim3(THREADS),
+                       0, stream, aq, ad, (int)m, wq, wd, (int)n, (int)k, y,
+                       tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL(k_gemm_mfma<false>, dim3((unsigned)tiles), dim3(THREADS),
+                       0, stream, aq, ad, (int)m, wq, wd, (int)n, (int)k, y,
+                       tiles_m, tiles_n);
   return hipGetLastError();
 }
 

@@ -544,6 +544,38 @@ def test_qgemm_small_and_large_grid_kernels_agree():
     assert_within_bound(y_small, yr, asum, k // 32, "small grid")
 
 
+def _misaligned_copy(t):
+    """The same values at an address 2 bytes past a 16-byte boundary."""
+    import torch
+    flat = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+    view = flat[1:t.numel() + 1].view(t.shape)
+    view.copy_(t)
+    assert view.data_ptr() % 16 == 2
+    return view
+
+
+@pytest.mark.parametrize("k", [256, 768])
+def test_qgemm_paired_and_per_stage_scale_loads_agree(k):
+    """The 4-wave GEMM loads the fp16 scales of two stages per row with one
+    16-byte load when k is a multiple of 256 and both scale arrays are 16-byte
+    aligned, else 2-byte loads every stage.  The same inputs with the scale
+    arrays moved 2 bytes off alignment take the second path: the outputs are
+    bit-identical and within the bound of the oracle (396 tiles of 128 x 128,
+    ragged in both dimensions; one and three pairs of stages)."""
+    m, n = 650, 8330
+    aq = W.random_int8(0, 530, (m, k), seed=k)
+    wq = W.random_int8(0, 531, (n, k), seed=k)
+    ad = W.random_scales(0, 532, (m, k // 32), seed=k)
+    wd = W.random_scales(0, 533, (n, k // 32), seed=k)
+    aq_g, ad_g, wq_g, wd_g = dev_tensor(aq), dev_tensor(ad), dev_tensor(wq), dev_tensor(wd)
+    assert ad_g.data_ptr() % 16 == 0 and wd_g.data_ptr() % 16 == 0
+    y_paired = host(bqi.qgemm_q8_0(aq_g, ad_g, wq_g, wd_g))
+    y_stage = host(bqi.qgemm_q8_0(aq_g, _misaligned_copy(ad_g), wq_g, _misaligned_copy(wd_g)))
+    assert np.array_equal(y_paired.view(np.uint32), y_stage.view(np.uint32))
+    yr, asum = oracle.qgemm_q8_0(aq, ad, wq, wd, nthreads=oracle_threads())
+    assert_within_bound(y_paired, yr, asum, k // 32, "paired scales k=%d" % k)
+
+
 @pytest.mark.parametrize("k", [256, 288])
 def test_qgemm_ragged_more_tiles_than_slots(k):
     """536 tiles of 128 x 128 (more than one round of workgroups, a short
