@@ -206,6 +206,15 @@ __global__ __launch_bounds__(RT) void k_route(
 // it alone reads (its 32 columns x 4 groups) to fp32 times 1/16 (the unpack
 // factor), 0 for groups past k; LDS operations of one wave complete in order,
 // so its later reads see the converted values without another barrier.
+//
+// When k is a multiple of 1024 and both scale arrays are 16-byte aligned
+// (PAIRED), the scales instead arrive two stages at a time: each weight
+// column's and activation row's 8 fp16 scales (16 bytes) with one direct load
+// per lane, three wave loads per workgroup every other stage in place of
+// twelve 2-byte loads every stage, into two pair buffers; the weight scales
+// are converted from there into the same fp32 slots, and the activation
+// scales are read from there.  A CU takes a 64-lane load instruction only
+// every ~32-38 cycles whatever its width, so this is ~10% of the MoE call.
 constexpr int GW = 4;              // waves per workgroup
 constexpr int GT = GW * 64;        // threads per workgroup
 constexpr int GBN = GW * 32;       // output columns per workgroup (32 per wave)
@@ -268,8 +277,8 @@ __device__ __forceinline__ i32x4 unpack_w4x16(i32x4 p, int shl) {
 // column 8(r/4) + 4(L/32) + r%4 of the wave's columns, routed row 32t + L%32
 // of the chunk.  Per term: t_r = fma(F_r, da, -1.5*2^23*da) = round(da * 16P)
 // with da the lane's activation scale, then acc = fma(t_r, dw_r / 16, acc).
-template <int R>
-__device__ __forceinline__ void grouped_stage(const GBuf &B, int wave, int lane_in,
+template <int R, bool PAIRED>
+__device__ __forceinline__ void grouped_stage(const GBuf &B, const uint16_t *ra, int wave, int lane_in,
                                               const i32x16 &seed, f32x16 (&acc)[R]) {
   // the lane index is laundered so that the LDS addresses below are rebuilt
   // each stage instead of being hoisted out of the stage loop into registers
@@ -282,11 +291,19 @@ __device__ __forceinline__ void grouped_stage(const GBuf &B, int wave, int lane_
   float da[R][GNB];
 #pragma unroll
   for (int t = 0; t < R; ++t) {
-    const i32x4 v = *reinterpret_cast<const i32x4 *>(&B.as[(32 * t + l32) * GNB]);
-    da[t][0] = half_bits_to_float((uint16_t)v.x);
-    da[t][1] = half_bits_to_float((uint16_t)v.y);
-    da[t][2] = half_bits_to_float((uint16_t)v.z);
-    da[t][3] = half_bits_to_float((uint16_t)v.w);
+    if constexpr (PAIRED) {
+      const uint2 v = *reinterpret_cast<const uint2 *>(ra + 2 * GNB * (32 * t + l32));
+      da[t][0] = half_bits_to_float((uint16_t)(v.x & 0xffffu));
+      da[t][1] = half_bits_to_float((uint16_t)(v.x >> 16));
+      da[t][2] = half_bits_to_float((uint16_t)(v.y & 0xffffu));
+      da[t][3] = half_bits_to_float((uint16_t)(v.y >> 16));
+    } else {
+      const i32x4 v = *reinterpret_cast<const i32x4 *>(&B.as[(32 * t + l32) * GNB]);
+      da[t][0] = half_bits_to_float((uint16_t)v.x);
+      da[t][1] = half_bits_to_float((uint16_t)v.y);
+      da[t][2] = half_bits_to_float((uint16_t)v.z);
+      da[t][3] = half_bits_to_float((uint16_t)v.w);
+    }
     // converted once here: left to itself the compiler folds the conversion
     // into each epilogue fma as v_fma_mix_f32, which issues at a lower rate
     asm volatile("" : "+v"(da[t][0]), "+v"(da[t][1]), "+v"(da[t][2]), "+v"(da[t][3]));
@@ -377,8 +394,9 @@ __device__ __forceinline__ int64_t unpack_w4x8(int64_t p, int shl) {
 
 // arow0 (a multiple of 16): the first of the 16 staged rows that the wave
 // reads.
-__device__ __forceinline__ void grouped_stage_half(const GBuf &B, int wave, int lane_in, int arow0,
-                                                   const i32x4 &seed4, f32x4 (&acc)[2]) {
+template <bool PAIRED>
+__device__ __forceinline__ void grouped_stage_half(const GBuf &B, const uint16_t *ra, int wave, int lane_in,
+                                                   int arow0, const i32x4 &seed4, f32x4 (&acc)[2]) {
   int lane = lane_in;
   asm volatile("" : "+v"(lane));
   const int l16 = lane & 15, kg = lane >> 4;
@@ -386,7 +404,14 @@ __device__ __forceinline__ void grouped_stage_half(const GBuf &B, int wave, int 
   const int aswz_l = (l16 >> 1) & 7;  // aswz of row arow0 + l16
   const int arow = arow0 + l16;
   float da[GNB];
-  {
+  if constexpr (PAIRED) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(ra + 2 * GNB * arow);
+    da[0] = half_bits_to_float((uint16_t)(v.x & 0xffffu));
+    da[1] = half_bits_to_float((uint16_t)(v.x >> 16));
+    da[2] = half_bits_to_float((uint16_t)(v.y & 0xffffu));
+    da[3] = half_bits_to_float((uint16_t)(v.y >> 16));
+    asm volatile("" : "+v"(da[0]), "+v"(da[1]), "+v"(da[2]), "+v"(da[3]));
+  } else {
     const i32x4 v = *reinterpret_cast<const i32x4 *>(&B.as[arow * GNB]);
     da[0] = half_bits_to_float((uint16_t)v.x);
     da[1] = half_bits_to_float((uint16_t)v.y);
@@ -444,9 +469,10 @@ enum GMode {
 // (columns 32w .. 32w+31 of the buffer) and staged rows 16w .. 16w+15 hold
 // the workgroup's columns and rows over quarter w, so each wave loads exactly
 // what it reads.  The four partial sums are added through LDS in wave order.
-template <int R, int MODE>
-__device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], const int *s_tok,
-                                              const int *s_row, int e, int n0, int crows) {
+template <int R, int MODE, bool PAIRED>
+__device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], uint16_t *raw,
+                                              const int *s_tok, const int *s_row, int e, int n0,
+                                              int crows) {
   constexpr bool HALF = MODE != G_FULL;   // 16-row tiles
   constexpr bool SPLIT = MODE == G_SPLIT;
   static_assert(MODE == G_FULL || (MODE == G_HALF && R == 1) || (SPLIT && R == 2),
@@ -533,6 +559,7 @@ __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], co
       const uint32_t lds = lds_addr(&D.a[1024 * (NA * wave_u + q)]);
       asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(abase), "{m0}"(lds) : "memory");
     }
+    if constexpr (PAIRED) return;
     const uint16_t *asbase = A.ad + g0;
 #pragma unroll
     for (int q = 0; q < NAS; ++q) {
@@ -550,12 +577,47 @@ __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], co
       asm volatile("s_nop 0\n\tglobal_load_lds_ushort %0, %1" :: "v"(2 * off), "s"(wsbase), "{m0}"(lds) : "memory");
     }
   };
+  // PAIRED: the fp16 scales of a pair of stages (2 GNB groups, 16 bytes per
+  // row or column) arrive with one direct load per lane into raw[pair % 2]:
+  // waves 0 and 1 load the weight scales of buffer columns 64 w .. +63,
+  // wave 2 those of the 64 staged activation rows (split: buffer column c and
+  // staged row r belong to quarter c / 32 and r / 16).  Pair p is loaded in
+  // stage 2p - 1, when every wave is past stage 2p - 2, the last reader of
+  // the buffer it overwrites; its stages read it after their stage barrier.
+  constexpr int RAW_A = GCH * 2 * GNB;          // halves per pair buffer of activation scales
+  constexpr int RAW_W = GBN * 2 * GNB;          // halves per pair buffer of weight scales
+  int raw_off = 0;
+  if constexpr (PAIRED) {
+    if (wave_u < 2) {
+      const int c = 64 * wave_u + lane;
+      raw_off = 2 * (min(n0 + (SPLIT ? (c & 31) : c), n - 1) * nbk + (SPLIT ? qg * (c >> 5) : 0));
+    } else if (wave_u == 2) {
+      raw_off = 2 * (s_tok[lane] * nbk + (SPLIT ? qg * (lane >> 4) : 0));
+    }
+  }
+  auto issue_raw = [&](int pair) {
+    if (wave_u < 2) {
+      const uint32_t lds = lds_addr(raw + 2 * RAW_A + RAW_W * (pair & 1) + 2 * GNB * 64 * wave_u);
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(raw_off + 4 * GNB * pair), "s"(wd_e), "{m0}"(lds) : "memory");
+    } else if (wave_u == 2) {
+      const uint32_t lds = lds_addr(raw + RAW_A * (pair & 1));
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(raw_off + 4 * GNB * pair), "s"(A.ad), "{m0}"(lds) : "memory");
+    }
+  };
   // The weight scales this wave reads in stage s (its 32 columns, all
   // groups), converted in place: lane L takes column 32 w + L%32, groups
   // 2 (L/32) and 2 (L/32) + 1.
   auto convert_ws = [&](int s) {
     GBuf &D = S[s % GNS];
     const int c = wave * 32 + (lane & 31);
+    if constexpr (PAIRED) {
+      const uint32_t two = *reinterpret_cast<const uint32_t *>(
+          raw + 2 * RAW_A + RAW_W * ((s >> 1) & 1) + 2 * GNB * c + GNB * (s & 1) + 2 * (lane >> 5));
+      const int g = 2 * (lane >> 5);
+      D.ws[g][c] = __builtin_bit_cast(uint32_t, half_bits_to_float((uint16_t)(two & 0xffffu)) * 0.0625f);
+      D.ws[g + 1][c] = __builtin_bit_cast(uint32_t, half_bits_to_float((uint16_t)(two >> 16)) * 0.0625f);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int g = 2 * (lane >> 5) + i;
@@ -580,16 +642,21 @@ __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], co
   // Stage s waits for its own loads (issued before stage s-1's compute); the
   // barrier then makes every wave's loads of stage s visible and frees the
   // buffer of stage s-1, which takes stage s+1's loads during this compute.
+  if constexpr (PAIRED) issue_raw(0);
   issue(0);
   for (int s = 0; s < stages; ++s) {
     wait_vmcnt<0>();
     lds_barrier();
     if (s + 1 < stages) issue(s + 1);
+    if constexpr (PAIRED) {
+      if ((s & 1) && s + 1 < stages) issue_raw((s + 1) >> 1);
+    }
     convert_ws(s);
+    const uint16_t *ra = raw + RAW_A * ((s >> 1) & 1) + GNB * (s & 1);
     if constexpr (HALF)
-      grouped_stage_half(S[s % GNS], wave, lane, SPLIT ? 16 * wave : 0, seed4, acc16);
+      grouped_stage_half<PAIRED>(S[s % GNS], ra, wave, lane, SPLIT ? 16 * wave : 0, seed4, acc16);
     else
-      grouped_stage<R>(S[s % GNS], wave, lane, seed, acc);
+      grouped_stage<R, PAIRED>(S[s % GNS], ra, wave, lane, seed, acc);
   }
 
   if constexpr (SPLIT) {
@@ -679,6 +746,7 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
   return v;
 }
 
+template <bool PAIRED>
 __global__ __launch_bounds__(GT, 3) void k_grouped_w4a8(
     const int8_t *__restrict__ aq, const uint16_t *__restrict__ ad, int top_k,
     const uint8_t *__restrict__ wq4, const uint16_t *__restrict__ wd,
@@ -686,6 +754,9 @@ __global__ __launch_bounds__(GT, 3) void k_grouped_w4a8(
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ rows,
     float *__restrict__ y) {
   __shared__ __attribute__((aligned(16))) GBuf S[GNS];
+  // PAIRED: raw fp16 scales of a pair of stages, two pair buffers of the
+  // activation scales [GCH][2 GNB], then two of the weight scales [GBN][2 GNB]
+  __shared__ __attribute__((aligned(16))) uint16_t raw[PAIRED ? 2 * (GCH + GBN) * 2 * GNB : 8];
   __shared__ int s_tok[GCH];  // token of each staged row
   __shared__ int s_row[GCH];  // routed row (output row) of each staged row
 
@@ -752,7 +823,7 @@ __global__ __launch_bounds__(GT, 3) void k_grouped_w4a8(
         s_tok[tid] = rr / top_k;
       }
       __syncthreads();
-      grouped_chunk<2, G_SPLIT>(A, S, s_tok, s_row, e, 32 * strip, crows);
+      grouped_chunk<2, G_SPLIT, PAIRED>(A, S, raw, s_tok, s_row, e, 32 * strip, crows);
     }
     return;
   }
@@ -779,11 +850,11 @@ __global__ __launch_bounds__(GT, 3) void k_grouped_w4a8(
     }
     __syncthreads();
     if (crows <= 16)
-      grouped_chunk<1, G_HALF>(A, S, s_tok, s_row, e, n0, crows);
+      grouped_chunk<1, G_HALF, PAIRED>(A, S, raw, s_tok, s_row, e, n0, crows);
     else if (crows <= 32)
-      grouped_chunk<1, G_FULL>(A, S, s_tok, s_row, e, n0, crows);
+      grouped_chunk<1, G_FULL, PAIRED>(A, S, raw, s_tok, s_row, e, n0, crows);
     else
-      grouped_chunk<2, G_FULL>(A, S, s_tok, s_row, e, n0, crows);
+      grouped_chunk<2, G_FULL, PAIRED>(A, S, raw, s_tok, s_row, e, n0, crows);
   }
 }
 
@@ -816,9 +887,15 @@ hipError_t launch_grouped_w4a8(const int8_t *aq, const uint16_t *ad,
                            ? rows_total / SPLIT_ROWS * ((n + 31) / 32)
                            : 0;
   const int64_t split_wgs = std::min(most, G_SPLIT_WGS);
-  hipLaunchKernelGGL(k_grouped_w4a8, dim3((unsigned)(n_experts * tiles_n + split_wgs)),
-                     dim3(GT), 0, stream, aq, ad, (int)top_k, wq4, wd,
-                     (int)n_experts, (int)n, (int)k, counts, offsets, rows, y);
+  const bool paired = (k / QK) % (8 * GNB) == 0 && ((uintptr_t)ad & 15) == 0 && ((uintptr_t)wd & 15) == 0;
+  if (paired)
+    hipLaunchKernelGGL(k_grouped_w4a8<true>, dim3((unsigned)(n_experts * tiles_n + split_wgs)),
+                       dim3(GT), 0, stream, aq, ad, (int)top_k, wq4, wd,
+                       (int)n_experts, (int)n, (int)k, counts, offsets, rows, y);
+  else
+    hipLaunchKernelGGL(k_grouped_w4a8<false>, dim3((unsigned)(n_experts * tiles_n + split_wgs)),
+                       dim3(GT), 0, stream, aq, ad, (int)top_k, wq4, wd,
+                       (int)n_experts, (int)n, (int)k, counts, offsets, rows, y);
   return hipGetLastError();
 }
 

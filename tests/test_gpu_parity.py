@@ -742,6 +742,35 @@ def test_grouped_w4a8_unaligned_scales():
     assert_within_bound(y, yr, asum, K // 32, "unaligned scales")
 
 
+@pytest.mark.parametrize("K,counts", [
+    (2048, (200, 70, 40, 13, 64, 33)),   # split pieces, 64-row, 32-row and 16-row chunks
+    (1024, (17, 16, 81, 1, 48, 0))])     # one pair of stages per K quarter of the split pieces
+def test_grouped_w4a8_paired_and_per_stage_scale_loads_agree(K, counts):
+    """With k a multiple of 1024 and both scale arrays 16-byte aligned the
+    grouped GEMM loads each row's and column's scales for two stages with one
+    16-byte load; otherwise 2-byte loads every stage.  The same inputs with
+    the scale arrays moved 2 bytes off alignment take the second path: the
+    outputs are bit-identical, and within the bound of the oracle (chunks of
+    64, 32 and 16 rows, and the split pieces past an expert's first 64)."""
+    E, N, tk = len(counts), 200, 1
+    ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    g = np.random.default_rng(zlib.crc32(b"paired scales") + K)
+    ids = g.permutation(ids).reshape(-1, tk)
+    T = ids.shape[0]
+    qa = W.random_int8("moe", 710, (T, K), seed=K)
+    da = W.random_scales("moe", 711, (T, K // 32), seed=K)
+    packed = g.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    wsc = W.random_scales("moe", 712, (E, N, K // 32), seed=K)
+    args = [dev_tensor(a) for a in (qa, da, ids, packed, wsc)]
+    assert args[1].data_ptr() % 16 == 0 and args[4].data_ptr() % 16 == 0
+    y_paired = host(bqi.qgemm_w4a8_grouped(*args))
+    y_stage = host(bqi.qgemm_w4a8_grouped(args[0], _misaligned_copy(args[1]), args[2], args[3],
+                                          _misaligned_copy(args[4])))
+    assert np.array_equal(y_paired.view(np.uint32), y_stage.view(np.uint32))
+    yr, asum = oracle.qgemm_w4a8_grouped(qa, da, ids, packed, wsc, nthreads=oracle_threads())
+    assert_within_bound(y_paired, yr, asum, K // 32, "paired grouped scales K=%d" % K)
+
+
 @pytest.mark.parametrize("weights", ["quantized_normal", "uniform_codes"])
 def test_grouped_w4a8_moe_workload_full(weights):
     m = W.MOE
