@@ -19,7 +19,8 @@
 // thread loads 2-byte scales into registers each stage.  Both give the same
 // LDS contents.  The load instructions, not their bytes, are what a CU takes
 // slowly (one 64-lane load per ~32-38 cycles), so the paired path's 2 scale
-// loads per stage instead of 16 make the GEMM ~4% faster.
+// loads per stage instead of 16 make the GEMM ~4% faster (k_gemm_mfma_w8
+// below takes the same paired path, ~6% faster).
 // The loads of stage s+1 are in flight while stage s computes.
 //
 // Scale epilogue (per 32x32 tile and block), two fp32 FMAs per output:
@@ -402,6 +403,7 @@ static_assert(BM * NBS == W8_THREADS, "one scale of each operand per thread and 
 // inline asm (dma_lds16 and the scale loads below), which the compiler
 // neither counts nor waits for, because its own count of direct loads ends in
 // a full drain (vmcnt(0)) at every stage.
+template <bool PAIRED>
 __global__ __launch_bounds__(W8_THREADS, 1) void k_gemm_mfma_w8(
     const int8_t *__restrict__ aq, const uint16_t *__restrict__ ad, int m,
     const int8_t *__restrict__ wq, const uint16_t *__restrict__ wd, int n,
@@ -446,6 +448,38 @@ __global__ __launch_bounds__(W8_THREADS, 1) void k_gemm_mfma_w8(
     T[buf].ad[blk][row] = half_bits_to_float((uint16_t)sa_reg);
     T[buf].wd[row][blk] = half_bits_to_float((uint16_t)sw_reg);
   };
+  // PAIRED: as in the 4-wave kernel, waves 0 and 1 load the scales of A tile
+  // rows 64 w .. +63 for two stages (16 bytes per lane), waves 2 and 3 those
+  // of W tile rows 64 (w - 2) .. +63, into the raw area after the stage
+  // buffers, and each lane converts its own row
+  uint16_t *raw = reinterpret_cast<uint16_t *>(gemm_lds + W8_LDS);  // [2][BM][2 NBS]
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const bool sc_a = wave_u < 2;
+  const int sc_row = 64 * (wave_u & 1) + lane;
+  const int sc_goff = 2 * ((sc_a ? min(m0 + sc_row, m - 1) : min(n0 + sc_row, n - 1)) * nbk);
+  const uint16_t *sc_base = sc_a ? ad : wd;
+  uint16_t *sc_raw = raw + (sc_a ? 0 : BM * 2 * NBS);
+  auto issue_raw = [&](int pair) {
+    if (wave_u < 4) {
+      const uint32_t lds = lds_addr(sc_raw + 2 * NBS * 64 * (wave_u & 1));
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(sc_goff + 4 * NBS * pair), "s"(sc_base), "{m0}"(lds) : "memory");
+    }
+  };
+  auto convert_raw = [&](int s, int buf) {
+    if (wave_u < 4) {
+      const uint2 v = *reinterpret_cast<const uint2 *>(sc_raw + 2 * NBS * sc_row + NBS * (s & 1));
+      const float f0 = half_bits_to_float((uint16_t)(v.x & 0xffffu)), f1 = half_bits_to_float((uint16_t)(v.x >> 16));
+      const float f2 = half_bits_to_float((uint16_t)(v.y & 0xffffu)), f3 = half_bits_to_float((uint16_t)(v.y >> 16));
+      if (sc_a) {
+        T[buf].ad[0][sc_row] = f0;
+        T[buf].ad[1][sc_row] = f1;
+        T[buf].ad[2][sc_row] = f2;
+        T[buf].ad[3][sc_row] = f3;
+      } else {
+        *reinterpret_cast<f32x4 *>(&T[buf].wd[sc_row][0]) = f32x4{f0, f1, f2, f3};
+      }
+    }
+  };
 
   float acc[2][16];
 #pragma unroll
@@ -458,10 +492,17 @@ __global__ __launch_bounds__(W8_THREADS, 1) void k_gemm_mfma_w8(
   for (int r = 0; r < 16; ++r) seed[r] = MAGIC_BITS;
 
   // stage 0 landed and its scales stored; stage 1's tiles in flight
-  issue_scales(0);
-  issue_direct(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" : "+v"(sa_reg), "+v"(sw_reg) :: "memory");
-  store_scales(0);
+  if constexpr (PAIRED) {
+    issue_raw(0);
+    issue_direct(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    convert_raw(0, 0);
+  } else {
+    issue_scales(0);
+    issue_direct(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" : "+v"(sa_reg), "+v"(sw_reg) :: "memory");
+    store_scales(0);
+  }
   if (stages > 1) issue_direct(1, 1);
   __syncthreads();
 
@@ -474,7 +515,11 @@ __global__ __launch_bounds__(W8_THREADS, 1) void k_gemm_mfma_w8(
     // register loads are issued only for a stage that follows: the last stage
     // leaves none in flight, so no register load outlives the waits that name
     // its destination.
-    if (s + 1 < stages) issue_scales(s + 1);
+    if constexpr (PAIRED) {
+      if ((s & 1) && s + 1 < stages) issue_raw((s + 1) >> 1);
+    } else {
+      if (s + 1 < stages) issue_scales(s + 1);
+    }
     issue_direct(min(s + 2, stages - 1), (s + 2) % W8_NBUF);
 
     float dwf[2][NBS];
@@ -529,15 +574,23 @@ __global__ __launch_bounds__(W8_THREADS, 1) void k_gemm_mfma_w8(
 
     if (s + 1 < stages) {
       // everything but stage s+2's 2 * W8_LOADS_PER_WAVE tile loads has landed
-      asm volatile("s_waitcnt vmcnt(%2)" : "+v"(sa_reg), "+v"(sw_reg) : "n"(2 * W8_LOADS_PER_WAVE) : "memory");
-      store_scales((s + 1) % W8_NBUF);
+      if constexpr (PAIRED) {
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * W8_LOADS_PER_WAVE) : "memory");
+        convert_raw(s + 1, (s + 1) % W8_NBUF);
+      } else {
+        asm volatile("s_waitcnt vmcnt(%2)" : "+v"(sa_reg), "+v"(sw_reg) : "n"(2 * W8_LOADS_PER_WAVE) : "memory");
+        store_scales((s + 1) % W8_NBUF);
+      }
       __syncthreads();
     }
   }
 
   // no direct load may land after the workgroup ends; the scale registers
   // are named so that this wait also orders them (none is in flight here)
-  asm volatile("s_waitcnt vmcnt(0)" : "+v"(sa_reg), "+v"(sw_reg) :: "memory");
+  if constexpr (PAIRED)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" : "+v"(sa_reg), "+v"(sw_reg) :: "memory");
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int col = n0 + wn * 64 + j * 32 + l32;
@@ -575,11 +628,21 @@ hipError_t launch_gemm_mfma(const int8_t *aq, const uint16_t *ad, int64_t m,
   const int tiles = tiles_m * tiles_n;
   if (tiles <= device_cus()) {
     // at most one tile per CU: the 8-wave, three-stage kernel
-    static bool raised[64];
-    const hipError_t e = raise_dynamic_lds((const void *)k_gemm_mfma_w8, W8_LDS, raised);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_gemm_mfma_w8, dim3((unsigned)tiles), dim3(W8_THREADS), W8_LDS, stream,
-                       aq, ad, (int)m, wq, wd, (int)n, (int)k, y, tiles_m, tiles_n);
+    const bool paired = (k / QK) % (2 * NBS) == 0 && ((uintptr_t)ad & 15) == 0 && ((uintptr_t)wd & 15) == 0;
+    constexpr int RAW = 2 * BM * 2 * NBS * 2;  // bytes of the PAIRED raw scale area
+    if (paired) {
+      static bool raised[64];
+      const hipError_t e = raise_dynamic_lds((const void *)k_gemm_mfma_w8<true>, W8_LDS + RAW, raised);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(k_gemm_mfma_w8<true>, dim3((unsigned)tiles), dim3(W8_THREADS), W8_LDS + RAW, stream,
+                         aq, ad, (int)m, wq, wd, (int)n, (int)k, y, tiles_m, tiles_n);
+    } else {
+      static bool raised[64];
+      const hipError_t e = raise_dynamic_lds((const void *)k_gemm_mfma_w8<false>, W8_LDS, raised);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(k_gemm_mfma_w8<false>, dim3((unsigned)tiles), dim3(W8_THREADS), W8_LDS, stream,
+                         aq, ad, (int)m, wq, wd, (int)n, (int)k, y, tiles_m, tiles_n);
+    }
     return hipGetLastError();
   }
   const bool paired = (k / QK) % (2 * NBS) == 0 && ((uintptr_t)ad & 15) == 0 && ((uintptr_t)wd & 15) == 0;

@@ -554,15 +554,16 @@ def _misaligned_copy(t):
     return view
 
 
-@pytest.mark.parametrize("k", [256, 768])
-def test_qgemm_paired_and_per_stage_scale_loads_agree(k):
-    """The 4-wave GEMM loads the fp16 scales of two stages per row with one
-    16-byte load when k is a multiple of 256 and both scale arrays are 16-byte
-    aligned, else 2-byte loads every stage.  The same inputs with the scale
-    arrays moved 2 bytes off alignment take the second path: the outputs are
-    bit-identical and within the bound of the oracle (396 tiles of 128 x 128,
-    ragged in both dimensions; one and three pairs of stages)."""
-    m, n = 650, 8330
+@pytest.mark.parametrize("m,n,k", [(650, 8330, 256), (650, 8330, 768), (200, 2000, 512),
+                                   (130, 3000, 1024)])
+def test_qgemm_paired_and_per_stage_scale_loads_agree(m, n, k):
+    """Both MFMA GEMM kernels load the fp16 scales of two stages per row with
+    one 16-byte load when k is a multiple of 256 and both scale arrays are
+    16-byte aligned, else 2-byte loads every stage.  The same inputs with the
+    scale arrays moved 2 bytes off alignment take the second path: the
+    outputs are bit-identical and within the bound of the oracle (396 tiles
+    of 128 x 128 on the 4-wave kernel, 32 and 48 on the 8-wave one, ragged in
+    both dimensions; one to four pairs of stages)."""
     aq = W.random_int8(0, 530, (m, k), seed=k)
     wq = W.random_int8(0, 531, (n, k), seed=k)
     ad = W.random_scales(0, 532, (m, k // 32), seed=k)
