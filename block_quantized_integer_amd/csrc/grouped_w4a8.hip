@@ -7,8 +7,9 @@
 // straight into int8 MFMA operands.
 //
 // Routing (k_route): one workgroup of 1024 threads per expert.  Each thread
-// owns a contiguous slice of 8 routed ids, counts the valid ids below the
-// expert (its offset) and equal to it, and one workgroup scan orders the
+// owns a contiguous slice of 8 routed ids (two 16-byte loads), counts the
+// valid ids below the expert (its offset) and equal to it, and one workgroup
+// scan (DPP within each wave, then the 16 wave totals through LDS) orders the
 // matches, so rows come out in increasing row order.  Up to 8192 routed rows
 // this is a single pass over ids held in registers; beyond, a counting pass
 // and a placing pass run chunk by chunk.  Deterministic.  The same pass
@@ -42,12 +43,16 @@ constexpr int RCHUNK = RT * RPT;  // ids per pass
 // the sum.  Contains two barriers.
 __device__ __forceinline__ int route_scan(int v, int *s_tmp, int &total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // inclusive wave scan with DPP: within each 16-lane row (shifts of 1, 2,
+  // 4, 8; lanes shifted in from outside the row add 0), then the end of row
+  // 0 / 2 into rows 1 / 3 and the end of row 1 into rows 2 and 3
   int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xf, 0xf, false);  // row_shr:1
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xf, 0xf, false);  // row_shr:2
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xf, 0xf, false);  // row_shr:4
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xf, 0xf, false);  // row_shr:8
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
   if (lane == 63) s_tmp[wave] = incl;
   __syncthreads();
   int wave_base = 0, sum = 0;
@@ -88,9 +93,18 @@ __global__ __launch_bounds__(RT) void k_route(
     const int r0 = tid * RPT;
     int v[RPT];
     int below = 0, eq = 0;
+    if (r0 + RPT <= rows_total && ((uintptr_t)ids & 15) == 0) {
+#pragma unroll
+      for (int j = 0; j < RPT; j += 4) {
+        const i32x4 q = *reinterpret_cast<const i32x4 *>(ids + r0 + j);
+        v[j] = q.x; v[j + 1] = q.y; v[j + 2] = q.z; v[j + 3] = q.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) v[j] = r0 + j < rows_total ? ids[r0 + j] : -1;
+    }
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
-      v[j] = r0 + j < rows_total ? ids[r0 + j] : -1;
       below += (v[j] >= 0 && v[j] < e);
       eq += (v[j] == e);
     }

@@ -677,6 +677,23 @@ def test_route_topk_bitexact():
     check_route(W.topk_ids(1025, 8, 128, seed=7), 128)
 
 
+def test_route_topk_ids_off_16_byte_alignment():
+    """Routed ids that start 4 bytes past a 16-byte boundary: the routing
+    pass reads them one at a time instead of 16 bytes at a time."""
+    import torch
+    for T, tk, E, seed in [(947, 8, 128, 8), (301, 3, 12, 9), (1025, 8, 128, 10)]:
+        ids = W.topk_ids(T, tk, E, seed=seed)
+        flat = torch.empty(ids.size + 4, dtype=torch.int32, device="cuda")
+        ids_dev = flat[1:ids.size + 1].view(T, tk)
+        ids_dev.copy_(dev_tensor(ids))
+        assert ids_dev.data_ptr() % 16 == 4
+        counts, offsets, rows = bqi.route_topk(ids_dev, E)
+        cr, orr, rr, _ = oracle.route_topk(ids, E)
+        assert np.array_equal(host(counts), cr)
+        assert np.array_equal(host(offsets), orr)
+        assert np.array_equal(host(rows)[: len(rr)], rr)
+
+
 def run_grouped(qa, da, ids, packed, wsc):
     y = bqi.qgemm_w4a8_grouped(dev_tensor(qa), dev_tensor(da), dev_tensor(ids),
                                dev_tensor(packed), dev_tensor(wsc))
