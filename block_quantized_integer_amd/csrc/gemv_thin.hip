@@ -192,8 +192,10 @@ __device__ __forceinline__ float half_wave_sum(float v) {
   v += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, v), 0x4e, 0xf, 0xf, false));  // lane ^ 2
   v += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, v), 0x141, 0xf, 0xf, false)); // half-row mirror
   v += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, v), 0x140, 0xf, 0xf, false)); // row mirror
-  v += __shfl_xor(v, 16);
-  return v;
+  // + lane ^ 16: the swap leaves each lane's own value in one result and its
+  // partner's in the other
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v), false, false);
+  return bits_to_float((int32_t)r[0]) + bits_to_float((int32_t)r[1]);
 }
 
 // Activation source of the register kernel: Q8_0 codes and scales, or fp32 /
@@ -384,13 +386,13 @@ __global__ __launch_bounds__(reg_threads(SRC, MT)) void k_gemv_reg(
   }
 
   // lanes 0..31 finish row 0, lanes 32..63 row 1
-  const bool lo = lane < 32;
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     if (i < m) {
-      const float keep = lo ? acc[0][i] : acc[1][i];
-      const float give = lo ? acc[1][i] : acc[0][i];
-      const float v = half_wave_sum(keep + __shfl_xor(give, 32));
+      // lane l < 32: acc0[l] + acc0[l + 32]; lane l >= 32: acc1[l - 32] + acc1[l]
+      const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, acc[0][i]),
+                                                       __builtin_bit_cast(uint32_t, acc[1][i]), false, false);
+      const float v = half_wave_sum(bits_to_float((int32_t)sw[0]) + bits_to_float((int32_t)sw[1]));
       const int row = row0 + (lane >> 5);
       if ((lane & 31) == 0 && row < n) y[(int64_t)i * n + row] = v;
     }

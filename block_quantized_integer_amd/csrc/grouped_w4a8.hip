@@ -960,25 +960,29 @@ __device__ __forceinline__ int32_t w4_hi(uint32_t p) {
 // three DPP steps then sum the lanes that differ in bits 0..2.  The result is
 // valid in the lanes with (l & 7) == 0.
 __device__ __forceinline__ float reduce_columns8(const float (&v)[8], int lane) {
-  const bool u32 = (lane & 32) != 0, u16 = (lane & 16) != 0, u8 = (lane & 8) != 0;
+  const bool u8 = (lane & 8) != 0;
   float v4[4], v2[2];
+  // lane ^ 32 and lane ^ 16 with gfx950's half swaps: swapping the upper 32
+  // lanes of a (the odd 16-lane rows of a) with the lower 32 lanes of b (the
+  // even rows of b) leaves, in every lane, the value it keeps in one result
+  // and its partner's in the other
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float keep = u32 ? v[q + 4] : v[q];
-    const float send = u32 ? v[q] : v[q + 4];
-    v4[q] = keep + __shfl_xor(send, 32);
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v[q]),
+                                                    __builtin_bit_cast(uint32_t, v[q + 4]), false, false);
+    v4[q] = bits_to_float((int32_t)r[0]) + bits_to_float((int32_t)r[1]);
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const float keep = u16 ? v4[q + 2] : v4[q];
-    const float send = u16 ? v4[q] : v4[q + 2];
-    v2[q] = keep + __shfl_xor(send, 16);
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v4[q]),
+                                                    __builtin_bit_cast(uint32_t, v4[q + 2]), false, false);
+    v2[q] = bits_to_float((int32_t)r[0]) + bits_to_float((int32_t)r[1]);
   }
   float s;
   {
     const float keep = u8 ? v2[1] : v2[0];
     const float send = u8 ? v2[0] : v2[1];
-    s = keep + __shfl_xor(send, 8);
+    s = keep + bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, send), 0x128, 0xf, 0xf, false));  // lane ^ 8
   }
   s += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, s), 0xb1, 0xf, 0xf, false));   // lane ^ 1
   s += bits_to_float(__builtin_amdgcn_mov_dpp(__builtin_bit_cast(int32_t, s), 0x4e, 0xf, 0xf, false));   // lane ^ 2
