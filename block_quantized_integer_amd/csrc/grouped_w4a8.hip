@@ -39,20 +39,25 @@ constexpr int RT = 1024;          // threads per routing workgroup
 constexpr int RPT = 8;            // ids per thread per pass
 constexpr int RCHUNK = RT * RPT;  // ids per pass
 
+// Inclusive sum over the 64 lanes of a wave, with DPP: within each 16-lane
+// row (shifts of 1, 2, 4, 8; lanes shifted in from outside the row add 0),
+// then the end of row 0 / 2 into rows 1 / 3 and the end of row 1 into rows 2
+// and 3.
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // Exclusive workgroup scan of one int per thread (RT threads); `total` gets
 // the sum.  Contains two barriers.
 __device__ __forceinline__ int route_scan(int v, int *s_tmp, int &total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // inclusive wave scan with DPP: within each 16-lane row (shifts of 1, 2,
-  // 4, 8; lanes shifted in from outside the row add 0), then the end of row
-  // 0 / 2 into rows 1 / 3 and the end of row 1 into rows 2 and 3
-  int incl = v;
-  incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xf, 0xf, false);  // row_shr:1
-  incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xf, 0xf, false);  // row_shr:2
-  incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xf, 0xf, false);  // row_shr:4
-  incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xf, 0xf, false);  // row_shr:8
-  incl += __builtin_amdgcn_update_dpp(0, incl, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
-  incl += __builtin_amdgcn_update_dpp(0, incl, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  const int incl = wave_scan_incl(v);
   if (lane == 63) s_tmp[wave] = incl;
   __syncthreads();
   int wave_base = 0, sum = 0;
@@ -749,17 +754,6 @@ __device__ __forceinline__ void grouped_chunk(const GArgs &A, GBuf (&S)[GNS], ui
   }
 }
 
-// Inclusive sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_sum(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(v, off);
-    if (lane >= off) v += t;
-  }
-  return v;
-}
-
 template <bool PAIRED>
 __global__ __launch_bounds__(GT, 3) void k_grouped_w4a8(
     const int8_t *__restrict__ aq, const uint16_t *__restrict__ ad, int top_k,
@@ -797,7 +791,7 @@ __global__ __launch_bounds__(GT, 3) void k_grouped_w4a8(
       rsum += c4[j];
       psum += split_pieces(c4[j]);
     }
-    const int rinc = wave_inclusive_sum(rsum), pinc = wave_inclusive_sum(psum);
+    const int rinc = wave_scan_incl(rsum), pinc = wave_scan_incl(psum);
     const int strips = (n + 31) / 32;
     const int step = (int)gridDim.x - main_wgs;
     const int64_t items = (int64_t)__builtin_amdgcn_readlane(pinc, 63) * strips;
