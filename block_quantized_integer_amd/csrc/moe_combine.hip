@@ -44,10 +44,19 @@ __global__ __launch_bounds__(CT) void k_moe_combine(const float *__restrict__ y,
       // is never formed, so no inf * 0 can enter the sum)
       float pj[TK];
       f32x4 v[TK];
+      // a full row of TK probabilities, 16-byte aligned: TK / 4 loads
+      const bool p4 = TK % 4 == 0 && top_k == TK && ((uintptr_t)pt & 15) == 0;
+      if (p4) {
+#pragma unroll
+        for (int j = 0; j < TK; j += 4) {
+          const f32x4 q = *reinterpret_cast<const f32x4 *>(pt + j);
+          pj[j] = q.x; pj[j + 1] = q.y; pj[j + 2] = q.z; pj[j + 3] = q.w;
+        }
+      }
 #pragma unroll
       for (int j = 0; j < TK; ++j) {
         const int jj = j < top_k ? j : 0;
-        pj[j] = pt[jj];
+        if (!p4) pj[j] = pt[jj];
         if constexpr (VEC) {
           v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(yt + (int64_t)jj * n + c));
         } else {
